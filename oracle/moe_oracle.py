@@ -1,0 +1,340 @@
+"""CPU oracle for the forward pass of one Mixture-of-Experts FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check of the entry
+module and the benchmark's CPU-baseline leg use it.  It shares no code with
+the HIP library; both receive the same seeded inputs from ``workloads``.
+
+What it computes follows the notebook "Mixture-of-experts and expert
+parallelism" (llm-systems-cookbook, serving track, notebook 09) plus the
+workload statements of the layer configurations:
+
+* "Top-k router": a bias-free linear map from the hidden state to N
+  logits, a softmax over all N experts, and the k best experts with their
+  gate weights (the softmax probabilities of the chosen experts).
+* "Dispatch and gather": each expert is an MLP fc2(gelu(fc1(x))) with
+  biases; the layer output starts at zero and, expert by expert, adds the
+  expert's output for every token that chose it, scaled by that token's gate
+  for the expert.
+* "Capacity factor": an expert has a per-batch slot budget of
+  tokens*k/N*factor (truncated to an integer); assignments beyond it are
+  dropped.  The drop rate is the summed overflow over the summed counts.
+
+Readings where the pages leave a step open (all listed in the design notes):
+selection is done on logits with ties to the lower expert index (softmax is
+strictly increasing, so this is the exact-arithmetic top-k); the kept
+assignments of an expert are its first C in flat order t*k+j; a dropped
+assignment contributes zero and the remaining gates are not rescaled;
+``renorm`` divides the chosen gates by their sum; ``residual`` adds x; the
+SwiGLU expert applies silu to the w1 branch and multiplies by the w3 branch;
+GELU is the erf form.
+
+Everything is computed in float64 from the exact stored input values (fp32
+and bf16 values widen exactly).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+
+# ----------------------------------------------------------------- helpers
+def f64(a) -> np.ndarray:
+    """Exact widening of a numpy array or a CPU torch tensor to float64."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.astype(np.float64, copy=False)
+    # torch tensor (fp32 or bf16): .double() is exact for both
+    return a.detach().cpu().double().numpy()
+
+
+# ----------------------------------------------------------------- routing
+def router_logits(x, w_router, b_router=None) -> np.ndarray:
+    """l[t, e] = sum_d x[t, d] * w_router[e, d]  (+ b_router[e]).
+
+    The notebook's router is a linear layer with no bias ("Top-k router");
+    the skewed-routing workload adds a fixed per-expert bias.
+    """
+    l = f64(x) @ f64(w_router).T
+    if b_router is not None:
+        l = l + f64(b_router)[None, :]
+    return l
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Softmax over all N experts of each token, max-subtracted."""
+    z = logits - logits.max(axis=1, keepdims=True)
+    ez = np.exp(z)
+    return ez / ez.sum(axis=1, keepdims=True)
+
+
+def expert_order(logits: np.ndarray) -> np.ndarray:
+    """Experts of each token by decreasing logit, ties to the lower index.
+
+    A stable sort of -logit keeps equal keys in ascending expert order.
+    """
+    return np.argsort(-logits, axis=1, kind="stable")
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """idx[t, :] = the first k experts of ``expert_order`` (int64)."""
+    N = logits.shape[1]
+    if not 1 <= k <= N:
+        raise ValueError(f"k={k} must lie in [1, N={N}]")
+    return expert_order(logits)[:, :k].astype(np.int64)
+
+
+def gate_values(probs: np.ndarray, idx: np.ndarray, renorm: bool) -> np.ndarray:
+    """g[t, j] = p[t, idx[t, j]], optionally divided by the sum over j."""
+    g = np.take_along_axis(probs, idx, axis=1)
+    if renorm:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g
+
+
+def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:
+    """Smallest gap between consecutive sorted logits among the first k+1.
+
+    For r = 1 .. min(k, N-1) this takes l_(r) - l_(r+1) of the descending
+    order; a positive value means both the chosen set and its order are
+    decided without ties.  Returns +inf per token when N == 1.
+    """
+    T, N = logits.shape
+    r = min(k, N - 1)
+    if r <= 0:
+        return np.full(T, np.inf)
+    top = -np.sort(-logits, axis=1)[:, : r + 1]
+    return (top[:, :-1] - top[:, 1:]).min(axis=1)
+
+
+def route(x, w_router, b_router, k: int, renorm: bool) -> dict:
+    """Router step: logits, softmax probabilities, top-k indices and gates."""
+    logits = router_logits(x, w_router, b_router)
+    probs = softmax(logits)
+    idx = select_topk(logits, k)
+    gate = gate_values(probs, idx, renorm)
+    return {"logits": logits, "probs": probs, "idx": idx, "gate": gate}
+
+
+# ---------------------------------------------------------------- dispatch
+def expert_counts(idx: np.ndarray, N: int) -> np.ndarray:
+    """counts[e] = number of (token, choice) pairs routed to expert e."""
+    flat = np.asarray(idx).reshape(-1)
+    return np.array([(flat == e).sum() for e in range(N)], dtype=np.int64)
+
+
+def capacity(T: int, k: int, N: int, cf: Optional[float]) -> Optional[int]:
+    """Per-expert slot budget int(T*k/N * cf); None means no limit.
+
+    Evaluated left to right in double precision and truncated, as the
+    notebook's "Capacity factor" section does; a negative factor means no
+    limit.
+    """
+    if cf is None or cf < 0:
+        return None
+    return int(T * k / N * cf)
+
+
+def dispatch(idx: np.ndarray, N: int, C: Optional[int]) -> dict:
+    """Group assignments by expert, keep the first C of each.
+
+    Assignment a = t*k + j.  For expert e its assignments are listed in
+    ascending a; the first min(count_e, C) are kept.  ``perm`` lists the
+    kept assignments expert by expert, ``offsets`` delimits each expert's
+    rows, ``slot[a]`` is the row of assignment a or -1 when dropped.
+    """
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    A = flat.size
+    counts = expert_counts(flat, N)
+    slot = np.full(A, -1, dtype=np.int64)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    perm_parts = []
+    row = 0
+    for e in range(N):
+        mine = np.nonzero(flat == e)[0]  # ascending flat index
+        kept = mine if C is None else mine[:C]
+        slot[kept] = row + np.arange(kept.size)
+        perm_parts.append(kept)
+        row += kept.size
+        offsets[e + 1] = row
+    perm = np.concatenate(perm_parts) if perm_parts else np.zeros(0, dtype=np.int64)
+    n_dropped = A - perm.size
+    return {"counts": counts, "offsets": offsets, "perm": perm, "slot": slot,
+            "n_dropped": int(n_dropped)}
+
+
+def drop_rate(counts: np.ndarray, C: Optional[int]) -> float:
+    """Summed overflow max(0, count - C) over summed counts."""
+    counts = np.asarray(counts, dtype=np.int64)
+    if C is None:
+        return 0.0
+    return float(np.clip(counts - C, 0, None).sum() / counts.sum())
+
+
+def imbalance(counts: np.ndarray, T: int, k: int, N: int) -> float:
+    """Largest expert load over the perfectly balanced load T*k/N."""
+    return float(np.max(counts) / (T * k / N))
+
+
+def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, N: int) -> float:
+    """N * sum_i f_i * P_i with f_i the fraction of tokens having expert i
+    among their choices and P_i the mean router probability of expert i
+    (notebook section "Switch Transformer auxiliary loss")."""
+    idx = np.asarray(idx)
+    f = np.array([(idx == e).any(axis=1).mean() for e in range(N)])
+    P = np.asarray(probs).mean(axis=0)
+    return float(N * (f * P).sum())
+
+
+# ----------------------------------------------------------------- experts
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """GELU in its exact form z * Phi(z), Phi the standard normal CDF."""
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def relu(z: np.ndarray) -> np.ndarray:
+    return np.maximum(z, 0.0)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """z * sigmoid(z)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_mlp(X, act: str, w1, b1=None, w3=None, w2=None, b2=None) -> np.ndarray:
+    """One expert on rows X[m, D] -> Y[m, D].
+
+    gelu/relu: Y = act(X w1^T + b1) w2^T + b2 (the notebook's Expert).
+    swiglu:    Y = (silu(X w1^T) * (X w3^T)) w2^T.
+    Weights use the nn.Linear layout [out, in].
+    """
+    X = f64(X)
+    Z = X @ f64(w1).T
+    if b1 is not None:
+        Z = Z + f64(b1)[None, :]
+    if act == "gelu":
+        H = gelu_erf(Z)
+    elif act == "relu":
+        H = relu(Z)
+    elif act == "swiglu":
+        H = silu(Z) * (X @ f64(w3).T)
+    else:
+        raise ValueError(f"unknown activation {act!r}")
+    Y = H @ f64(w2).T
+    if b2 is not None:
+        Y = Y + f64(b2)[None, :]
+    return Y
+
+
+def _expert_params(params: dict, e: int) -> dict:
+    def sl(name):
+        t = params.get(name)
+        return None if t is None else t[e]
+    return {"w1": sl("w1"), "b1": sl("b1"), "w3": sl("w3"), "w2": sl("w2"), "b2": sl("b2")}
+
+
+# ----------------------------------------------------------------- forward
+def combine_from_experts(x, params: dict, act: str, k: int, gate: np.ndarray,
+                         disp: dict, residual: bool,
+                         tokens: Optional[Sequence[int]] = None) -> dict:
+    """Per-expert loop of "Dispatch and gather" over the kept assignments.
+
+    out starts at zero (or at x with ``residual``); for each expert e the
+    rows of its kept assignments are gathered, run through expert e, scaled
+    by their gates and added to their tokens' outputs.  With ``tokens`` only
+    those tokens' outputs are produced (rows of other tokens are skipped).
+    Returns ``y`` (float64, [T, D] or [len(tokens), D]) and ``y_perm``
+    (ungated expert output of every computed kept row; NaN elsewhere).
+    """
+    xs = x
+    T = xs.shape[0]
+    D = xs.shape[1]
+    perm = disp["perm"]
+    offsets = disp["offsets"]
+    N = offsets.size - 1
+    if tokens is None:
+        want = np.ones(T, dtype=bool)
+        out_rows = np.arange(T)
+    else:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        want = np.zeros(T, dtype=bool)
+        want[tokens] = True
+        out_rows = tokens
+    where = np.full(T, -1, dtype=np.int64)
+    where[out_rows] = np.arange(out_rows.size)
+    out = np.zeros((out_rows.size, D), dtype=np.float64)
+    if residual:
+        out += f64(xs[out_rows] if tokens is not None else xs)
+    y_perm = np.full((perm.size, D), np.nan)
+    for e in range(N):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        a = perm[rows]
+        t = a // k
+        sel = want[t]
+        if not sel.any():
+            continue
+        rows, a, t = rows[sel], a[sel], t[sel]
+        j = a % k
+        Ye = expert_mlp(f64(xs[t]), act, **_expert_params(params, e))
+        y_perm[rows] = Ye
+        np.add.at(out, where[t], Ye * gate[t, j][:, None])
+    return {"y": out, "y_perm": y_perm}
+
+
+def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
+                capacity_slots: Optional[int] = None, residual: bool = False,
+                tokens: Optional[Sequence[int]] = None) -> dict:
+    """Whole layer: route, dispatch with capacity, experts, combine.
+
+    ``params`` holds w_router, b_router, w1, b1, w3, w2, b2 (numpy arrays or
+    CPU tensors in the C-ABI layouts; absent entries are None).
+    """
+    r = route(x, params["w_router"], params.get("b_router"), k, renorm)
+    N = r["logits"].shape[1]
+    d = dispatch(r["idx"], N, capacity_slots)
+    c = combine_from_experts(x, params, act, k, r["gate"], d, residual, tokens)
+    out = dict(r)
+    out.update(d)
+    out.update(c)
+    return out
+
+
+def brute_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
+                  capacity_slots: Optional[int] = None, residual: bool = False) -> np.ndarray:
+    """Second formulation for tiny inputs: every expert on every token.
+
+    Builds the sparse gate matrix G[t, e] (the gate of each kept assignment,
+    zero elsewhere) and contracts it with the dense stack of all experts'
+    outputs.  Kept assignments are found by counting, for each (t, j), the
+    earlier assignments to the same expert (O(A^2)).
+    """
+    X = f64(x)
+    T = X.shape[0]
+    logits = router_logits(X, params["w_router"], params.get("b_router"))
+    N = logits.shape[1]
+    # selection by explicit comparison: expert e precedes e' when its logit is
+    # larger, or equal with a smaller index
+    idx = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        order = sorted(range(N), key=lambda e: (-logits[t, e], e))
+        idx[t] = order[:k]
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    g = np.array([[p[t, idx[t, j]] for j in range(k)] for t in range(T)])
+    if renorm:
+        g = g / g.sum(axis=1, keepdims=True)
+    flat = idx.reshape(-1)
+    G = np.zeros((T, N))
+    for a in range(flat.size):
+        rank = int((flat[:a] == flat[a]).sum())
+        if capacity_slots is None or rank < capacity_slots:
+            G[a // k, flat[a]] += g[a // k, a % k]
+    Yall = np.stack([expert_mlp(X, act, **_expert_params(params, e)) for e in range(N)])
+    y = np.einsum("te,ted->td", G, Yall.transpose(1, 0, 2))
+    if residual:
+        y = y + X
+    return y

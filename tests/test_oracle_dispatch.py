@@ -1,0 +1,123 @@
+"""Pins of the oracle's dispatch (counts, stable grouping, capacity drops)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.cpu
+
+
+def test_hand_derived_dispatch_example():
+    with open(os.path.join(GOLDEN, "dispatch_tiny.json")) as f:
+        g = json.load(f)
+    idx = np.array(g["idx"])
+    T, k = idx.shape
+    for case in g["cases"]:
+        C = oracle.capacity(T, k, g["N"], case["cf"])
+        assert C == case["capacity"]
+        d = oracle.dispatch(idx, g["N"], C)
+        assert d["counts"].tolist() == case["counts"]
+        assert d["offsets"].tolist() == case["offsets"]
+        assert d["perm"].tolist() == case["perm"]
+        assert d["slot"].tolist() == case["slot"]
+        assert d["n_dropped"] == case["n_dropped"]
+
+
+def test_capacity_truncates_like_the_notebook():
+    # switch-style layer: 16384 tokens, top-1, 128 experts
+    assert oracle.capacity(16384, 1, 128, 1.0) == 128
+    assert oracle.capacity(16384, 1, 128, 1.5) == 192
+    # notebook sizes: 1024 tokens, top-2, 8 experts -> 256 and 384 slots
+    assert oracle.capacity(1024, 2, 8, 1.0) == 256
+    assert oracle.capacity(1024, 2, 8, 1.5) == 384
+    # truncation, not rounding: 10*1/3*1.0 = 3.33 -> 3 ; 10*2/3*1.0 = 6.67 -> 6
+    assert oracle.capacity(10, 1, 3, 1.0) == 3
+    assert oracle.capacity(10, 2, 3, 1.0) == 6
+    assert oracle.capacity(10, 2, 3, None) is None
+    assert oracle.capacity(10, 2, 3, 0.0) == 0
+
+
+def _random_idx(rng, T, N, k):
+    return np.stack([rng.permutation(N)[:k] for _ in range(T)])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_counts_perm_slot_against_library_routines(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 12))
+    k = int(rng.integers(1, N + 1))
+    T = int(rng.integers(1, 200))
+    idx = _random_idx(rng, T, N, k)
+    flat = idx.reshape(-1)
+    # skew some tokens onto expert 0 when allowed
+    d = oracle.dispatch(idx, N, None)
+    assert np.array_equal(d["counts"], np.bincount(flat, minlength=N))
+    assert d["counts"].sum() == T * k
+    assert np.array_equal(d["perm"], np.argsort(flat, kind="stable"))
+    assert np.array_equal(d["slot"][d["perm"]], np.arange(T * k))
+    for C in (0, 1, 2, 5, T * k):
+        dc = oracle.dispatch(idx, N, C)
+        stable = np.argsort(flat, kind="stable")
+        kept = []
+        for e in range(N):
+            kept += [a for a in stable if flat[a] == e][:C]
+        assert dc["perm"].tolist() == kept
+        assert dc["n_dropped"] == int(np.clip(dc["counts"] - C, 0, None).sum())
+        assert np.array_equal(np.diff(dc["offsets"]), np.minimum(dc["counts"], C))
+
+
+def test_rank_brute_force():
+    rng = np.random.default_rng(9)
+    T, N, k = 40, 5, 2
+    idx = _random_idx(rng, T, N, k)
+    flat = idx.reshape(-1)
+    for C in (3, 8, 16, None):
+        d = oracle.dispatch(idx, N, C)
+        for a in range(flat.size):
+            rank = int((flat[:a] == flat[a]).sum())
+            kept = C is None or rank < C
+            if kept:
+                assert d["slot"][a] == d["offsets"][flat[a]] + rank
+            else:
+                assert d["slot"][a] == -1
+
+
+def test_drop_rate_non_increasing_in_capacity_factor():
+    rng = np.random.default_rng(11)
+    T, N, k = 512, 8, 2
+    # skewed routing
+    p = np.array([0.4, 0.2, 0.1, 0.1, 0.08, 0.06, 0.04, 0.02])
+    idx = np.stack([rng.choice(N, size=k, replace=False, p=p) for _ in range(T)])
+    counts = oracle.expert_counts(idx, N)
+    prev = None
+    for cf in np.linspace(0.0, 4.0, 41):
+        C = oracle.capacity(T, k, N, float(cf))
+        d = oracle.dispatch(idx, N, C)
+        rate = oracle.drop_rate(counts, C)
+        assert rate == pytest.approx(d["n_dropped"] / (T * k), abs=0)
+        if prev is not None:
+            assert rate <= prev
+        prev = rate
+    # capacity at least the largest count -> no drops
+    d = oracle.dispatch(idx, N, int(counts.max()))
+    assert d["n_dropped"] == 0
+
+
+def test_imbalance_and_aux_loss_closed_forms():
+    T, N, k = 64, 8, 2
+    # round-robin assignment and uniform gates (the notebook's balanced case)
+    idx = (np.arange(T * k) % N).reshape(T, k)
+    probs = np.full((T, N), 1.0 / N)
+    counts = oracle.expert_counts(idx, N)
+    assert oracle.imbalance(counts, T, k, N) == 1.0
+    # every expert appears in a fraction 2/8 of tokens: loss = N * sum (2/8)(1/8) = k
+    assert oracle.switch_aux_loss(idx, probs, N) == pytest.approx(2.0, abs=1e-15)
+    # all tokens on experts 0,1 with all probability there: loss = N * (1*0.5 + 1*0.5) = N
+    idx2 = np.tile([0, 1], (T, 1))
+    probs2 = np.zeros((T, N))
+    probs2[:, :2] = 0.5
+    assert oracle.switch_aux_loss(idx2, probs2, N) == pytest.approx(N, abs=1e-12)

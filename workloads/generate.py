@@ -1,0 +1,154 @@
+"""Seeded random draws for one MoE layer instance (inputs only).
+
+Two recipes:
+
+* ``"p5"`` replays the order of draws of the notebook "Mixture-of-experts and
+  expert parallelism" (sections "Top-k router" and "Dispatch and gather"):
+  global seed ``seed``, a bias-free ``nn.Linear(D, N)`` router whose weight is
+  then replaced by standard normals times 0.1, then x as standard normals;
+  global seed ``seed + 1``, then one ``Expert`` per index, each made of
+  ``nn.Linear(D, F)`` and ``nn.Linear(F, D)`` with PyTorch's default uniform
+  initialisation of weights and biases.
+* ``"normal0.02"``: x ~ N(0, 1); router, expert weights and (when present)
+  expert biases ~ N(0, 0.02^2).  Every (tensor, expert) pair has its own
+  ``torch.Generator`` so that one expert can be regenerated alone and the
+  draws can run on several threads.  The optional "zipf1.2" router bias is
+  b[e] = -1.2 * ln(e + 1), the logarithm of a Zipf(s=1.2) weight over expert
+  rank, stored in fp32.
+
+bf16 tensors are drawn in fp32 and rounded to nearest-even.  All tensors are
+CPU tensors in the layouts of the C ABI: x[T,D], w_router[N,D], b_router[N],
+w1[N,F,D], b1[N,F], w3[N,F,D], w2[N,D,F], b2[N,D].
+"""
+from __future__ import annotations
+
+import math
+import os
+import zlib
+from concurrent.futures import ThreadPoolExecutor
+from typing import Iterable, Optional
+
+import torch
+
+from .configs import MoeConfig
+
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+_STD_W = 0.02
+_ALL_PARTS = ("x", "router", "experts")
+
+
+def _stream_seed(base: int, tensor: str, e: int) -> int:
+    return (base * 1_000_003 + zlib.crc32(tensor.encode()) * 65_537 + e * 7_919) % (2**62)
+
+
+def _normal(shape, seed: int, std: float, dtype: torch.dtype, out: Optional[torch.Tensor] = None):
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        v.mul_(std)
+    v = v.to(dtype)
+    if out is not None:
+        out.copy_(v)
+        return out
+    return v
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def zipf_router_bias(N: int, s: float = 1.2) -> torch.Tensor:
+    return torch.tensor([-s * math.log(e + 1.0) for e in range(N)], dtype=torch.float32)
+
+
+def _expert_tensor_specs(cfg: MoeConfig):
+    """(name, per-expert shape) of each expert parameter the config has."""
+    specs = [("w1", (cfg.F, cfg.D))]
+    if cfg.act == "swiglu":
+        specs.append(("w3", (cfg.F, cfg.D)))
+    specs.append(("w2", (cfg.D, cfg.F)))
+    if cfg.expert_bias:
+        specs += [("b1", (cfg.F,)), ("b2", (cfg.D,))]
+    return specs
+
+
+def expert_slice(cfg: MoeConfig, tensor: str, e: int) -> torch.Tensor:
+    """Regenerate one expert's parameter alone ("normal0.02" recipe only)."""
+    if cfg.init != "normal0.02":
+        raise ValueError("expert_slice is defined for the normal0.02 recipe")
+    shape = dict(_expert_tensor_specs(cfg))[tensor]
+    return _normal(shape, _stream_seed(cfg.seed, tensor, e), _STD_W, _TORCH_DTYPE[cfg.dtype])
+
+
+def _gen_p5(cfg: MoeConfig, parts: Iterable[str]) -> dict:
+    if cfg.dtype != "fp32":
+        raise ValueError("the notebook recipe is fp32")
+    out: dict = {}
+    with torch.random.fork_rng(devices=[]):
+        torch.manual_seed(cfg.seed)
+        router = torch.nn.Linear(cfg.D, cfg.N, bias=False)
+        router.weight.data = torch.randn_like(router.weight.data) * 0.1
+        x = torch.randn(cfg.T, cfg.D)
+        if cfg.x_seed:
+            x = _normal((cfg.T, cfg.D), _stream_seed(cfg.seed, "x", cfg.x_seed), 1.0, torch.float32)
+        out["x"] = x.contiguous()
+        out["w_router"] = router.weight.data.clone().contiguous()
+        out["b_router"] = None
+        if "experts" in parts:
+            torch.manual_seed(cfg.seed + 1)
+            w1, b1, w2, b2 = [], [], [], []
+            for _ in range(cfg.N):
+                fc1 = torch.nn.Linear(cfg.D, cfg.F)
+                fc2 = torch.nn.Linear(cfg.F, cfg.D)
+                w1.append(fc1.weight.data)
+                b1.append(fc1.bias.data)
+                w2.append(fc2.weight.data)
+                b2.append(fc2.bias.data)
+            out["w1"] = torch.stack(w1).contiguous()
+            out["b1"] = torch.stack(b1).contiguous()
+            out["w3"] = None
+            out["w2"] = torch.stack(w2).contiguous()
+            out["b2"] = torch.stack(b2).contiguous()
+    return out
+
+
+def _gen_normal(cfg: MoeConfig, parts: Iterable[str]) -> dict:
+    dt = _TORCH_DTYPE[cfg.dtype]
+    out: dict = {}
+    if "x" in parts:
+        out["x"] = _normal((cfg.T, cfg.D), _stream_seed(cfg.seed, "x", cfg.x_seed), 1.0, dt)
+    if "router" in parts:
+        out["w_router"] = _normal((cfg.N, cfg.D), _stream_seed(cfg.seed, "router", 0), _STD_W, dt)
+        if cfg.router_bias is None:
+            out["b_router"] = None
+        elif cfg.router_bias == "zipf1.2":
+            out["b_router"] = zipf_router_bias(cfg.N, 1.2)
+        else:
+            raise ValueError(f"unknown router bias recipe {cfg.router_bias!r}")
+    if "experts" in parts:
+        specs = _expert_tensor_specs(cfg)
+        jobs = []
+        for name, shape in specs:
+            t = torch.empty((cfg.N,) + shape, dtype=dt)
+            out[name] = t
+            for e in range(cfg.N):
+                jobs.append((t[e], shape, _stream_seed(cfg.seed, name, e)))
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(lambda j: _normal(j[1], j[2], _STD_W, dt, out=j[0]), jobs))
+        for name in ("w3", "b1", "b2"):
+            out.setdefault(name, None)
+    return out
+
+
+def generate(cfg: MoeConfig, parts: Iterable[str] = _ALL_PARTS) -> dict:
+    """Draw the tensors of one instance; ``parts`` may omit "experts"."""
+    parts = tuple(parts)
+    if cfg.init == "p5":
+        return _gen_p5(cfg, parts)
+    if cfg.init == "normal0.02":
+        return _gen_normal(cfg, parts)
+    raise ValueError(f"unknown init recipe {cfg.init!r}")
