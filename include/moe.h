@@ -1,0 +1,169 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: forward pass of one Mixture-of-Experts
+ * FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one described by the notebook "Mixture-of-experts and
+ * expert parallelism" (llm-systems-cookbook, serving track): a linear router
+ * without bias, a softmax over the N experts and the top-k of it ("Top-k
+ * router"); tokens grouped by their chosen expert and run through that
+ * expert's MLP, whose outputs are weighted by the gates and summed back into
+ * token order ("Dispatch and gather"); an optional per-expert slot budget
+ * that drops overflow ("Capacity factor").  The three stages -- input
+ * routing, expert computation, result aggregation -- are also the workflow
+ * named in "MoE Parallelism for Inference: Tricks and PyTorch Deep Dive"
+ * ("Why Parallelism Matters in MoE Inference").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are row-major, device memory, allocated and owned by the
+ *   caller.  The library never allocates or frees memory and keeps no state
+ *   besides a cached device-attribute query per device.
+ * - Weights use the nn.Linear layout [out, in], stacked over experts:
+ *     x[T,D], out[T,D]             dtype of the shape (fp32 or bf16)
+ *     w_router[N,D]                dtype of the shape
+ *     b_router[N]                  fp32 (only with MOE_ROUTER_BIAS)
+ *     w1[N,F,D], w3[N,F,D]         dtype of the shape (w3 only for SwiGLU)
+ *     w2[N,D,F]                    dtype of the shape
+ *     b1[N,F], b2[N,D]             dtype of the shape (only with MOE_HAS_BIAS)
+ * - An assignment is a (token t, choice j) pair with flat index a = t*k + j.
+ *   topk_idx[T,k] and slot[T*k] are int32, topk_gate[T,k] is fp32.
+ * - Every call is asynchronous on the caller's HIP stream (NULL = the null
+ *   stream): outputs are valid once the stream has reached the call.  Calls
+ *   are re-entrant and thread-safe; calls that share output or workspace
+ *   buffers must be ordered by the caller.
+ * - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Arguments are
+ *   validated on the host before any launch; on error nothing is launched.
+ *   T = 0 is a valid no-op.  NaN/Inf inputs give unspecified results.
+ *
+ * Supported shapes: 1 <= N <= 256, 1 <= k <= min(N, 8), T < 2^31 / k.
+ * bf16: D and F multiples of 64.  fp32: D and F multiples of 16.
+ * SwiGLU experts carry no biases (MOE_HAS_BIAS with SWIGLU is unsupported).
+ * T*D, T*k*D, T*k*F and F*D must stay below 2^32 (32-bit offsets).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* same type as hipStream_t */
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad size, flag, null required pointer */
+  MOE_ERR_UNSUPPORTED = -2, /* legal but outside the supported shapes */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+};
+
+enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/* Expert MLP:
+ *   GELU  : y = w2 . gelu(w1 . x + b1) + b2, gelu in its exact erf form
+ *           (the notebook's Expert, "Dispatch and gather")
+ *   RELU  : same with max(0, .) (Switch-style FFN)
+ *   SWIGLU: y = w2 . (silu(w1 . x) * (w3 . x)), silu(z) = z / (1 + e^-z)   */
+enum moe_act { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
+
+enum moe_flags {
+  MOE_RENORM = 1u,      /* gates divided by their sum over the k choices */
+  MOE_RESIDUAL = 2u,    /* out = x + sum of kept, gated expert outputs */
+  MOE_HAS_BIAS = 4u,    /* b1 and b2 are present */
+  MOE_ROUTER_BIAS = 8u  /* b_router is added to the router logits */
+};
+
+typedef struct moe_shape {
+  int64_t T;        /* tokens */
+  int32_t D;        /* model dim */
+  int32_t F;        /* expert hidden dim */
+  int32_t N;        /* experts */
+  int32_t k;        /* experts per token */
+  int32_t capacity; /* slots per expert; -1 = no limit (see moe_capacity) */
+  int32_t dtype;    /* enum moe_dtype */
+  int32_t act;      /* enum moe_act */
+  uint32_t flags;   /* enum moe_flags, or-ed */
+} moe_shape;
+
+/* Per-expert slot budget of the notebook's "Capacity factor" section:
+ * int(T*k/N * cf), evaluated left to right in double and truncated.
+ * cf < 0 (or NaN) returns -1 (no limit); results above INT32_MAX saturate. */
+int32_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf);
+
+/* Bytes of device workspace that moe_expert_ffn and moe_forward need for
+ * this shape (written to *bytes).  The workspace needs 256-byte alignment
+ * and holds no state between calls. */
+int moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Router ("Top-k router"): logits l = x . w_router^T (+ b_router), softmax
+ * over all N, and the k experts with the largest logits in decreasing order,
+ * ties to the lower expert index.  topk_gate[t,j] is the softmax probability
+ * of expert topk_idx[t,j] (divided by the sum over j with MOE_RENORM).
+ * Logits are accumulated in fp32; a token whose top-(k+1) fp32 logits lie
+ * within 1e-4 of each other has all N logits recomputed in fp64 from the
+ * exact products before it is ranked.  logits_opt (fp32 [T,N], may be NULL)
+ * receives the logits used for the ranking, rounded to fp32. */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router,
+              const float* b_router, int32_t* topk_idx, float* topk_gate,
+              float* logits_opt, moe_stream_t stream);
+
+/* Dispatch ("Dispatch and gather", "Capacity factor"): counts[e] = number of
+ * assignments to expert e (before the capacity cut).  The assignments of
+ * expert e are ranked in increasing flat index; the first min(counts[e],
+ * capacity) are kept.  offsets[N+1] is the exclusive scan of the kept counts,
+ * perm[offsets[e] .. offsets[e+1]) lists expert e's kept assignments in rank
+ * order, slot[a] is the row of assignment a in that grouped order or -1 if it
+ * was dropped, and *n_dropped = T*k - offsets[N].  perm must hold T*k
+ * entries; entries past offsets[N] are left untouched.  Expert ids outside
+ * [0, N) are treated as dropped and not counted.  Bit-exact, deterministic. */
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
+                 moe_stream_t stream);
+
+/* Expert MLPs on the grouped rows: for every expert e and every row r in
+ * [offsets[e], offsets[e+1]), token t = perm[r] / k,
+ *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [T*k, D])
+ * Rows past offsets[N] are left untouched.  One launch per layer (fc1+act)
+ * and one for fc2, each a persistent grouped GEMM whose work list covers
+ * column shards of w1/w3 and row shards of w2 for all experts at once (the
+ * row/column expert decomposition of "Accelerating MoE Model Inference with
+ * Expert Sharding", abstract), or a fused weight-streaming kernel when the
+ * rows per expert are few.  fp32 accumulation; the hidden activations are
+ * held in the shape's dtype.  ws/ws_bytes: see moe_workspace_bytes. */
+int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
+                   const int32_t* offsets, const void* w1, const void* b1, const void* w3,
+                   const void* w2, const void* b2, void* y_perm, void* ws, size_t ws_bytes,
+                   moe_stream_t stream);
+
+/* Combine ("Dispatch and gather"): out[t] = (x[t] with MOE_RESIDUAL, else 0)
+ * + sum over j = 0..k-1 with slot[t*k+j] >= 0 of topk_gate[t,j] *
+ * y_perm[slot[t*k+j]], summed in fp32 in increasing j and rounded once to
+ * the shape's dtype.  A token with every choice dropped gets exactly 0, or
+ * exactly x[t] with MOE_RESIDUAL.  x_residual may be NULL without
+ * MOE_RESIDUAL. */
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* slot,
+                const float* topk_gate, const void* x_residual, void* out,
+                moe_stream_t stream);
+
+/* The whole layer: moe_route, moe_dispatch, the expert MLPs and the combine,
+ * stream-ordered, with the intermediate tensors in ws.  The routing outputs
+ * (topk_idx, topk_gate, counts, offsets, perm, slot, n_dropped; sizes as
+ * above) are caller buffers so that they can be inspected. */
+int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
+                const float* b_router, const void* w1, const void* b1, const void* w3,
+                const void* w2, const void* b2, void* out, int32_t* topk_idx,
+                float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* perm,
+                int32_t* slot, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/* Static, human-readable text of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

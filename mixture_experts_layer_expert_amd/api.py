@@ -1,0 +1,174 @@
+"""Python binding of the C ABI (include/moe.h): argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, checks that
+their dtype, device and contiguity match what the C entry point reads, and
+passes raw pointers plus the current HIP stream.  Every step of the layer runs
+in the HIP library; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_DT = {"fp32": (L.MOE_DTYPE_F32, torch.float32), "bf16": (L.MOE_DTYPE_BF16, torch.bfloat16)}
+_ACT = {"gelu": L.MOE_ACT_GELU, "relu": L.MOE_ACT_RELU, "swiglu": L.MOE_ACT_SWIGLU}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = L.load().moe_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class MoeShape:
+    T: int
+    D: int
+    F: int
+    N: int
+    k: int
+    capacity: int = -1
+    dtype: str = "bf16"
+    act: str = "swiglu"
+    renorm: bool = False
+    residual: bool = False
+    has_bias: bool = False
+    router_bias: bool = False
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _DT[self.dtype][1]
+
+    def c(self) -> L.MoeShapeC:
+        flags = ((L.MOE_RENORM if self.renorm else 0) | (L.MOE_RESIDUAL if self.residual else 0)
+                 | (L.MOE_HAS_BIAS if self.has_bias else 0)
+                 | (L.MOE_ROUTER_BIAS if self.router_bias else 0))
+        return L.MoeShapeC(self.T, self.D, self.F, self.N, self.k, self.capacity,
+                           _DT[self.dtype][0], _ACT[self.act], flags)
+
+    @staticmethod
+    def from_config(cfg, T: Optional[int] = None) -> "MoeShape":
+        T = cfg.T if T is None else T
+        cap = capacity(T, cfg.k, cfg.N, -1.0 if cfg.cf is None else cfg.cf)
+        return MoeShape(T=T, D=cfg.D, F=cfg.F, N=cfg.N, k=cfg.k, capacity=cap, dtype=cfg.dtype,
+                        act=cfg.act, renorm=cfg.renorm, residual=cfg.residual,
+                        has_bias=cfg.expert_bias, router_bias=cfg.router_bias is not None)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != L.MOE_OK:
+        raise MoeError(fn, status)
+
+
+def capacity(T: int, k: int, N: int, cf: float) -> int:
+    return int(L.load().moe_capacity(T, k, N, float(cf)))
+
+
+def workspace_bytes(shape: MoeShape) -> int:
+    n = ctypes.c_size_t(0)
+    sc = shape.c()
+    _check("moe_workspace_bytes", L.load().moe_workspace_bytes(ctypes.byref(sc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def route(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, logits=None, stream=None):
+    dt = shape.torch_dtype
+    sc = shape.c()
+    _check("moe_route", L.load().moe_route(
+        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(logits, torch.float32, "logits"),
+        _stream(stream)))
+
+
+def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None):
+    i32 = torch.int32
+    sc = shape.c()
+    _check("moe_dispatch", L.load().moe_dispatch(
+        ctypes.byref(sc), _ptr(topk_idx, i32, "topk_idx"), _ptr(counts, i32, "counts"),
+        _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"), _ptr(slot, i32, "slot"),
+        _ptr(n_dropped, i32, "n_dropped"), _stream(stream)))
+
+
+def expert_ffn(shape: MoeShape, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, stream=None):
+    dt = shape.torch_dtype
+    i32 = torch.int32
+    sc = shape.c()
+    _check("moe_expert_ffn", L.load().moe_expert_ffn(
+        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(perm, i32, "perm"), _ptr(offsets, i32, "offsets"),
+        _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"), _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"),
+        _ptr(b2, dt, "b2"), _ptr(y_perm, dt, "y_perm"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def combine(shape: MoeShape, y_perm, slot, topk_gate, x_residual, out, stream=None):
+    dt = shape.torch_dtype
+    sc = shape.c()
+    _check("moe_combine", L.load().moe_combine(
+        ctypes.byref(sc), _ptr(y_perm, dt, "y_perm"), _ptr(slot, torch.int32, "slot"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(x_residual, dt, "x_residual"),
+        _ptr(out, dt, "out"), _stream(stream)))
+
+
+def forward(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, topk_idx, topk_gate,
+            counts, offsets, perm, slot, n_dropped, ws, stream=None):
+    dt = shape.torch_dtype
+    i32 = torch.int32
+    sc = shape.c()
+    _check("moe_forward", L.load().moe_forward(
+        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+        _ptr(b_router, torch.float32, "b_router"), _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"),
+        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), _ptr(b2, dt, "b2"), _ptr(out, dt, "out"),
+        _ptr(topk_idx, i32, "topk_idx"), _ptr(topk_gate, torch.float32, "topk_gate"),
+        _ptr(counts, i32, "counts"), _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"),
+        _ptr(slot, i32, "slot"), _ptr(n_dropped, i32, "n_dropped"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class MoeBuffers:
+    """Device buffers of one layer call (outputs, routing tensors, workspace),
+    allocated once with torch so that repeated calls allocate nothing."""
+
+    def __init__(self, shape: MoeShape, device="cuda"):
+        self.shape = shape
+        A = shape.T * shape.k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.out = torch.empty(shape.T, shape.D, dtype=shape.torch_dtype, device=device)
+        self.topk_idx = torch.empty(shape.T, shape.k, **i32)
+        self.topk_gate = torch.empty(shape.T, shape.k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(shape.N, **i32)
+        self.offsets = torch.empty(shape.N + 1, **i32)
+        self.perm = torch.empty(max(A, 1), **i32)
+        self.slot = torch.empty(max(A, 1), **i32)
+        self.n_dropped = torch.empty(1, **i32)
+        self.ws = torch.empty(max(workspace_bytes(shape), 256), dtype=torch.uint8, device=device)
+
+    def forward(self, x, p: dict, stream=None):
+        forward(self.shape, x, p["w_router"], p.get("b_router"), p["w1"], p.get("b1"), p.get("w3"),
+                p["w2"], p.get("b2"), self.out, self.topk_idx, self.topk_gate, self.counts,
+                self.offsets, self.perm, self.slot, self.n_dropped, self.ws, stream)
+        return self.out

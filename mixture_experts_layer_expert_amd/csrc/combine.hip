@@ -1,0 +1,86 @@
+// Combine: gate-weighted sum of each token's kept expert outputs, back in
+// token order ("Dispatch and gather" section of the notebook
+// "Mixture-of-experts and expert parallelism": the output starts at zero and
+// receives every chosen expert's output scaled by its gate).  With a
+// residual the start value is x instead (dropped tokens pass through).
+//
+// Memory-bound: each token reads k rows of y_perm (+ x) and writes one row.
+// A workgroup walks tokens; its threads cover the row in 16-byte chunks.
+// The sum runs in fp32 in increasing choice order, so it is deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<bf16> {
+  static constexpr int W = 8;
+  typedef bf16x8 type;
+};
+template <>
+struct Vec<float> {
+  static constexpr int W = 4;
+  typedef f32x4 type;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot,
+                                                      const float* __restrict__ gate,
+                                                      const T* __restrict__ x, T* __restrict__ out,
+                                                      int64_t T_, int D, int k) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  const int chunks = D / W;
+  for (int64_t t = blockIdx.x; t < T_; t += gridDim.x) {
+    int s[kMaxTopK];
+    float g[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      s[j] = (j < k) ? slot[t * k + j] : -1;
+      g[j] = (j < k) ? gate[t * k + j] : 0.f;
+    }
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+      float acc[W];
+      if (x) {
+        V xv = *(const V*)(x + t * D + c * W);
+#pragma unroll
+        for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < W; ++u) acc[u] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (s[j] >= 0) {
+          V yv = *(const V*)(y + (int64_t)s[j] * D + c * W);
+#pragma unroll
+          for (int u = 0; u < W; ++u) acc[u] = fmaf(g[j], (float)yv[u], acc[u]);
+        }
+      }
+      V o;
+#pragma unroll
+      for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
+      *(V*)(out + t * D + c * W) = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
+                          const float* gate, const void* x_res, void* out, hipStream_t st) {
+  const int64_t grid64 = s.T < (int64_t)device_cu_count() * 16 ? s.T : (int64_t)device_cu_count() * 16;
+  const dim3 grid((unsigned)grid64);
+  const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
+  if (s.dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)y_perm, slot, gate,
+                       (const bf16*)xr, (bf16*)out, s.T, s.D, s.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, (const float*)y_perm, slot, gate,
+                       (const float*)xr, (float*)out, s.T, s.D, s.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,183 @@
+// Grouped GEMM of the expert MLPs in fp32 (VALU), for fp32 layers such as
+// the notebook's own 1024-token example ("Dispatch and gather" section of
+// "Mixture-of-experts and expert parallelism").  Same contract and work list
+// as the bf16 MFMA kernel: (expert, 64-row tile, 64-column tile) items for
+// all experts in one persistent launch; rows of x gathered through perm for
+// fc1; bias + GELU/ReLU or SwiGLU fused into the store.
+//
+// Tile: 64x64 outputs, 256 threads, 4x4 outputs per thread, k step 16,
+// operands staged k-major in LDS so that each thread reads 4 rows and 4
+// columns as float4s.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int TBM = 64, TBN = 64, TBK = 16;
+
+struct ParamsF {
+  const float* A;
+  const int32_t* perm;
+  int topk;
+  const int32_t* offsets;
+  int n_experts;
+  const float* B;
+  const float* B2;
+  const float* bias;
+  float* C;
+  int K;
+  int n_out;
+  int act;
+};
+
+__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
+__device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(ParamsF p) {
+  __shared__ float sA[TBK][TBM + 4];
+  __shared__ float sB[TBK][TBN + 4];
+  __shared__ float sB2[SWIGLU ? TBK : 1][TBN + 4];
+  __shared__ int s_tile_start[kMaxExperts + 1];
+  __shared__ int s_scan[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int N = p.n_experts;
+  const int ntiles = (p.n_out + TBN - 1) / TBN;
+
+  int my_tiles = 0;
+  if (tid < N) {
+    int rows = p.offsets[tid + 1] - p.offsets[tid];
+    my_tiles = ((rows + TBM - 1) / TBM) * ntiles;
+    s_scan[tid] = my_tiles;
+  }
+  __syncthreads();
+  for (int d = 1; d < kMaxExperts; d <<= 1) {
+    int v = 0;
+    if (tid < N && tid >= d) v = s_scan[tid - d];
+    __syncthreads();
+    if (tid < N && tid >= d) s_scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < N) s_tile_start[tid] = s_scan[tid] - my_tiles;
+  if (tid == 0) s_tile_start[N] = (N > 0) ? s_scan[N - 1] : 0;
+  __syncthreads();
+  const int total = s_tile_start[N];
+
+  const int tr = tid / 16, tc = tid % 16;  // 16x16 threads, 4x4 outputs each
+  // loader mapping: 64 rows x 16 k = 1024 floats = 256 float4s
+  const int ld_row = tid / 4, ld_k4 = (tid % 4) * 4;
+
+  for (int L = blockIdx.x; L < total; L += gridDim.x) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_tile_start[mid] <= L) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int row_begin = p.offsets[e];
+    const int rows_e = p.offsets[e + 1] - row_begin;
+    const int mtiles = (rows_e + TBM - 1) / TBM;
+    const int local = L - s_tile_start[e];
+    const int mt = local % mtiles, nt = local / mtiles;
+    const int row0 = row_begin + mt * TBM, row_end = row_begin + rows_e;
+    const int n0 = nt * TBN;
+
+    int r = row0 + ld_row;
+    if (r > row_end - 1) r = row_end - 1;
+    const int src = p.perm ? p.perm[r] / p.topk : r;
+    const float* a_src = p.A + (size_t)src * p.K + ld_k4;
+    int fb = n0 + ld_row;
+    if (fb > p.n_out - 1) fb = p.n_out - 1;
+    const float* b_src = p.B + ((size_t)e * p.n_out + fb) * p.K + ld_k4;
+    const float* b2_src = SWIGLU ? p.B2 + ((size_t)e * p.n_out + fb) * p.K + ld_k4 : nullptr;
+
+    float acc[4][4] = {};
+    float acc3[SWIGLU ? 4 : 1][SWIGLU ? 4 : 1] = {};
+    for (int k0 = 0; k0 < p.K; k0 += TBK) {
+      float4 av = *(const float4*)(a_src + k0);
+      float4 bv = *(const float4*)(b_src + k0);
+      sA[ld_k4 + 0][ld_row] = av.x;
+      sA[ld_k4 + 1][ld_row] = av.y;
+      sA[ld_k4 + 2][ld_row] = av.z;
+      sA[ld_k4 + 3][ld_row] = av.w;
+      sB[ld_k4 + 0][ld_row] = bv.x;
+      sB[ld_k4 + 1][ld_row] = bv.y;
+      sB[ld_k4 + 2][ld_row] = bv.z;
+      sB[ld_k4 + 3][ld_row] = bv.w;
+      if constexpr (SWIGLU) {
+        float4 b3 = *(const float4*)(b2_src + k0);
+        sB2[ld_k4 + 0][ld_row] = b3.x;
+        sB2[ld_k4 + 1][ld_row] = b3.y;
+        sB2[ld_k4 + 2][ld_row] = b3.z;
+        sB2[ld_k4 + 3][ld_row] = b3.w;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < TBK; ++kk) {
+        float4 a4 = *(const float4*)&sA[kk][tr * 4];
+        float4 b4 = *(const float4*)&sB[kk][tc * 4];
+        const float a_[4] = {a4.x, a4.y, a4.z, a4.w};
+        const float b_[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a_[i], b_[j], acc[i][j]);
+        if constexpr (SWIGLU) {
+          float4 c4 = *(const float4*)&sB2[kk][tc * 4];
+          const float c_[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc3[i][j] = fmaf(a_[i], c_[j], acc3[i][j]);
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ro = row0 + tr * 4 + i;
+      if (ro >= row_end) continue;
+      float* crow = p.C + (size_t)ro * p.n_out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = n0 + tc * 4 + j;
+        if (f >= p.n_out) continue;
+        float z = acc[i][j];
+        if constexpr (SWIGLU) {
+          z = silu(z) * acc3[i][j];
+        } else {
+          if (p.bias) z += p.bias[(size_t)e * p.n_out + f];
+          if (p.act == kActGelu) z = gelu_erf(z);
+          else if (p.act == kActRelu) z = fmaxf(z, 0.f);
+        }
+        crow[f] = z;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st) {
+  ParamsF p;
+  p.A = (const float*)g.A;
+  p.perm = g.perm;
+  p.topk = g.topk;
+  p.offsets = g.offsets;
+  p.n_experts = g.n_experts;
+  p.B = (const float*)g.B;
+  p.B2 = (const float*)g.B2;
+  p.bias = (const float*)g.bias;
+  p.C = (float*)g.C;
+  p.K = g.K;
+  p.n_out = g.n_out;
+  p.act = g.act;
+  const int grid = device_cu_count() * 4;
+  if (g.act == kActSwiGLU)
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3(grid), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,224 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, and the stream-ordered launch sequence
+//   route -> dispatch -> fc1(+act) -> fc2 -> combine.
+// No allocation, no synchronisation, no state beyond a per-device CU count.
+#include <atomic>
+#include <cmath>
+#include <limits>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline size_t elem_size(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+int validate(const moe_shape* sp) {
+  if (!sp) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *sp;
+  if (s.T < 0 || s.D <= 0 || s.F <= 0 || s.N <= 0 || s.k <= 0) return MOE_ERR_INVALID_ARG;
+  if (s.k > s.N || s.capacity < -1) return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.act != MOE_ACT_GELU && s.act != MOE_ACT_RELU && s.act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
+  const uint32_t known = MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS;
+  if (s.flags & ~known) return MOE_ERR_INVALID_ARG;
+  if (s.act == MOE_ACT_SWIGLU && (s.flags & MOE_HAS_BIAS)) return MOE_ERR_UNSUPPORTED;
+  if (s.N > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  const int mult = (s.dtype == MOE_DTYPE_BF16) ? 64 : 16;
+  if (s.D % mult || s.F % mult) return MOE_ERR_UNSUPPORTED;
+  // 32-bit element offsets inside the kernels
+  const double lim = 4294967295.0;
+  const double A = (double)s.T * s.k;
+  if (A > 2147483647.0) return MOE_ERR_UNSUPPORTED;
+  if ((double)s.T * s.D > lim || A * s.F > lim || A * s.D > lim || (double)s.F * s.D > lim)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of the expert stage: hidden activations H[T*k, F].
+size_t ffn_ws_bytes(const moe_shape& s) {
+  return align_up((size_t)s.T * s.k * s.F * elem_size(s));
+}
+
+// Workspace of the whole layer: y_perm[T*k, D] followed by the expert stage.
+size_t forward_ws_bytes(const moe_shape& s) {
+  return align_up((size_t)s.T * s.k * s.D * elem_size(s)) + ffn_ws_bytes(s);
+}
+
+int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
+                    const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
+                    void* y_perm, void* ws, hipStream_t st) {
+  const bool bias = (s.flags & MOE_HAS_BIAS) != 0;
+  GroupedGemm fc1{};
+  fc1.A = x;
+  fc1.perm = perm;
+  fc1.topk = s.k;
+  fc1.offsets = offsets;
+  fc1.n_experts = s.N;
+  fc1.a_rows = s.T;
+  fc1.B = w1;
+  fc1.B2 = w3;
+  fc1.bias = bias ? b1 : nullptr;
+  fc1.C = ws;  // H
+  fc1.K = s.D;
+  fc1.n_out = s.F;
+  fc1.act = s.act == MOE_ACT_GELU ? kActGelu : s.act == MOE_ACT_RELU ? kActRelu : kActSwiGLU;
+
+  GroupedGemm fc2{};
+  fc2.A = ws;
+  fc2.perm = nullptr;
+  fc2.topk = 1;
+  fc2.offsets = offsets;
+  fc2.n_experts = s.N;
+  fc2.a_rows = s.T * s.k;
+  fc2.B = w2;
+  fc2.B2 = nullptr;
+  fc2.bias = bias ? b2 : nullptr;
+  fc2.C = y_perm;
+  fc2.K = s.F;
+  fc2.n_out = s.D;
+  fc2.act = kActNone;
+
+  hipError_t e;
+  if (s.dtype == MOE_DTYPE_BF16) {
+    int64_t expect = (s.T * s.k + s.N - 1) / s.N;
+    if (s.capacity >= 0 && expect > s.capacity) expect = s.capacity;
+    e = launch_grouped_gemm_bf16(fc1, expect, st);
+    if (e == hipSuccess) e = launch_grouped_gemm_bf16(fc2, expect, st);
+  } else {
+    e = launch_grouped_gemm_f32(fc1, st);
+    if (e == hipSuccess) e = launch_grouped_gemm_f32(fc2, st);
+  }
+  return hip_status(e);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_capacity(int64_t T, int32_t k, int32_t N, double cf) {
+  if (!(cf >= 0.0) || N <= 0) return -1;
+  const double c = (double)T * (double)k / (double)N * cf;
+  if (c >= 2147483647.0) return std::numeric_limits<int32_t>::max();
+  return (int32_t)std::floor(c);
+}
+
+int moe_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = forward_ws_bytes(*shape);
+  return MOE_OK;
+}
+
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+              int32_t* topk_idx, float* topk_gate, float* logits_opt, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt,
+                                 (hipStream_t)stream));
+}
+
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* slot, int32_t* n_dropped, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!topk_idx || !counts || !offsets || !perm || !slot || !n_dropped) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped,
+                                    (hipStream_t)stream));
+}
+
+int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
+                   const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
+                   void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !perm || !offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (s.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_HAS_BIAS) && (!b1 || !b2)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ffn_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
+  return expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, (hipStream_t)stream);
+}
+
+int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* slot, const float* topk_gate,
+                const void* x_residual, void* out, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!y_perm || !slot || !topk_gate || !out) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_RESIDUAL) && !x_residual) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(s, y_perm, slot, topk_gate, x_residual, out, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
+                void* out, int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                int32_t* perm, int32_t* slot, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !w1 || !w2 || !out || !topk_idx || !topk_gate || !counts || !offsets ||
+      !perm || !slot || !n_dropped)
+    return MOE_ERR_INVALID_ARG;
+  if (s.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_HAS_BIAS) && (!b1 || !b2)) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < forward_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  void* y_perm = ws;
+  void* ffn_ws = (unsigned char*)ws + align_up((size_t)s.T * s.k * s.D * elem_size(s));
+  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, st);
+  if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  int r = expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ffn_ws, st);
+  if (r != MOE_OK) return r;
+  return hip_status(launch_combine(s, y_perm, slot, topk_gate, x, out, st));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

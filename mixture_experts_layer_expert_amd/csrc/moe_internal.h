@@ -1,0 +1,67 @@
+// Internal declarations shared by the HIP translation units of libmoe_mi355x.
+// Nothing here is part of the C ABI (include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+// A token whose fp32 top-(k+1) logits are closer than this is re-ranked from
+// fp64 logits.  fp32 accumulation error at the supported D is ~1e-6.
+constexpr float kRefineMargin = 1e-4f;
+
+enum GemmAct { kActNone = 0, kActGelu = 1, kActRelu = 2, kActSwiGLU = 3 };
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---- launchers (stream-ordered, no synchronisation, return hipError_t) ----
+hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,
+                        int32_t* idx, float* gate, float* logits, hipStream_t st);
+
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
+                           hipStream_t st);
+
+// Grouped GEMM over experts:  C[r, n] = act(sum_k A[row(r), k] * B[e, n, k] + bias[e, n])
+// for r in [offsets[e], offsets[e+1]).  row(r) = perm[r] / topk when perm is
+// non-null (gather of x), else r.  For SwiGLU, B = w1 and B2 = w3 and
+// C[r, n] = silu(A.w1[e,n]) * (A.w3[e,n]).
+struct GroupedGemm {
+  const void* A;
+  const int32_t* perm;
+  int topk;
+  const int32_t* offsets;
+  int n_experts;
+  int64_t a_rows;  // rows addressable in A (for clamping of tail loads)
+  const void* B;
+  const void* B2;
+  const void* bias;
+  void* C;
+  int K;
+  int n_out;
+  int act;  // GemmAct
+};
+
+// Picks the bf16 MFMA tile configuration from the expected rows per expert.
+hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows_per_expert,
+                                    hipStream_t st);
+hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st);
+
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
+                          const float* gate, const void* x_res, void* out, hipStream_t st);
+
+}  // namespace moe

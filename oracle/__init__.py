@@ -4,7 +4,7 @@ Only the tests, the entry module's smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.
 """
 from .moe_oracle import (  # noqa: F401
-    brute_forward, capacity, combine_from_experts, dispatch, drop_rate, expert_counts,
+    brute_forward, capacity, combine_from_experts, combine_rows, dispatch, drop_rate, expert_counts,
     expert_mlp, expert_order, f64, gate_values, gelu_erf, imbalance, moe_forward, relu,
     route, router_logits, select_topk, silu, softmax, switch_aux_loss, topk_margin,
 )

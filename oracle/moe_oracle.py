@@ -285,6 +285,23 @@ def combine_from_experts(x, params: dict, act: str, k: int, gate: np.ndarray,
     return {"y": out, "y_perm": y_perm}
 
 
+def combine_rows(y_perm, slot, gate, k: int, x=None) -> np.ndarray:
+    """Aggregation alone, from given expert output rows: out[t] is the sum
+    over choices j whose assignment t*k+j was kept of gate[t, j] times row
+    slot[t*k+j] of y_perm, plus x[t] when x is given."""
+    y_perm = f64(y_perm)
+    slot = np.asarray(slot).reshape(-1)
+    gate = np.asarray(gate, dtype=np.float64)
+    T = gate.shape[0]
+    out = np.zeros((T, y_perm.shape[1])) if x is None else f64(x).copy()
+    for t in range(T):
+        for j in range(k):
+            s = slot[t * k + j]
+            if s >= 0:
+                out[t] += gate[t, j] * y_perm[s]
+    return out
+
+
 def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                 capacity_slots: Optional[int] = None, residual: bool = False,
                 tokens: Optional[Sequence[int]] = None) -> dict:

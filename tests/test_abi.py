@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports every entry point that include/moe.h
+declares, and rejects bad arguments on the host before any launch.  No call
+here reaches the GPU (every call fails validation or is host-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mixture_experts_layer_expert_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_capacity", "moe_workspace_bytes", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+        assert isinstance(getattr(lib, n), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    from mixture_experts_layer_expert_amd import _lib as L
+    for code in (L.MOE_OK, L.MOE_ERR_INVALID_ARG, L.MOE_ERR_UNSUPPORTED, L.MOE_ERR_WORKSPACE, L.MOE_ERR_HIP):
+        assert lib.moe_status_string(code).decode() not in ("", "unknown status")
+    assert lib.moe_status_string(12345).decode() == "unknown status"
+
+
+def test_capacity_helper_matches_the_notebook_rule(lib):
+    assert lib.moe_capacity(16384, 1, 128, 1.0) == 128
+    assert lib.moe_capacity(16384, 1, 128, 1.5) == 192
+    assert lib.moe_capacity(1024, 2, 8, 1.0) == 256
+    assert lib.moe_capacity(10, 1, 3, 1.0) == 3   # truncation
+    assert lib.moe_capacity(10, 2, 3, 0.0) == 0
+    assert lib.moe_capacity(10, 2, 3, -1.0) == -1
+    assert lib.moe_capacity(10, 2, 3, float("nan")) == -1
+    assert lib.moe_capacity(2**40, 8, 1, 1.0) == 2**31 - 1
+
+
+def _shape(**kw):
+    from mixture_experts_layer_expert_amd import _lib as L
+    base = dict(T=64, D=128, F=256, N=8, k=2, capacity=-1, dtype=L.MOE_DTYPE_BF16,
+                act=L.MOE_ACT_SWIGLU, flags=0)
+    base.update(kw)
+    return L.MoeShapeC(**base)
+
+
+def _ws(lib, s):
+    n = ctypes.c_size_t(0)
+    rc = lib.moe_workspace_bytes(ctypes.byref(s), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_bytes_and_validation(lib):
+    from mixture_experts_layer_expert_amd import _lib as L
+    rc, n = _ws(lib, _shape())
+    assert rc == L.MOE_OK
+    # y_perm[T*k, D] + H[T*k, F], bf16, 256-byte aligned pieces
+    assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2
+    bad = [
+        (dict(k=0), L.MOE_ERR_INVALID_ARG), (dict(k=9, N=16), L.MOE_ERR_UNSUPPORTED),
+        (dict(k=9), L.MOE_ERR_INVALID_ARG), (dict(N=300, k=2), L.MOE_ERR_UNSUPPORTED),
+        (dict(T=-1), L.MOE_ERR_INVALID_ARG), (dict(capacity=-2), L.MOE_ERR_INVALID_ARG),
+        (dict(dtype=7), L.MOE_ERR_INVALID_ARG), (dict(act=5), L.MOE_ERR_INVALID_ARG),
+        (dict(flags=1 << 7), L.MOE_ERR_INVALID_ARG), (dict(D=100), L.MOE_ERR_UNSUPPORTED),
+        (dict(F=96), L.MOE_ERR_UNSUPPORTED), (dict(flags=L.MOE_HAS_BIAS), L.MOE_ERR_UNSUPPORTED),
+        (dict(T=2**31, D=4096), L.MOE_ERR_UNSUPPORTED),
+    ]
+    for kw, want in bad:
+        assert _ws(lib, _shape(**kw))[0] == want, kw
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_bytes(None, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_bytes(ctypes.byref(_shape()), None) == L.MOE_ERR_INVALID_ARG
+    # fp32 needs multiples of 16
+    assert _ws(lib, _shape(dtype=L.MOE_DTYPE_F32, D=48, F=80))[0] == L.MOE_OK
+    assert _ws(lib, _shape(dtype=L.MOE_DTYPE_F32, D=40, F=80))[0] == L.MOE_ERR_UNSUPPORTED
+
+
+def test_entry_points_reject_null_pointers_before_launch(lib):
+    from mixture_experts_layer_expert_amd import _lib as L
+    s = ctypes.byref(_shape())
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert lib.moe_route(s, None, fake, None, fake, fake, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(_shape(flags=L.MOE_ROUTER_BIAS)), fake, fake, None, fake, fake,
+                         None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(s, fake, None, fake, fake, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, None, fake, None, fake, fake, 1 << 30,
+                              None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
+    assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, fake, fake, None, fake, fake, 16,
+                              None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(ctypes.byref(_shape(flags=L.MOE_RESIDUAL)), fake, fake, fake, None, fake,
+                           None) == L.MOE_ERR_INVALID_ARG
+    args = [fake] * 16
+    args[8] = None  # out
+    assert lib.moe_forward(s, *args, fake, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    ok = [fake] * 16
+    ok[2] = None  # b_router unused
+    ok[4] = None  # b1
+    ok[7] = None  # b2
+    assert lib.moe_forward(s, *ok, fake, 10, None) == L.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.moe_forward(s, *ok, ctypes.c_void_p(0x1001), 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    from mixture_experts_layer_expert_amd import _lib as L
+    s = ctypes.byref(_shape(T=0))
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
+    assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None) == L.MOE_OK
+    assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK

@@ -191,3 +191,22 @@ def test_active_parameter_fraction_is_k_over_N():
     dense = 2 * 2 * D * F * T * N
     assert executed / dense == pytest.approx(k / N, abs=0)
     assert math.isclose(r["perm"].size / (T * N), k / N)
+
+
+def test_combine_rows_hand_example_and_consistency():
+    # two tokens, k=2: token 0 keeps both choices, token 1 lost choice 1
+    y_perm = np.array([[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]])
+    slot = np.array([2, 0, 1, -1])
+    gate = np.array([[0.5, 0.25], [0.75, 0.125]])
+    out = oracle.combine_rows(y_perm, slot, gate, 2)
+    assert out.tolist() == [[0.5 * 100 + 0.25 * 1, 0.5 * 200 + 0.25 * 2], [0.75 * 10, 0.75 * 20]]
+    x = np.array([[1.0, 1.0], [2.0, 2.0]])
+    assert np.array_equal(oracle.combine_rows(y_perm, slot, gate, 2, x), out + x)
+    # equals the per-expert loop on a random layer
+    rng = np.random.default_rng(17)
+    T, D, F, N, k = 30, 6, 10, 5, 2
+    p = _params(rng, N, D, F, "gelu", True)
+    xx = rng.standard_normal((T, D))
+    r = oracle.moe_forward(xx, p, k=k, act="gelu", capacity_slots=9, residual=True)
+    y = oracle.combine_rows(r["y_perm"], r["slot"], r["gate"], k, xx)
+    assert np.allclose(y, r["y"], rtol=1e-13, atol=1e-13)
