@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kBatch = 8192;  // assignments staged in LDS at a time
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                             int64_t A, int N, int C,
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
   __shared__ int base[kMaxExperts];
   __shared__ int wcnt[kWavesPerBlock][kMaxExperts];
   __shared__ int scan_tmp[kMaxExperts];
+  __shared__ int ids[kBatch];
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -47,12 +49,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
   for (int i = tid; i < kWavesPerBlock * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
   __syncthreads();
 
-  // pass 1: histogram
-  for (int64_t a = tid; a < A; a += kThreads) {
-    int e = idx[a];
-    if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
+  // pass 1: histogram (batches staged in LDS with coalesced loads)
+  for (int64_t b0 = 0; b0 < A; b0 += kBatch) {
+    const int nb = (int)(A - b0 < kBatch ? A - b0 : kBatch);
+    for (int i = tid; i < nb; i += kThreads) ids[i] = idx[b0 + i];
+    __syncthreads();
+    for (int i = tid; i < nb; i += kThreads) {
+      const int e = ids[i];
+      if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // exclusive scan of kept counts (N <= 256: Hillis-Steele in LDS)
   int kept = 0;
@@ -87,10 +94,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
   while ((1 << bits) < N) ++bits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // pass 2: stable ranks, chunk by chunk
+  // pass 2: stable ranks, chunk by chunk (chunks of a batch read from LDS)
   for (int64_t c0 = 0; c0 < A; c0 += kThreads) {
+    if (c0 % kBatch == 0) {
+      const int nb = (int)(A - c0 < kBatch ? A - c0 : kBatch);
+      __syncthreads();
+      for (int i = tid; i < nb; i += kThreads) ids[i] = idx[c0 + i];
+      __syncthreads();
+    }
     const int64_t a = c0 + tid;
-    int e = (a < A) ? idx[a] : -1;
+    int e = (a < A) ? ids[(int)(a % kBatch)] : -1;
     const bool valid = (e >= 0 && e < N);
     uint64_t same = __ballot(valid);
     for (int b = 0; b < bits; ++b) {

@@ -24,24 +24,36 @@
 // it.  Tiles that are adjacent in the list share a weight panel (row tile
 // varies fastest), so they meet in the same XCD's L2.
 //
-// Tile pipeline.  4 waves.  K is consumed 64 at a time.  Both operand tiles
-// go global -> LDS with global_load_lds_dwordx4 (no register staging), into
-// a 2-stage ring; a wave-instruction fills 1 KiB = 8 rows x 128 B.  Inside a
+// Tile pipeline.  4 waves.  K is consumed 64 at a time (a "job" is one k
+// step of one tile).  Both operand tiles go global -> LDS with
+// global_load_lds_dwordx4 (no register staging) into a 2- or 3-stage ring
+// fed as one continuous stream of jobs, so the next tile's first k steps load
+// while the current tile finishes; a wave-instruction fills 1 KiB = 8 rows x
+// 128 B.  Fragments are read from LDS one k sub-step ahead of the MFMAs.  Inside a
 // row the eight 16-byte chunks are XOR-swizzled by the row index so that the
 // MFMA fragment reads (ds_read_b128, one row per lane) are conflict-free.
 // MFMA v_mfma_f32_32x32x16_bf16 with the weight tile as the first operand:
 // each lane then owns 4 consecutive output columns of one row, which the
 // epilogue stores as 8-byte chunks.
+#include <stdlib.h>
+#include <string.h>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BK = 64;         // k elements per stage (128 bytes per row)
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kStages = 2;
 
-__device__ inline int swz(int row) { return row & 7; }
+// Chunk swizzle.  The LDS serves a 64-lane ds_read_b128 16 lanes at a time
+// from 64 four-byte banks (256 bytes).  A tile row of CPR 16-byte chunks
+// covers CPR*16 bytes, so 256/(CPR*16) consecutive rows share a chunk
+// permutation and fall into distinct bank ranges; XOR-ing the chunk index
+// with (row / that) makes 16 consecutive rows hit 16 distinct 16-byte bank
+// groups.  128-byte rows (BK=64): (row>>1)&7; 64-byte rows (BK=32): (row>>2)&3.
+template <int CPR>
+__device__ inline int swz(int row) {
+  return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -52,19 +64,29 @@ __device__ inline void dma16(const void* g, lds_ptr_t l) {
 __device__ inline float gelu_erf(float z) { return 0.5f * z * (1.f + erff(z * 0.70710678118654752f)); }
 __device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
-template <int BM, int BNB, int WM, int WN>
+template <int BM, int BNB, int WM, int WN, int BK_>
 struct Tile {
-  static constexpr int TM = BM / WM;    // tokens per wave
-  static constexpr int TN = BNB / WN;   // weight rows per wave
-  static constexpr int FM = TM / 32;    // 32-token MFMA tiles per wave
-  static constexpr int FN = TN / 32;    // 32-row MFMA tiles per wave
-  static constexpr int QA = BM / 32;    // A dma instructions per wave per stage
-  static constexpr int QB = BNB / 32;   // B dma instructions per wave per stage
-  static constexpr int kLdsA = BM * BK;   // bf16 elements per stage
+  static constexpr int BK = BK_;            // k elements per stage
+  static constexpr int CPR = BK / 8;        // 16-byte chunks per tile row
+  static constexpr int RPI = 64 / CPR;      // tile rows per dma instruction (1 KiB)
+  static constexpr int NW = WM * WN;        // waves per workgroup
+  static constexpr int THREADS = NW * kWave;
+  static constexpr int TM = BM / WM;        // tokens per wave
+  static constexpr int TN = BNB / WN;       // weight rows per wave
+  static constexpr int FM = TM / 32;        // 32-token MFMA tiles per wave
+  static constexpr int FN = TN / 32;        // 32-row MFMA tiles per wave
+  static constexpr int QA = BM / (RPI * NW);  // A dma instructions per wave per stage
+  static constexpr int QB = BNB / (RPI * NW); // B dma instructions per wave per stage
+  static constexpr int kLdsA = BM * BK;     // bf16 elements per stage
   static constexpr int kLdsB = BNB * BK;
-  static constexpr size_t kLdsBytes = (size_t)kStages * (kLdsA + kLdsB) * 2;
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int kStageBytes = (kLdsA + kLdsB) * 2;
+  // as many stages (2..4) as fit in 150 KiB (room for the work list)
+  static constexpr int kStages = (4 * kStageBytes <= 150 * 1024) ? 4 : (3 * kStageBytes <= 150 * 1024) ? 3 : 2;
+  static constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
+  static_assert(BK == 32 || BK == 64, "BK 32 or 64");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile multiple of 32");
+  static_assert(QA >= 1 && QB >= 1 && QA * RPI * NW == BM && QB * RPI * NW == BNB, "dma split");
 };
 
 struct Params {
@@ -82,20 +104,56 @@ struct Params {
   int act;
 };
 
-template <int BM, int BNB, int WM, int WN, int ACT>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
-  using TL = Tile<BM, BNB, WM, WN>;
+// Waits until at most `younger` jobs' worth of DMA instructions (n per job)
+// are outstanding.  Loads return in issue order, so this means every older
+// job has landed in LDS.  Epilogue stores issued after a job only make the
+// wait stricter.
+template <int NJ>
+__device__ inline void wait_dma(int younger) {
+  if (younger <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (younger == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
+  } else if (younger == 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NJ) : "memory");
+  }
+}
+
+// Block barrier for the stage ring.  __syncthreads() carries a workgroup
+// fence, for which the compiler drains every outstanding vector memory op
+// (vmcnt(0)) -- that would also wait for the DMA of jobs still meant to be
+// in flight.  Here the caller has already waited for the DMA it needs; this
+// only completes the wave's own LDS reads (so no refill can overtake them)
+// and synchronises.  The "memory" clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ inline void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ inline float fast_silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  constexpr int CPR = TL::CPR, RPI = TL::RPI;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
   constexpr int BN_OUT = kSwiGLU ? BNB / 2 : BNB;  // output columns per tile
+  constexpr int NJ = TL::QA + TL::QB;               // dma instructions per job per wave
+  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
+  static_assert(3 * NJ <= 63, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* sA = (bf16*)smem_raw;                       // [kStages][BM][BK]
-  bf16* sB = sA + kStages * TL::kLdsA;              // [kStages][BNB][BK]
+  bf16* sA = (bf16*)smem_raw;                       // [STAGES][BM][BK]
+  bf16* sB = sA + STAGES * TL::kLdsA;               // [STAGES][BNB][BK]
   __shared__ int s_tile_start[kMaxExperts + 1];
   __shared__ int s_scan[kMaxExperts];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int N = p.n_experts;
@@ -129,178 +187,242 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(Params p) {
   const int L_end = min(total, (xcd + 1) * span);
 
   const int KT = p.K / BK;
-  const int lrow = lane / 8;   // row within an 8-row dma group
-  const int lchunk = lane % 8; // physical chunk this lane fills
+  const int lrow = lane / CPR;    // row within the dma instruction's rows
+  const int lchunk = lane % CPR;  // physical chunk this lane fills
 
-  for (int L = L_begin; L < L_end; L += per_xcd) {
-    // expert of tile L: last e with tile_start[e] <= L
-    int lo = 0, hi = N - 1;
+  struct TileInfo {
+    int e, row0, row_end, n0;
+  };
+  auto tile_info = [&](int L) {
+    int lo = 0, hi = N - 1;  // expert of tile L: last e with tile_start[e] <= L
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
       if (s_tile_start[mid] <= L) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int row_begin = p.offsets[e];
-    const int rows_e = p.offsets[e + 1] - row_begin;
+    TileInfo t;
+    t.e = lo;
+    const int row_begin = p.offsets[lo];
+    const int rows_e = p.offsets[lo + 1] - row_begin;
     const int mtiles = (rows_e + BM - 1) / BM;
-    const int local = L - s_tile_start[e];
-    const int mt = local % mtiles;
-    const int nt = local / mtiles;
-    const int row0 = row_begin + mt * BM;
-    const int row_end = row_begin + rows_e;
-    const int n0 = nt * BN_OUT;  // first output column of the tile
+    const int local = L - s_tile_start[lo];
+    t.row0 = row_begin + (local % mtiles) * BM;
+    t.row_end = row_begin + rows_e;
+    t.n0 = (local / mtiles) * BN_OUT;
+    return t;
+  };
 
-    // ---- per-lane source offsets (elements) of the rows this lane loads
-    uint32_t offA[TL::QA];
+  // ---- DMA side: per-lane 32-bit byte offsets of the tile being loaded,
+  // added to wave-uniform base pointers (saddr + voffset addressing).
+  uint32_t offA[TL::QA], offB[TL::QB];
+  const char* b1e = (const char*)p.B;
+  const char* b2e = (const char*)p.B;
+  int L_dma = L_begin, kt_dma = 0, job_issued = 0;
+  auto setup_dma = [&](int L) {
+    const TileInfo t = tile_info(L);
 #pragma unroll
     for (int q = 0; q < TL::QA; ++q) {
-      const int trow = (wave * TL::QA + q) * 8 + lrow;  // row within the A tile
-      int r = row0 + trow;
-      if (r > row_end - 1) r = row_end - 1;  // tail rows re-load a valid row
+      const int trow = (wave * TL::QA + q) * RPI + lrow;  // row within the A tile
+      int r = t.row0 + trow;
+      if (r > t.row_end - 1) r = t.row_end - 1;  // tail rows re-load a valid row
       const int src = p.perm ? (p.perm[r] / p.topk) : r;
-      const int c = lchunk ^ swz(trow);
-      offA[q] = (uint32_t)src * (uint32_t)p.K + (uint32_t)(c * 8);
+      offA[q] = ((uint32_t)src * (uint32_t)p.K + (uint32_t)((lchunk ^ swz<CPR>(trow)) * 8)) * 2u;
     }
-    uint32_t offB[TL::QB];
-    const bf16* baseB[TL::QB];
 #pragma unroll
     for (int q = 0; q < TL::QB; ++q) {
-      const int brow = (wave * TL::QB + q) * 8 + lrow;  // row within the B tile
-      int feat;
-      const bf16* base;
-      if constexpr (kSwiGLU) {
-        const int g = brow / 32;
-        feat = n0 + (g / 2) * 32 + (brow % 32);
-        base = (g & 1) ? p.B2 : p.B;
-        if (feat > p.n_out - 1) feat = p.n_out - 1;  // column tail
-      } else {
-        feat = n0 + brow;
-        base = p.B;
-        if (feat > p.n_out - 1) feat = p.n_out - 1;  // column tail
-      }
-      const int c = lchunk ^ swz(brow);
-      baseB[q] = base + (size_t)e * p.n_out * p.K;
-      offB[q] = (uint32_t)feat * (uint32_t)p.K + (uint32_t)(c * 8);
+      const int brow = (wave * TL::QB + q) * RPI + lrow;  // row within the B tile
+      int feat = kSwiGLU ? t.n0 + (brow / 64) * 32 + (brow % 32) : t.n0 + brow;
+      if (feat > p.n_out - 1) feat = p.n_out - 1;  // column tail
+      offB[q] = ((uint32_t)feat * (uint32_t)p.K + (uint32_t)((lchunk ^ swz<CPR>(brow)) * 8)) * 2u;
     }
-
-    auto issue = [&](int stage, int kt) {
-      bf16* a_dst = sA + stage * TL::kLdsA;
-      bf16* b_dst = sB + stage * TL::kLdsB;
-      const uint32_t koff = (uint32_t)kt * BK;
+    const size_t eoff = (size_t)t.e * p.n_out * p.K * 2;
+    b1e = (const char*)p.B + eoff;
+    b2e = kSwiGLU ? (const char*)p.B2 + eoff : b1e;
+  };
+  auto issue_next = [&]() {
+    if (L_dma >= L_end) return;
+    const int stage = job_issued % STAGES;
+    bf16* a_dst = sA + stage * TL::kLdsA;
+    bf16* b_dst = sB + stage * TL::kLdsB;
+    const size_t kbytes = (size_t)kt_dma * BK * 2;
+    const char* a_base = (const char*)p.A + kbytes;
 #pragma unroll
-      for (int q = 0; q < TL::QA; ++q)
-        dma16(p.A + offA[q] + koff, (lds_ptr_t)(a_dst + (wave * TL::QA + q) * 512));
+    for (int q = 0; q < TL::QA; ++q)
+      dma16(a_base + offA[q], (lds_ptr_t)(a_dst + (wave * TL::QA + q) * 512));
+    const char* b1 = b1e + kbytes;
+    const char* b2 = b2e + kbytes;
 #pragma unroll
-      for (int q = 0; q < TL::QB; ++q)
-        dma16(baseB[q] + offB[q] + koff, (lds_ptr_t)(b_dst + (wave * TL::QB + q) * 512));
-    };
+    for (int q = 0; q < TL::QB; ++q) {
+      // SwiGLU: 32-row groups alternate w1 (even) and w3 (odd)
+      const char* base = (kSwiGLU && ((((wave * TL::QB + q) * RPI) / 32) & 1)) ? b2 : b1;
+      dma16(base + offB[q], (lds_ptr_t)(b_dst + (wave * TL::QB + q) * 512));
+    }
+    ++job_issued;
+    if (++kt_dma == KT) {
+      kt_dma = 0;
+      L_dma += per_xcd;
+      if (L_dma < L_end) setup_dma(L_dma);
+    }
+  };
 
-    f32x16 acc[TL::FN][TL::FM];
+  // Prologue: fill every stage.  At the barrier of job j the stage of job j
+  // is refilled with job j + STAGES, and job j + 1 must already be in flight.
+  if (L_begin < L_end) setup_dma(L_begin);
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) issue_next();
+
+  // ---- compute side: one flat loop over the jobs (tile, k step) of this
+  // workgroup.  Per job, 4 k sub-steps of 16; fragments are read one
+  // sub-step ahead into a second register buffer.  The block barrier sits
+  // before the last sub-step: by then every wave has read all fragments of
+  // the job, so the stage can be refilled, and the first fragments of the
+  // next job are read while the last sub-step's MFMAs run.
+  constexpr int KS = BK / 16;
+  const int n_tiles_mine = (L_end > L_begin) ? (L_end - L_begin + per_xcd - 1) / per_xcd : 0;
+  const int n_jobs = n_tiles_mine * KT;
+  bf16x8 bf[2][TL::FN], af[2][TL::FM];
+  auto load_frags = [&](int stage, int ks, int buf) {
+    const bf16* a_s = sA + stage * TL::kLdsA;
+    const bf16* b_s = sB + stage * TL::kLdsB;
+    const int c = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TL::FN; ++i) {
+      const int row = wn * TL::TN + i * 32 + (lane & 31);
+      bf[buf][i] = *(const bf16x8*)(b_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < TL::FM; ++j) {
+      const int row = wm * TL::TM + j * 32 + (lane & 31);
+      af[buf][j] = *(const bf16x8*)(a_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
+    }
+  };
+  f32x16 acc[TL::FN][TL::FM];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < TL::FN; ++i)
 #pragma unroll
       for (int j = 0; j < TL::FM; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    issue(0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kt + 1 < KT) issue((kt + 1) % kStages, kt + 1);
-      const bf16* a_s = sA + (kt % kStages) * TL::kLdsA;
-      const bf16* b_s = sB + (kt % kStages) * TL::kLdsB;
+  };
+  auto mfmas = [&](int buf) {
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int c = 2 * ks + (lane >> 5);
-        bf16x8 bf[TL::FN], af[TL::FM];
+    for (int i = 0; i < TL::FN; ++i)
 #pragma unroll
-        for (int i = 0; i < TL::FN; ++i) {
-          const int row = wn * TL::TN + i * 32 + (lane & 31);
-          bf[i] = *(const bf16x8*)(b_s + row * BK + ((c ^ swz(row)) * 8));
-        }
+      for (int j = 0; j < TL::FM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[buf][i], af[buf][j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: one fragment read per (FN*FM)/(FN+FM) MFMAs
+  auto interleave = [&]() {
+    constexpr int NR = TL::FN + TL::FM, NM = TL::FN * TL::FM;
+    constexpr int PER = NM / NR > 0 ? NM / NR : 1;
 #pragma unroll
-        for (int j = 0; j < TL::FM; ++j) {
-          const int row = wm * TL::TM + j * 32 + (lane & 31);
-          af[j] = *(const bf16x8*)(a_s + row * BK + ((c ^ swz(row)) * 8));
-        }
-#pragma unroll
-        for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-          for (int j = 0; j < TL::FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[i], af[j], acc[i][j], 0, 0, 0);
-      }
+    for (int r = 0; r < NR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
     }
+  };
 
-    // ---- epilogue: lane owns token column (lane & 31) of each 32x32 tile and
-    // output rows (r/4)*8 + (lane/32)*4 + r%4 of it.
-#pragma unroll
-    for (int j = 0; j < TL::FM; ++j) {
-      const int r_out = row0 + wm * TL::TM + j * 32 + (lane & 31);
-      const bool live = r_out < row_end;
-      bf16* crow = p.C + (size_t)r_out * p.n_out;
-      if constexpr (kSwiGLU) {
-#pragma unroll
-        for (int ip = 0; ip < TL::FN / 2; ++ip) {
-          const int fbase = n0 + (wn * TL::TN / 64 + ip) * 32;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = fbase + q * 8 + (lane >> 5) * 4;
-            bf16x4 v;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float g = acc[2 * ip][j][q * 4 + u];
-              const float up = acc[2 * ip + 1][j][q * 4 + u];
-              v[u] = (bf16)(silu(g) * up);
-            }
-            if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < TL::FN; ++i) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = n0 + wn * TL::TN + i * 32 + q * 8 + (lane >> 5) * 4;
-            bf16x4 v;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              float z = acc[i][j][q * 4 + u];
-              if (p.bias && f < p.n_out) z += (float)p.bias[(size_t)e * p.n_out + f + u];
-              if constexpr (ACT == kActGelu) z = gelu_erf(z);
-              if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
-              v[u] = (bf16)z;
-            }
-            if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
-          }
-        }
-      }
-    }
-    __syncthreads();  // LDS ring is refilled by the next tile
+  int L_cmp = L_begin, kt_cmp = 0;
+  TileInfo tc;
+  if (n_jobs > 0) {
+    tc = tile_info(L_cmp);
+    wait_dma<NJ>(job_issued - 1);
+    ring_barrier();
+    load_frags(0, 0, 0);
   }
+  zero_acc();
+  for (int job = 0; job < n_jobs; ++job) {
+    const int stage = job % STAGES;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      load_frags(stage, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+      interleave();
+    }
+    // all fragments of this job are in registers: refill its stage later
+    const bool more = job + 1 < n_jobs;
+    wait_dma<NJ>(job_issued - (job + 1) - 1);
+    ring_barrier();
+    issue_next();
+    if (more) load_frags((job + 1) % STAGES, 0, KS & 1);
+    mfmas((KS - 1) & 1);
+    if (more) interleave();
+    if (++kt_cmp == KT) {
+      // ---- epilogue: lane owns token column (lane & 31) of each 32x32 tile
+      // and output rows (r/4)*8 + (lane/32)*4 + r%4 of it.
+#pragma unroll
+      for (int j = 0; j < TL::FM; ++j) {
+        const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
+        const bool live = r_out < tc.row_end;
+        bf16* crow = p.C + (size_t)r_out * p.n_out;
+        if constexpr (kSwiGLU) {
+#pragma unroll
+          for (int ip = 0; ip < TL::FN / 2; ++ip) {
+            const int fbase = tc.n0 + (wn * TL::TN / 64 + ip) * 32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int f = fbase + q * 8 + (lane >> 5) * 4;
+              bf16x4 v;
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                v[u] = (bf16)(fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u]);
+              if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < TL::FN; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int f = tc.n0 + wn * TL::TN + i * 32 + q * 8 + (lane >> 5) * 4;
+              bf16x4 bv = {};
+              if (p.bias && f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
+              bf16x4 v;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                float z = acc[i][j][q * 4 + u] + (float)bv[u];
+                if constexpr (ACT == kActGelu) z = gelu_erf(z);
+                if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
+                v[u] = (bf16)z;
+              }
+              if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
+          }
+        }
+      }
+      kt_cmp = 0;
+      L_cmp += per_xcd;
+      if (more) tc = tile_info(L_cmp);
+      zero_acc();
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int BM, int BNB, int WM, int WN, int ACT>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
-  using TL = Tile<BM, BNB, WM, WN>;
-  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, ACT>;
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  constexpr int S = TL::kStages;
+  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, S>;
   // once per process and instantiation (thread-safe static initialisation)
   static const hipError_t attr_err = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::kLdsBytes);
   if (attr_err != hipSuccess) return attr_err;
   int grid = device_cu_count();
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), TL::kLdsBytes, st, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TL::THREADS), TL::kLdsBytes, st, p);
   return hipGetLastError();
 }
 
-template <int BM, int BNB, int WM, int WN>
+template <int BM, int BNB, int WM, int WN, int BK>
 hipError_t launch_act(const Params& p, hipStream_t st) {
   switch (p.act) {
-    case kActGelu: return launch_cfg<BM, BNB, WM, WN, kActGelu>(p, st);
-    case kActRelu: return launch_cfg<BM, BNB, WM, WN, kActRelu>(p, st);
-    case kActSwiGLU: return launch_cfg<BM, BNB, WM, WN, kActSwiGLU>(p, st);
-    default: return launch_cfg<BM, BNB, WM, WN, kActNone>(p, st);
+    case kActGelu: return launch_cfg<BM, BNB, WM, WN, BK, kActGelu>(p, st);
+    case kActRelu: return launch_cfg<BM, BNB, WM, WN, BK, kActRelu>(p, st);
+    case kActSwiGLU: return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU>(p, st);
+    default: return launch_cfg<BM, BNB, WM, WN, BK, kActNone>(p, st);
   }
 }
 
@@ -321,11 +443,21 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.n_out = g.n_out;
   p.act = g.act;
   // Tile choice from the mean rows per expert: large groups use 256x256
-  // tiles (4 waves of 128x128), mid-size groups 128-row tiles, small ones
-  // 32-row tiles.  Output columns per tile: 256 (128 for SwiGLU).
-  if (expected_rows >= 192) return launch_act<256, 256, 2, 2>(p, st);
-  if (expected_rows >= 48) return launch_act<128, 256, 1, 4>(p, st);
-  return launch_act<32, 256, 1, 4>(p, st);
+  // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64),
+  // small ones 32x256 (4 waves of 32x64).  Output columns per tile: 256 (128
+  // for SwiGLU).
+  // MOE_GEMM_TILE (tuning): force one of the instantiated tile shapes.
+  static const char* forced = getenv("MOE_GEMM_TILE");
+  if (forced) {
+    if (!strcmp(forced, "256x256w8k64")) return launch_act<256, 256, 2, 4, 64>(p, st);
+    if (!strcmp(forced, "256x256w8k32")) return launch_act<256, 256, 2, 4, 32>(p, st);
+    if (!strcmp(forced, "128x256w8k64")) return launch_act<128, 256, 2, 4, 64>(p, st);
+    if (!strcmp(forced, "128x256w8k32")) return launch_act<128, 256, 2, 4, 32>(p, st);
+    if (!strcmp(forced, "32x256w4k64")) return launch_act<32, 256, 1, 4, 64>(p, st);
+  }
+  if (expected_rows >= 192) return launch_act<256, 256, 2, 4, 64>(p, st);
+  if (expected_rows >= 48) return launch_act<128, 256, 2, 4, 64>(p, st);
+  return launch_act<32, 256, 1, 4, 64>(p, st);
 }
 
 }  // namespace moe

@@ -43,11 +43,11 @@ int validate(const moe_shape* sp) {
   if (s.N > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   const int mult = (s.dtype == MOE_DTYPE_BF16) ? 64 : 16;
   if (s.D % mult || s.F % mult) return MOE_ERR_UNSUPPORTED;
-  // 32-bit element offsets inside the kernels
+  // 32-bit byte offsets inside the kernels
   const double lim = 4294967295.0;
   const double A = (double)s.T * s.k;
   if (A > 2147483647.0) return MOE_ERR_UNSUPPORTED;
-  if ((double)s.T * s.D > lim || A * s.F > lim || A * s.D > lim || (double)s.F * s.D > lim)
+  if ((double)s.T * s.D * 4 > lim || A * s.F * 4 > lim || A * s.D * 4 > lim || (double)s.F * s.D * 4 > lim)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

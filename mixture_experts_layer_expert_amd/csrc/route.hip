@@ -1,16 +1,16 @@
 // Router: logits, softmax and top-k of every token ("Top-k router" section of
 // the notebook "Mixture-of-experts and expert parallelism").
 //
-// One block = 4 waves = 64 tokens, 16 tokens per wave.
-//  1. bf16: each wave computes its 16x(16*NT) logit tile with
-//     v_mfma_f32_16x16x32_bf16, operands read straight from global memory
-//     (x rows are used once; the router matrix is L2-resident).  fp32: VALU
-//     dot products.  The tile goes to LDS.
+// One block = 4 waves = 32 tokens.
+//  1. bf16: the block's 32x(16*NT) logit tile is computed with
+//     v_mfma_f32_16x16x32_bf16, D split 4 ways over the waves (partial tiles
+//     summed in LDS), operands read straight from global memory (x rows are
+//     used once; the router matrix is L2-resident).  fp32: VALU dot products.
 //  2. A 16-lane group ranks one token: every lane owns experts l, l+16, ...;
 //     k+1 rounds of (value, index) arg-max over the group with xor shuffles.
 //     Larger value wins, equal values go to the lower expert index.
 //  3. If two of the top-(k+1) fp32 logits are closer than kRefineMargin, the
-//     wave recomputes that token's logits in fp64 from exact products
+//     whole block recomputes that token's logits in fp64 from exact products
 //     (bf16*bf16 and fp32*fp32 are exact in fp64) and ranks those instead.
 //  4. Gates are softmax probabilities of the chosen experts, optionally
 //     renormalised over the k choices.
@@ -21,10 +21,6 @@
 
 namespace moe {
 namespace {
-
-constexpr int kTokPerWave = 16;
-constexpr int kWaves = 4;
-constexpr int kTokPerBlock = kTokPerWave * kWaves;
 
 struct RouteArgs {
   const void* x;
@@ -138,31 +134,38 @@ __device__ inline double to_f64(T v) { return (double)(float)v; }
 template <>
 __device__ inline double to_f64<float>(float v) { return (double)v; }
 
-// fp64 logits of token t for all N experts, written to dl[0..N).  The wave
-// splits D over its 64 lanes and reduces with xor shuffles.
+// Chunk of 16 bytes of the input dtype.
 template <typename T>
-__device__ void refine_logits(const RouteArgs& a, int64_t t, int lane, double* dl) {
-  const T* x = (const T*)a.x + t * (int64_t)a.D;
-  const T* w = (const T*)a.wr;
-  for (int e = 0; e < a.N; ++e) {
-    const T* we = w + (int64_t)e * a.D;
-    double s = 0.0;
-    for (int d = lane; d < a.D; d += kWave) s = fma(to_f64(x[d]), to_f64(we[d]), s);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (lane == 0) dl[e] = s + (a.has_bias ? (double)a.br[e] : 0.0);
-  }
-}
+struct Chunk;
+template <>
+struct Chunk<bf16> {
+  static constexpr int W = 8;
+  typedef bf16x8 type;
+};
+template <>
+struct Chunk<float> {
+  static constexpr int W = 4;
+  typedef f32x4 type;
+};
 
-// fp32 logits of the wave's 16 tokens with bf16 MFMA, into lds[16][ldl].
-template <int NT>
-__device__ void logits_bf16(const RouteArgs& a, int64_t t0, int lane, float* lds, int ldl) {
+// fp32 partial logits of the block's 32 tokens with bf16 MFMA.  Wave w takes
+// the 32-wide k steps w, w+4, w+8, ... (4-way split of D); each lane loads its
+// 16-byte fragments straight from global memory, U steps at a time so that
+// several loads are in flight.  Result: lg[token][expert].  Contains block
+// barriers: every thread of the block must call it.
+template <int NT, int U>
+__device__ void logits_bf16(const RouteArgs& a, int64_t t0, int wave, int lane, float* lg,
+                            int ldl) {
   const bf16* x = (const bf16*)a.x;
   const bf16* wr = (const bf16*)a.wr;
   const int D = a.D;
-  int64_t row = t0 + (lane & 15);
-  if (row > a.T - 1) row = a.T - 1;
-  const bf16* xa = x + row * D + (lane >> 4) * 8;
+  const bf16* xa[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    int64_t row = t0 + m * 16 + (lane & 15);
+    if (row > a.T - 1) row = a.T - 1;
+    xa[m] = x + row * D + (lane >> 4) * 8;
+  }
   const bf16* wb[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -170,101 +173,160 @@ __device__ void logits_bf16(const RouteArgs& a, int64_t t0, int lane, float* lds
     if (e > a.N - 1) e = a.N - 1;
     wb[nt] = wr + (int64_t)e * D + (lane >> 4) * 8;
   }
-  f32x4 acc[NT];
+  f32x4 acc[2][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < D; kk += 32) {
-    bf16x8 av = *(const bf16x8*)(xa + kk);
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      bf16x8 bv = *(const bf16x8*)(wb[nt] + kk);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nt], 0, 0, 0);
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = D / 32;
+  for (int s0 = wave; s0 < steps; s0 += 4 * U) {
+    bf16x8 av[U][2], bv[U][NT];
+    // MFMAs run whatever the EXEC mask is, so an out-of-range step gets zero
+    // operands (adding exactly 0) instead of being skipped by a branch.
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + 4 * u;
+      const bool in = s < steps;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) av[u][m] = in ? *(const bf16x8*)(xa[m] + s * 32) : bf16x8{};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bv[u][nt] = in ? *(const bf16x8*)(wb[nt] + s * 32) : bf16x8{};
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][m], bv[u][nt], acc[m][nt], 0, 0, 0);
   }
-  const float* br = a.br;
+  // Sum the four partial tiles into lg in fixed wave order (deterministic);
+  // wave 0 adds the router bias.
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int e = nt * 16 + (lane & 15);
-    float b = (a.has_bias && e < a.N) ? br[e] : 0.f;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = nt * 16 + (lane & 15);
+        const float b = (w == 0 && a.has_bias && e < a.N) ? a.br[e] : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lds[(4 * (lane >> 4) + r) * ldl + e] = acc[nt][r] + b;
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* dst = &lg[(m * 16 + 4 * (lane >> 4) + r) * ldl + e];
+            *dst = (w == 0 ? b : *dst) + acc[m][nt][r];
+          }
+      }
+    }
+    __syncthreads();
   }
 }
 
-// fp32 logits with VALU fma: lane = token (lane & 15), experts lane>>4, +4, ...
-__device__ void logits_f32(const RouteArgs& a, int64_t t0, int lane, float* lds, int ldl) {
+// fp32 logits with VALU fma (fp32 layers): thread = (token, expert subset).
+__device__ void logits_f32(const RouteArgs& a, int64_t t0, int tid, float* lg, int ldl) {
   const float* x = (const float*)a.x;
   const float* wr = (const float*)a.wr;
   const int D = a.D;
-  int64_t row = t0 + (lane & 15);
+  const int r = tid / 8;  // 32 tokens x 8 threads
+  int64_t row = t0 + r;
   if (row > a.T - 1) row = a.T - 1;
-  const float4* xr = (const float4*)(x + row * D);
-  for (int e = lane >> 4; e < a.N; e += 4) {
-    const float4* we = (const float4*)(wr + (int64_t)e * D);
+  const f32x4* xr = (const f32x4*)(x + row * D);
+  for (int e = tid % 8; e < a.N; e += 8) {
+    const f32x4* we = (const f32x4*)(wr + (int64_t)e * D);
     float s = 0.f;
     for (int d = 0; d < D / 4; ++d) {
-      float4 xv = xr[d], wv = we[d];
-      s = fmaf(xv.x, wv.x, s);
-      s = fmaf(xv.y, wv.y, s);
-      s = fmaf(xv.z, wv.z, s);
-      s = fmaf(xv.w, wv.w, s);
+      f32x4 xv = xr[d], wv = we[d];
+      s = fmaf(xv[0], wv[0], s);
+      s = fmaf(xv[1], wv[1], s);
+      s = fmaf(xv[2], wv[2], s);
+      s = fmaf(xv[3], wv[3], s);
     }
-    lds[(lane & 15) * ldl + e] = s + (a.has_bias ? a.br[e] : 0.f);
+    lg[r * ldl + e] = s + (a.has_bias ? a.br[e] : 0.f);
   }
 }
 
+// Exact-product fp64 logits of token t, computed by the whole block: thread
+// (expert e = tid % N, slice s = tid / N) sums its share of the D/8 (bf16) or
+// D/4 (fp32) 16-byte chunks of row e of the router against the same chunks
+// of the token's row; the slices are then added per expert into dl.
+template <typename T>
+__device__ void refine_block(const RouteArgs& a, int64_t t, int tid, double* dp, double* dl) {
+  constexpr int W = Chunk<T>::W;
+  typedef typename Chunk<T>::type V;
+  const int D = a.D, N = a.N;
+  const V* xv = (const V*)((const T*)a.x + t * (int64_t)D);
+  const int S = (256 / N) > 0 ? 256 / N : 1;
+  const int e = tid % N, s = tid / N;
+  if (s < S) {
+    const int chunks = D / W;
+    const int c0 = (int)((int64_t)chunks * s / S), c1 = (int)((int64_t)chunks * (s + 1) / S);
+    const V* wv = (const V*)((const T*)a.wr + (int64_t)e * D);
+    double acc = 0.0;
+#pragma unroll 4
+    for (int c = c0; c < c1; ++c) {
+      V v = wv[c], u8 = xv[c];
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc = fma(to_f64(u8[u]), to_f64(v[u]), acc);
+    }
+    dp[s * N + e] = acc;
+  }
+  __syncthreads();
+  if (tid < N) {
+    double sum = a.has_bias ? (double)a.br[tid] : 0.0;
+    for (int j = 0; j < S; ++j) sum += dp[j * N + tid];
+    dl[tid] = sum;
+  }
+  __syncthreads();
+}
+
+// Block = 4 waves = 32 tokens.
 template <typename T, int NT>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   constexpr int ldl = 16 * NT + 1;
-  __shared__ float lds_all[kTokPerBlock * ldl];
-  __shared__ double dl_all[kWaves][16 * NT];
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int64_t t0 = (int64_t)blockIdx.x * kTokPerBlock + wave * kTokPerWave;
-  float* lds = lds_all + wave * kTokPerWave * ldl;
-  double* dl = dl_all[wave];
+  constexpr int U = NT >= 8 ? 1 : (NT >= 4 ? 2 : 4);
+  __shared__ float lg[32 * ldl];  // logits of the block's 32 tokens
+  __shared__ double dp[256];
+  __shared__ double dl[16 * NT];
+  __shared__ int flagged[32];
+  __shared__ int nflag;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int64_t t0 = (int64_t)blockIdx.x * 32;
+  if (tid == 0) nflag = 0;
 
   if constexpr (sizeof(T) == 2) {
-    logits_bf16<NT>(a, t0, lane, lds, ldl);
+    logits_bf16<NT, U>(a, t0, wave, lane, lg, ldl);
   } else {
-    logits_f32(a, t0, lane, lds, ldl);
+    logits_f32(a, t0, tid, lg, ldl);
+    __syncthreads();
   }
-  __syncthreads();
 
   const int grp = lane >> 4, l16 = lane & 15;
-  uint32_t need = 0;  // tokens of this wave (bit = token within wave) to refine
-  for (int it = 0; it < 4; ++it) {
-    const int tk = it * 4 + grp;
-    const int64_t t = t0 + tk;
-    bool ok = group_rank<float, NT>(lds + tk * ldl, a, t, l16, kRefineMargin, false);
+  for (int it = 0; it < 2; ++it) {
+    const int r = it * 16 + wave * 4 + grp;
+    const int64_t t = t0 + r;
+    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
     if (a.logits && t < a.T)
-      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lds[tk * ldl + e];
-    uint64_t bad = __ballot(!ok && l16 == 0 && t < a.T);
-    for (int g = 0; g < 4; ++g)
-      if ((bad >> (16 * g)) & 1ull) need |= 1u << (it * 4 + g);
+      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
+    if (!ok && l16 == 0 && t < a.T) flagged[atomicAdd(&nflag, 1)] = r;
   }
-  while (need) {
-    const int tk = __builtin_ctz(need);
-    need &= need - 1;
-    const int64_t t = t0 + tk;
-    refine_logits<T>(a, t, lane, dl);
-    // dl is private to this wave: order its LDS traffic at wavefront scope
-    // (waves refine different numbers of tokens, so no block barrier here).
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (grp == 0) {
+  __syncthreads();
+  const int nf = nflag;  // block-uniform
+  for (int i = 0; i < nf; ++i) {
+    const int r = flagged[i];
+    const int64_t t = t0 + r;
+    refine_block<T>(a, t, tid, dp, dl);
+    if (wave == 0 && grp == 0) {
       group_rank<double, NT>(dl, a, t, l16, -1.0, true);
       if (a.logits)
         for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = (float)dl[e];
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
   }
 }
 
 template <typename T, int NT>
 hipError_t launch_nt(const RouteArgs& a, hipStream_t st) {
-  const int64_t blocks = (a.T + kTokPerBlock - 1) / kTokPerBlock;
+  const int64_t blocks = (a.T + 31) / 32;
   hipLaunchKernelGGL((route_kernel<T, NT>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }

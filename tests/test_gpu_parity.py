@@ -53,10 +53,18 @@ def _route_case(gpu, x, w, k, renorm=False, b=None):
                          router_bias=b is not None)
     idx = torch.empty(T, k, dtype=torch.int32, device=gpu)
     gate = torch.empty(T, k, dtype=torch.float32, device=gpu)
-    api.route(shape, x.to(gpu), w.to(gpu), None if b is None else b.to(gpu), idx, gate)
+    logits = torch.empty(T, N, dtype=torch.float32, device=gpu)
+    api.route(shape, x.to(gpu), w.to(gpu), None if b is None else b.to(gpu), idx, gate, logits)
     torch.cuda.synchronize()
     ref = oracle.route(x, w, b, k, renorm)
-    return idx.cpu().numpy(), gate.cpu().numpy(), ref
+    got = idx.cpu().numpy()
+    bad = np.nonzero((got != ref["idx"]).any(axis=1))[0]
+    for t in bad[:5]:
+        _say(f"token {t}: gpu idx {got[t].tolist()} oracle {ref['idx'][t].tolist()}\n"
+             f"  gpu logits {logits[t].cpu().numpy().tolist()}\n  oracle {ref['logits'][t].tolist()}")
+    if bad.size:
+        _say(f"{bad.size} mismatching tokens of {T}: {bad[:20].tolist()}")
+    return got, gate.cpu().numpy(), ref
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
