@@ -5,7 +5,7 @@
 // residual the start value is x instead (dropped tokens pass through).
 //
 // Memory-bound: each token reads k rows of y_perm (+ x) and writes one row.
-// A workgroup walks tokens; its threads cover the row in 16-byte chunks.
+// Every thread handles one 16-byte chunk of one token at a time.
 // The sum runs in fp32 in increasing choice order, so it is deterministic.
 #include "moe_internal.h"
 
@@ -33,37 +33,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
   const int chunks = D / W;
-  for (int64_t t = blockIdx.x; t < T_; t += gridDim.x) {
-    int s[kMaxTopK];
-    float g[kMaxTopK];
+  const int64_t items = T_ * chunks;  // one 16-byte chunk of one token each
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / chunks;
+    const int c = (int)(i - t * chunks);
+    float acc[W];
+    if (x) {
+      V xv = *(const V*)(x + t * D + c * W);
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc[u] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      s[j] = (j < k) ? slot[t * k + j] : -1;
-      g[j] = (j < k) ? gate[t * k + j] : 0.f;
-    }
-    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-      float acc[W];
-      if (x) {
-        V xv = *(const V*)(x + t * D + c * W);
+      if (j < k) {
+        const int s = slot[t * k + j];
+        if (s >= 0) {
+          const float g = gate[t * k + j];
+          V yv = *(const V*)(y + (int64_t)s * D + c * W);
 #pragma unroll
-        for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
-      } else {
-#pragma unroll
-        for (int u = 0; u < W; ++u) acc[u] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (s[j] >= 0) {
-          V yv = *(const V*)(y + (int64_t)s[j] * D + c * W);
-#pragma unroll
-          for (int u = 0; u < W; ++u) acc[u] = fmaf(g[j], (float)yv[u], acc[u]);
+          for (int u = 0; u < W; ++u) acc[u] = fmaf(g, (float)yv[u], acc[u]);
         }
       }
-      V o;
-#pragma unroll
-      for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
-      *(V*)(out + t * D + c * W) = o;
     }
+    V o;
+#pragma unroll
+    for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
+    *(V*)(out + t * D + c * W) = o;
   }
 }
 
@@ -71,8 +70,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
                           const float* gate, const void* x_res, void* out, hipStream_t st) {
-  const int64_t grid64 = s.T < (int64_t)device_cu_count() * 16 ? s.T : (int64_t)device_cu_count() * 16;
-  const dim3 grid((unsigned)grid64);
+  const int W = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;
+  const int64_t items = s.T * (s.D / W);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t blocks = (items + 255) / 256;
+  const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
   const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
   if (s.dtype == MOE_DTYPE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)y_perm, slot, gate,

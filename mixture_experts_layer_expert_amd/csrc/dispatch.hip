@@ -4,26 +4,30 @@
 // expert is trick 2 of "MoE Parallelism for Inference: Tricks and PyTorch
 // Deep Dive").
 //
-// One workgroup of 1024 threads (16 waves), two passes over the T*k
-// assignments:
-//  1. histogram of expert ids with LDS atomics (order-free, so exact), then
-//     an exclusive scan of min(count, capacity) -> offsets.
-//  2. stable ranking in chunks of 1024 assignments, chunk after chunk:
-//     inside a wave the lanes holding the same expert are found with one
-//     ballot per bit of the expert id; a lane's rank is the number of such
-//     lanes below it, plus the counts of the same expert in lower waves of
-//     the chunk, plus the running count of earlier chunks.  The rank is the
-//     position in increasing flat index, so the result is the stable order.
-// The assignment volume is small (T*k <= a few 10^4 on the workloads), so a
-// single workgroup finishes in a few microseconds without global atomics.
+// One workgroup of 1024 threads (16 waves).  The T*k assignments are split
+// into 16 contiguous segments, one per wave, so that the result is the
+// stable order (segments, 64-wide chunks inside a segment and lanes inside
+// a chunk all follow increasing flat index a = t*k + j):
+//  A. each wave walks its segment chunk by chunk; the lanes holding the same
+//     expert are found with one ballot per bit of the expert id, a lane's
+//     rank inside its wave is the wave's running count of that expert plus
+//     the same-expert lanes below it; the lowest such lane advances the
+//     running count (wave-private LDS counters, no atomics, no barriers).
+//     The in-wave rank is parked in slot[a].
+//  B. per expert, an exclusive scan of the 16 wave counts gives each wave's
+//     base and the expert's total; a scan of min(total, capacity) over the
+//     experts gives offsets.
+//  C. each wave re-walks its segment: rank = wave base + in-wave rank; a
+//     rank below the capacity gets slot[a] = offsets[e] + rank and
+//     perm[slot] = a, the rest slot[a] = -1.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kBatch = 8192;  // assignments staged in LDS at a time
+constexpr int kWaves = kThreads / kWave;
+constexpr int kPrefetch = 8;  // chunks whose ids are loaded ahead
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                             int64_t A, int N, int C,
@@ -32,98 +36,105 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
                                                             int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ slot,
                                                             int32_t* __restrict__ n_dropped) {
-  __shared__ int cnt[kMaxExperts];
+  __shared__ int wcnt[kWaves][kMaxExperts];  // A: running counts; then wave bases
+  __shared__ int scan[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
-  __shared__ int base[kMaxExperts];
-  __shared__ int wcnt[kWavesPerBlock][kMaxExperts];
-  __shared__ int scan_tmp[kMaxExperts];
-  __shared__ int ids[kBatch];
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-
-  for (int i = tid; i < kMaxExperts; i += kThreads) {
-    cnt[i] = 0;
-    base[i] = 0;
-  }
-  for (int i = tid; i < kWavesPerBlock * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
+  for (int i = tid; i < kWaves * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
   __syncthreads();
 
-  // pass 1: histogram (batches staged in LDS with coalesced loads)
-  for (int64_t b0 = 0; b0 < A; b0 += kBatch) {
-    const int nb = (int)(A - b0 < kBatch ? A - b0 : kBatch);
-    for (int i = tid; i < nb; i += kThreads) ids[i] = idx[b0 + i];
-    __syncthreads();
-    for (int i = tid; i < nb; i += kThreads) {
-      const int e = ids[i];
-      if (e >= 0 && e < N) atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-  }
+  int bits = 0;
+  while ((1 << bits) < N) ++bits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // segment of this wave, in whole 64-wide chunks
+  const int64_t chunks = (A + kWave - 1) / kWave;
+  const int64_t per = (chunks + kWaves - 1) / kWaves;
+  const int64_t a_begin = (int64_t)wave * per * kWave;
+  const int64_t a_end = (a_begin + per * kWave < A) ? a_begin + per * kWave : A;
 
-  // exclusive scan of kept counts (N <= 256: Hillis-Steele in LDS)
+  // ---- A: in-wave ranks
+  for (int64_t b0 = a_begin; b0 < a_end; b0 += kPrefetch * kWave) {
+    int ev[kPrefetch];
+#pragma unroll
+    for (int c = 0; c < kPrefetch; ++c) {
+      const int64_t a = b0 + c * kWave + lane;
+      ev[c] = (a < a_end) ? idx[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < kPrefetch; ++c) {
+      const int64_t a = b0 + c * kWave + lane;
+      const int e = ev[c];
+      const bool valid = a < a_end && e >= 0 && e < N;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < bits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        same &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const int below = __popcll(same & lt_mask);
+        const int base = wcnt[wave][e];  // every lane reads before the leader writes
+        if (below == 0) wcnt[wave][e] = base + __popcll(same);
+        slot[a] = base + below;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- B: wave bases per expert, totals, capacity cut, offsets
   int kept = 0;
   if (tid < N) {
-    kept = cnt[tid];
-    if (C >= 0 && kept > C) kept = C;
-    scan_tmp[tid] = kept;
-    counts[tid] = cnt[tid];
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = run;
+      run += c;
+    }
+    counts[tid] = run;
+    kept = (C >= 0 && run > C) ? C : run;
+    scan[tid] = kept;
   }
   __syncthreads();
   for (int d = 1; d < kMaxExperts; d <<= 1) {
     int v = 0;
-    if (tid < N && tid >= d) v = scan_tmp[tid - d];
+    if (tid < N && tid >= d) v = scan[tid - d];
     __syncthreads();
-    if (tid < N && tid >= d) scan_tmp[tid] += v;
+    if (tid < N && tid >= d) scan[tid] += v;
     __syncthreads();
   }
   if (tid < N) {
-    off[tid] = scan_tmp[tid] - kept;  // exclusive
-    offsets[tid] = scan_tmp[tid] - kept;
+    off[tid] = scan[tid] - kept;
+    offsets[tid] = scan[tid] - kept;
   }
   if (tid == 0) {
-    int total = N > 0 ? scan_tmp[N - 1] : 0;
+    const int total = N > 0 ? scan[N - 1] : 0;
     off[N] = total;
     offsets[N] = total;
     *n_dropped = (int32_t)(A - total);
   }
   __syncthreads();
 
-  // bits needed to tell the expert ids apart
-  int bits = 0;
-  while ((1 << bits) < N) ++bits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  // pass 2: stable ranks, chunk by chunk (chunks of a batch read from LDS)
-  for (int64_t c0 = 0; c0 < A; c0 += kThreads) {
-    if (c0 % kBatch == 0) {
-      const int nb = (int)(A - c0 < kBatch ? A - c0 : kBatch);
-      __syncthreads();
-      for (int i = tid; i < nb; i += kThreads) ids[i] = idx[c0 + i];
-      __syncthreads();
+  // ---- C: final ranks -> slot and perm
+  for (int64_t b0 = a_begin; b0 < a_end; b0 += kPrefetch * kWave) {
+    int ev[kPrefetch], rv[kPrefetch];
+#pragma unroll
+    for (int c = 0; c < kPrefetch; ++c) {
+      const int64_t a = b0 + c * kWave + lane;
+      ev[c] = (a < a_end) ? idx[a] : -1;
+      rv[c] = (a < a_end) ? slot[a] : 0;
     }
-    const int64_t a = c0 + tid;
-    int e = (a < A) ? ids[(int)(a % kBatch)] : -1;
-    const bool valid = (e >= 0 && e < N);
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      same &= bit ? bb : ~bb;
-    }
-    if (!valid) same = 0;
-    const int below = __popcll(same & lt_mask);
-    const bool leader = valid && below == 0;
-    if (leader) wcnt[wave][e] = __popcll(same);
-    __syncthreads();
-    int rank = 0;
-    if (valid) {
-      rank = base[e] + below;
-      for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
-    }
-    __syncthreads();
-    if (valid) {
-      atomicAdd(&base[e], 1);
+#pragma unroll
+    for (int c = 0; c < kPrefetch; ++c) {
+      const int64_t a = b0 + c * kWave + lane;
+      if (a >= a_end) continue;
+      const int e = ev[c];
+      if (e < 0 || e >= N) {
+        slot[a] = -1;
+        continue;
+      }
+      const int rank = wcnt[wave][e] + rv[c];
       if (C < 0 || rank < C) {
         const int s = off[e] + rank;
         slot[a] = s;
@@ -131,11 +142,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
       } else {
         slot[a] = -1;
       }
-    } else if (a < A) {
-      slot[a] = -1;
     }
-    if (leader) wcnt[wave][e] = 0;
-    __syncthreads();
   }
 }
 

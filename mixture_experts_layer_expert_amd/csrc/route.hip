@@ -244,30 +244,53 @@ __device__ void logits_f32(const RouteArgs& a, int64_t t0, int tid, float* lg, i
   }
 }
 
+// Product of two stored input values, exact: a bf16*bf16 product has at most
+// 16 significant bits and is exact in fp32; fp32*fp32 is exact in fp64.
+__device__ inline double exact_product(float x, bf16 w) { return (double)(x * (float)w); }
+__device__ inline double exact_product(float x, float w) { return (double)x * (double)w; }
+
 // Exact-product fp64 logits of token t, computed by the whole block: thread
 // (expert e = tid % N, slice s = tid / N) sums its share of the D/8 (bf16) or
-// D/4 (fp32) 16-byte chunks of row e of the router against the same chunks
-// of the token's row; the slices are then added per expert into dl.
+// D/4 (fp32) 16-byte chunks of row e of the router against the token's row
+// (staged in LDS as fp32, which holds bf16 and fp32 values exactly, when xf
+// is given; else read from global memory); the slices are then added per
+// expert into dl.  Router chunks are loaded 8 at a time so the loads overlap;
+// four fp64 accumulators shorten the dependency chain.
 template <typename T>
-__device__ void refine_block(const RouteArgs& a, int64_t t, int tid, double* dp, double* dl) {
+__device__ void refine_block(const RouteArgs& a, int64_t t, int tid, float* xf, double* dp,
+                             double* dl) {
   constexpr int W = Chunk<T>::W;
   typedef typename Chunk<T>::type V;
   const int D = a.D, N = a.N;
-  const V* xv = (const V*)((const T*)a.x + t * (int64_t)D);
+  const T* xrow = (const T*)a.x + t * (int64_t)D;
+  if (xf) {
+    for (int d = tid; d < D; d += 256) xf[d] = (float)xrow[d];
+    __syncthreads();
+  }
   const int S = (256 / N) > 0 ? 256 / N : 1;
   const int e = tid % N, s = tid / N;
   if (s < S) {
     const int chunks = D / W;
-    const int c0 = (int)((int64_t)chunks * s / S), c1 = (int)((int64_t)chunks * (s + 1) / S);
+    const int c0 = chunks * s / S, c1 = chunks * (s + 1) / S;
     const V* wv = (const V*)((const T*)a.wr + (int64_t)e * D);
-    double acc = 0.0;
-#pragma unroll 4
-    for (int c = c0; c < c1; ++c) {
-      V v = wv[c], u8 = xv[c];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    auto add_chunk = [&](int c, const V& w) {
 #pragma unroll
-      for (int u = 0; u < W; ++u) acc = fma(to_f64(u8[u]), to_f64(v[u]), acc);
+      for (int v = 0; v < W; ++v) {
+        const float xx = xf ? xf[c * W + v] : (float)xrow[c * W + v];
+        acc[v & 3] += exact_product(xx, w[v]);
+      }
+    };
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      V w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = wv[c + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add_chunk(c + u, w[u]);
     }
-    dp[s * N + e] = acc;
+    for (; c < c1; ++c) add_chunk(c, wv[c]);
+    dp[s * N + e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
   __syncthreads();
   if (tid < N) {
@@ -282,7 +305,8 @@ __device__ void refine_block(const RouteArgs& a, int64_t t, int tid, double* dp,
 template <typename T, int NT>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   constexpr int ldl = 16 * NT + 1;
-  constexpr int U = NT >= 8 ? 1 : (NT >= 4 ? 2 : 4);
+  // k steps whose operands are loaded together (loads in flight per wave)
+  constexpr int U = NT >= 16 ? 2 : (NT >= 8 ? 3 : (NT >= 4 ? 6 : 8));
   __shared__ float lg[32 * ldl];  // logits of the block's 32 tokens
   __shared__ double dp[256];
   __shared__ double dl[16 * NT];
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   for (int i = 0; i < nf; ++i) {
     const int r = flagged[i];
     const int64_t t = t0 + r;
-    refine_block<T>(a, t, tid, dp, dl);
+    refine_block<T>(a, t, tid, nullptr, dp, dl);
     if (wave == 0 && grp == 0) {
       group_rank<double, NT>(dl, a, t, l16, -1.0, true);
       if (a.logits)
@@ -322,6 +346,205 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 router for D a multiple of 128: x rows and router rows are streamed
+// global -> LDS with global_load_lds_dwordx4 through an S-stage ring, K taken
+// 128 at a time (256-byte rows, 4 rows per 1 KiB dma instruction, so x and
+// the router matrix both split evenly over the 4 waves).  TB tokens per
+// block (64, 32 or 16): wave w computes m-tile w % (TB/16) over the k
+// sub-steps congruent to w / (TB/16); partial tiles are summed in LDS in
+// fixed wave order.  Selection and fp64 re-ranking as above.
+template <int NT, int TB>
+struct RouteRing {
+  static constexpr int NP = 16 * NT;          // expert rows held (padded)
+  static constexpr int MT = TB / 16;          // 16-token m-tiles per block
+  static constexpr int KSPLIT = 4 / MT;       // waves sharing an m-tile
+  static constexpr int IA = TB / 4;           // dma instructions for x per stage
+  static constexpr int IB = NP / 4;           // ... for the router matrix
+  static constexpr int NJ = (IA + IB) / 4;    // per wave per stage
+  static constexpr int kStageElems = (TB + NP) * 128;
+  static constexpr int kStageBytes = kStageElems * 2;
+  static constexpr int S0 = (140 * 1024) / kStageBytes;
+  static constexpr int S = S0 > 8 ? 8 : S0;
+  static constexpr int kLogitFloats = KSPLIT * TB * (NP + 1);
+  static constexpr int kBytes =
+      (S * kStageBytes > kLogitFloats * 4) ? S * kStageBytes : kLogitFloats * 4;
+  static_assert(S >= 2, "ring needs two stages");
+  static_assert((IA + IB) % 4 == 0, "even dma split");
+  static_assert(NJ * (S - 1) <= 63, "vmcnt range");
+};
+
+template <int NJ, int K>
+__device__ inline void wait_vm_k(int younger) {
+  if constexpr (K >= 0) {
+    if (younger == K) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * NJ) : "memory");
+      return;
+    }
+    wait_vm_k<NJ, K - 1>(younger);
+  }
+}
+
+__device__ inline void ring_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ inline void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 16, 0, 0);
+}
+
+template <int NT, int TB>
+__global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
+  using R = RouteRing<NT, TB>;
+  constexpr int ldl = R::NP + 1;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* ring = (bf16*)smem_raw;
+  float* lg = (float*)smem_raw;  // logits tiles, after the ring is drained
+  __shared__ double dp[256];
+  __shared__ double dl[16 * NT];
+  __shared__ int flagged[TB];
+  __shared__ int nflag;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int D = a.D;
+  const int KT = D / 128;
+  if (tid == 0) nflag = 0;
+
+  // dma sources: wave's instruction q covers 4 rows of A (x) or B (router)
+  uint32_t src[R::NJ];
+  bool is_a[R::NJ];
+#pragma unroll
+  for (int q = 0; q < R::NJ; ++q) {
+    const int g = wave * R::NJ + q;
+    const int lrow = lane / 16, pc = lane % 16;
+    if (g < R::IA) {
+      const int row = g * 4 + lrow;
+      int64_t t = t0 + row;
+      if (t > a.T - 1) t = a.T - 1;
+      src[q] = (uint32_t)(t * D + ((pc ^ (row & 15)) * 8)) * 2u;
+      is_a[q] = true;
+    } else {
+      const int row = (g - R::IA) * 4 + lrow;
+      const int e = row < a.N ? row : a.N - 1;
+      src[q] = (uint32_t)(e * D + ((pc ^ (row & 15)) * 8)) * 2u;
+      is_a[q] = false;
+    }
+  }
+  const char* xb = (const char*)a.x;
+  const char* wb = (const char*)a.wr;
+  int issued = 0;
+  auto issue = [&]() {
+    if (issued >= KT) return;
+    bf16* dst = ring + (issued % R::S) * R::kStageElems;
+    const uint32_t kb = (uint32_t)issued * 256u;
+#pragma unroll
+    for (int q = 0; q < R::NJ; ++q) {
+      const int g = wave * R::NJ + q;
+      const char* base = (g < R::IA ? xb : wb) + kb;
+      dma16(base + src[q], dst + g * 512);
+    }
+    ++issued;
+  };
+#pragma unroll
+  for (int s = 0; s < R::S - 1; ++s) issue();
+
+  const int mt = wave % R::MT, kp = wave / R::MT;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vm_k<R::NJ, R::S - 1>(issued - kt - 1);
+    ring_sync();
+    issue();  // refills the stage read in the previous step
+    const bf16* st = ring + (kt % R::S) * R::kStageElems;
+    const bf16* sa = st;
+    const bf16* sb = st + TB * 128;
+    // this wave's k sub-steps: kp, kp + KSPLIT, ... (no per-wave branch
+    // around the MFMAs)
+#pragma unroll
+    for (int j = 0; j < 4 / R::KSPLIT; ++j) {
+      const int ss = j * R::KSPLIT + kp;
+      const int c = ss * 4 + (lane >> 4);
+      const int ra = mt * 16 + (lane & 15);
+      const bf16x8 av = *(const bf16x8*)(sa + ra * 128 + ((c ^ (ra & 15)) * 8));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int rb = nt * 16 + (lane & 15);
+        const bf16x8 bv = *(const bf16x8*)(sb + rb * 128 + ((c ^ (rb & 15)) * 8));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nt], 0, 0, 0);
+      }
+    }
+  }
+  ring_sync();  // every wave is done with the ring: reuse it for the logits
+  // partial tile of this wave -> lg[kp][token][expert]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      lg[(kp * TB + mt * 16 + 4 * (lane >> 4) + r) * ldl + nt * 16 + (lane & 15)] = acc[nt][r];
+  __syncthreads();
+  // sum the KSPLIT partial tiles in fixed order, add the router bias
+  for (int i = tid; i < TB * R::NP; i += 256) {
+    const int r = i / R::NP, e = i % R::NP;
+    float v = (a.has_bias && e < a.N) ? a.br[e] : 0.f;
+#pragma unroll
+    for (int p = 0; p < R::KSPLIT; ++p) v += lg[(p * TB + r) * ldl + e];
+    lg[r * ldl + e] = v;  // p = 0 tile is overwritten by its own final value only
+  }
+  __syncthreads();
+
+  const int grp = lane >> 4, l16 = lane & 15;
+  for (int it = 0; it < TB / 16; ++it) {
+    const int r = it * 16 + wave * 4 + grp;
+    const int64_t t = t0 + r;
+    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
+    if (a.logits && t < a.T)
+      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
+    if (!ok && l16 == 0 && t < a.T) flagged[atomicAdd(&nflag, 1)] = r;
+  }
+  __syncthreads();
+  const int nf = nflag;
+  // fp32 copy of a flagged token's row goes after the logits tiles if it fits
+  constexpr int kLgBytes = (R::kLogitFloats * 4 + 15) / 16 * 16;
+  float* xd = (R::kBytes - kLgBytes >= 4 * D) ? (float*)(smem_raw + kLgBytes) : nullptr;
+  for (int i = 0; i < nf; ++i) {
+    const int r = flagged[i];
+    const int64_t t = t0 + r;
+    refine_block<bf16>(a, t, tid, xd, dp, dl);
+    if (wave == 0 && grp == 0) {
+      group_rank<double, NT>(dl, a, t, l16, -1.0, true);
+      if (a.logits)
+        for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = (float)dl[e];
+    }
+    __syncthreads();
+  }
+}
+
+template <int NT, int TB>
+hipError_t launch_ring(const RouteArgs& a, hipStream_t st) {
+  using R = RouteRing<NT, TB>;
+  auto kern = route_ring_kernel<NT, TB>;
+  static const hipError_t attr_err =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, R::kBytes);
+  if (attr_err != hipSuccess) return attr_err;
+  const int64_t blocks = (a.T + TB - 1) / TB;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), R::kBytes, st, a);
+  return hipGetLastError();
+}
+
+// Tokens per block: as many as keep >= ~2 blocks per CU busy, fewer for the
+// widest expert counts (their ring stages are large).
+template <int NT>
+hipError_t launch_ring_nt(const RouteArgs& a, hipStream_t st) {
+  const int64_t cus = device_cu_count();
+  if constexpr (NT < 16) {
+    if (a.T >= 64 * cus) return launch_ring<NT, 64>(a, st);
+    if (a.T >= 32 * cus) return launch_ring<NT, 32>(a, st);
+  }
+  return launch_ring<NT, 16>(a, st);
 }
 
 template <typename T, int NT>
@@ -333,6 +556,15 @@ hipError_t launch_nt(const RouteArgs& a, hipStream_t st) {
 
 template <typename T>
 hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.D % 128 == 0) {
+      if (a.N <= 16) return launch_ring_nt<1>(a, st);
+      if (a.N <= 32) return launch_ring_nt<2>(a, st);
+      if (a.N <= 64) return launch_ring_nt<4>(a, st);
+      if (a.N <= 128) return launch_ring_nt<8>(a, st);
+      return launch_ring_nt<16>(a, st);
+    }
+  }
   if (a.N <= 16) return launch_nt<T, 1>(a, st);
   if (a.N <= 32) return launch_nt<T, 2>(a, st);
   if (a.N <= 64) return launch_nt<T, 4>(a, st);

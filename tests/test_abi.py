@@ -129,3 +129,19 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
     assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None) == L.MOE_OK
     assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK
+
+
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel stub the library references is defined in it (a kernel
+    whose host stub is not emitted leaves an undefined moe:: symbol and the
+    library fails to load)."""
+    import shutil
+    import subprocess
+    from mixture_experts_layer_expert_amd import _lib
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    bad = [l for l in out.splitlines() if "3moe" in l]
+    assert not bad, bad[:5]
