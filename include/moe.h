@@ -70,10 +70,16 @@ enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 enum moe_act { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 };
 
 enum moe_flags {
-  MOE_RENORM = 1u,      /* gates divided by their sum over the k choices */
-  MOE_RESIDUAL = 2u,    /* out = x + sum of kept, gated expert outputs */
-  MOE_HAS_BIAS = 4u,    /* b1 and b2 are present */
-  MOE_ROUTER_BIAS = 8u  /* b_router is added to the router logits */
+  MOE_RENORM = 1u,       /* gates divided by their sum over the k choices */
+  MOE_RESIDUAL = 2u,     /* out = x + sum of kept, gated expert outputs */
+  MOE_HAS_BIAS = 4u,     /* b1 and b2 are present */
+  MOE_ROUTER_BIAS = 8u,  /* b_router is added to the router logits */
+  /* Algorithm choice for bf16 layers with at most 16 rows per expert: one
+   * fused launch per layer over (expert, F-shard) items that streams the
+   * weights into registers and writes fp32 shard partials, instead of the
+   * two grouped-GEMM launches.  Same results within the bf16 tolerance;
+   * ignored where it does not apply.  Off by default (slower on MI355X). */
+  MOE_FUSED_DECODE = 16u
 };
 
 typedef struct moe_shape {
@@ -130,9 +136,10 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* count
  * and one for fc2, each a persistent grouped GEMM whose work list covers
  * column shards of w1/w3 and row shards of w2 for all experts at once (the
  * row/column expert decomposition of "Accelerating MoE Model Inference with
- * Expert Sharding", abstract), or a fused weight-streaming kernel when the
- * rows per expert are few.  fp32 accumulation; the hidden activations are
- * held in the shape's dtype.  ws/ws_bytes: see moe_workspace_bytes. */
+ * Expert Sharding", abstract), or with MOE_FUSED_DECODE a fused
+ * weight-streaming kernel when the rows per expert are few.  fp32
+ * accumulation; the hidden activations are held in the shape's dtype.
+ * ws/ws_bytes: see moe_workspace_bytes. */
 int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
                    const int32_t* offsets, const void* w1, const void* b1, const void* w3,
                    const void* w2, const void* b2, void* y_perm, void* ws, size_t ws_bytes,

@@ -40,6 +40,7 @@ class MoeShape:
     residual: bool = False
     has_bias: bool = False
     router_bias: bool = False
+    fused_decode: bool = False  # MOE_FUSED_DECODE algorithm choice
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -48,17 +49,19 @@ class MoeShape:
     def c(self) -> L.MoeShapeC:
         flags = ((L.MOE_RENORM if self.renorm else 0) | (L.MOE_RESIDUAL if self.residual else 0)
                  | (L.MOE_HAS_BIAS if self.has_bias else 0)
-                 | (L.MOE_ROUTER_BIAS if self.router_bias else 0))
+                 | (L.MOE_ROUTER_BIAS if self.router_bias else 0)
+                 | (L.MOE_FUSED_DECODE if self.fused_decode else 0))
         return L.MoeShapeC(self.T, self.D, self.F, self.N, self.k, self.capacity,
                            _DT[self.dtype][0], _ACT[self.act], flags)
 
     @staticmethod
-    def from_config(cfg, T: Optional[int] = None) -> "MoeShape":
+    def from_config(cfg, T: Optional[int] = None, fused_decode: bool = False) -> "MoeShape":
         T = cfg.T if T is None else T
         cap = capacity(T, cfg.k, cfg.N, -1.0 if cfg.cf is None else cfg.cf)
         return MoeShape(T=T, D=cfg.D, F=cfg.F, N=cfg.N, k=cfg.k, capacity=cap, dtype=cfg.dtype,
                         act=cfg.act, renorm=cfg.renorm, residual=cfg.residual,
-                        has_bias=cfg.expert_bias, router_bias=cfg.router_bias is not None)
+                        has_bias=cfg.expert_bias, router_bias=cfg.router_bias is not None,
+                        fused_decode=fused_decode)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "") -> Optional[int]:

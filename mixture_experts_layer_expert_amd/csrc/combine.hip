@@ -66,6 +66,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   }
 }
 
+// Same combine, reading fp32 partial rows of NS shards (summed in shard
+// order) instead of one y_perm row.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_shards_kernel(const float* __restrict__ part, int NS,
+                                                             int64_t rows_cap,
+                                                             const int32_t* __restrict__ slot,
+                                                             const float* __restrict__ gate,
+                                                             const T* __restrict__ x, T* __restrict__ out,
+                                                             int64_t T_, int D, int k) {
+  constexpr int W = Vec<T>::W;
+  typedef typename Vec<T>::type V;
+  const int chunks = D / W;
+  const int64_t items = T_ * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / chunks;
+    const int c = (int)(i - t * chunks);
+    float acc[W];
+    if (x) {
+      V xv = *(const V*)(x + t * D + c * W);
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc[u] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const int sl = slot[t * k + j];
+        if (sl >= 0) {
+          const float g = gate[t * k + j];
+          float y[W];
+#pragma unroll
+          for (int u = 0; u < W; ++u) y[u] = 0.f;
+          for (int s = 0; s < NS; ++s) {
+            const float* src = part + ((int64_t)s * rows_cap + sl) * D + c * W;
+#pragma unroll
+            for (int u = 0; u < W; u += 4) {
+              const f32x4 v = *(const f32x4*)(src + u);
+              y[u] += v[0];
+              y[u + 1] += v[1];
+              y[u + 2] += v[2];
+              y[u + 3] += v[3];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < W; ++u) acc[u] = fmaf(g, y[u], acc[u]);
+        }
+      }
+    }
+    V o;
+#pragma unroll
+    for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
+    *(V*)(out + t * D + c * W) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
@@ -85,4 +143,25 @@ hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t*
   return hipGetLastError();
 }
 
+}  // namespace moe
+
+namespace moe {
+hipError_t launch_combine_shards(const moe_shape& s, const float* part, int n_shards,
+                                 const int32_t* slot, const float* gate, const void* x_res, void* out,
+                                 hipStream_t st) {
+  const int W = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;
+  const int64_t items = s.T * (s.D / W);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t blocks = (items + 255) / 256;
+  const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
+  const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
+  const int64_t rows_cap = s.T * (int64_t)s.k;
+  if (s.dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(combine_shards_kernel<bf16>, grid, dim3(256), 0, st, part, n_shards, rows_cap, slot,
+                       gate, (const bf16*)xr, (bf16*)out, s.T, s.D, s.k);
+  else
+    hipLaunchKernelGGL(combine_shards_kernel<float>, grid, dim3(256), 0, st, part, n_shards, rows_cap, slot,
+                       gate, (const float*)xr, (float*)out, s.T, s.D, s.k);
+  return hipGetLastError();
+}
 }  // namespace moe

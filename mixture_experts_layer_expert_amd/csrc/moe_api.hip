@@ -37,7 +37,7 @@ int validate(const moe_shape* sp) {
   if (s.k > s.N || s.capacity < -1) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.act != MOE_ACT_GELU && s.act != MOE_ACT_RELU && s.act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  const uint32_t known = MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS;
+  const uint32_t known = MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE;
   if (s.flags & ~known) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && (s.flags & MOE_HAS_BIAS)) return MOE_ERR_UNSUPPORTED;
   if (s.N > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
@@ -54,8 +54,21 @@ int validate(const moe_shape* sp) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Workspace of the expert stage: hidden activations H[T*k, F].
+// Mean rows per expert, capped by the capacity: picks the kernel shape.
+int64_t expected_rows(const moe_shape& s) {
+  int64_t expect = (s.T * s.k + s.N - 1) / s.N;
+  if (s.capacity >= 0 && expect > s.capacity) expect = s.capacity;
+  return expect;
+}
+
+bool use_decode(const moe_shape& s) {
+  return (s.flags & MOE_FUSED_DECODE) && decode_applicable(s, expected_rows(s));
+}
+
+// Workspace of the expert stage: hidden activations H[T*k, F] for the
+// grouped-GEMM path, fp32 shard partials for the fused decode path.
 size_t ffn_ws_bytes(const moe_shape& s) {
+  if (use_decode(s)) return align_up(decode_part_bytes(s));
   return align_up((size_t)s.T * s.k * s.F * elem_size(s));
 }
 
@@ -64,9 +77,16 @@ size_t forward_ws_bytes(const moe_shape& s) {
   return align_up((size_t)s.T * s.k * s.D * elem_size(s)) + ffn_ws_bytes(s);
 }
 
+// Expert stage.  With the decode path the fp32 shard partials stay in ws;
+// y_perm is produced from them only when y_perm is non-null (stage API).
 int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
                     const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
                     void* y_perm, void* ws, hipStream_t st) {
+  if (use_decode(s)) {
+    hipError_t e = launch_decode_ffn(s, x, perm, offsets, w1, b1, w3, w2, b2, (float*)ws, st);
+    if (e == hipSuccess && y_perm) e = launch_reduce_shards(s, (const float*)ws, offsets, y_perm, st);
+    return hip_status(e);
+  }
   const bool bias = (s.flags & MOE_HAS_BIAS) != 0;
   GroupedGemm fc1{};
   fc1.A = x;
@@ -100,8 +120,7 @@ int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, cons
 
   hipError_t e;
   if (s.dtype == MOE_DTYPE_BF16) {
-    int64_t expect = (s.T * s.k + s.N - 1) / s.N;
-    if (s.capacity >= 0 && expect > s.capacity) expect = s.capacity;
+    const int64_t expect = expected_rows(s);
     e = launch_grouped_gemm_bf16(fc1, expect, st);
     if (e == hipSuccess) e = launch_grouped_gemm_bf16(fc2, expect, st);
   } else {
@@ -205,8 +224,12 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, st);
   if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  int r = expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ffn_ws, st);
+  const bool decode = use_decode(s);
+  int r = expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, decode ? nullptr : y_perm, ffn_ws, st);
   if (r != MOE_OK) return r;
+  if (decode)
+    return hip_status(launch_combine_shards(s, (const float*)ffn_ws, decode_shards(s), slot, topk_gate, x,
+                                            out, st));
   return hip_status(launch_combine(s, y_perm, slot, topk_gate, x, out, st));
 }
 

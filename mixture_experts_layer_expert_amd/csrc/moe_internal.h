@@ -64,4 +64,20 @@ hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
                           const float* gate, const void* x_res, void* out, hipStream_t st);
 
+// Decode path: fused per-(expert, F-shard) weight-streaming MLP writing fp32
+// shard partials part[NS][T*k][D]; used when rows per expert are few.
+int decode_shards(const moe_shape& s);
+bool decode_applicable(const moe_shape& s, int64_t expected_rows_per_expert);
+size_t decode_part_bytes(const moe_shape& s);
+hipError_t launch_decode_ffn(const moe_shape& s, const void* x, const int32_t* perm,
+                             const int32_t* offsets, const void* w1, const void* b1, const void* w3,
+                             const void* w2, const void* b2, float* part, hipStream_t st);
+// y_perm = sum of the shard partials (bf16), for the stage API.
+hipError_t launch_reduce_shards(const moe_shape& s, const float* part, const int32_t* offsets,
+                                void* y_perm, hipStream_t st);
+// Combine reading the fp32 shard partials directly (whole-layer path).
+hipError_t launch_combine_shards(const moe_shape& s, const float* part, int n_shards,
+                                 const int32_t* slot, const float* gate, const void* x_res, void* out,
+                                 hipStream_t st);
+
 }  // namespace moe

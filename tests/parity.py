@@ -74,8 +74,8 @@ def check_outputs(y_gpu: np.ndarray, ref: dict, cfg, x_rows: np.ndarray, tokens=
     return err
 
 
-def run_forward(cfg, g: dict, T=None) -> api.MoeBuffers:
-    shape = api.MoeShape.from_config(cfg, T)
+def run_forward(cfg, g: dict, T=None, fused_decode=False) -> api.MoeBuffers:
+    shape = api.MoeShape.from_config(cfg, T, fused_decode)
     buf = api.MoeBuffers(shape)
     buf.forward(g["x"], g)
     torch.cuda.synchronize()

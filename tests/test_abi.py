@@ -73,16 +73,27 @@ def _ws(lib, s):
 
 def test_workspace_bytes_and_validation(lib):
     from mixture_experts_layer_expert_amd import _lib as L
-    rc, n = _ws(lib, _shape())
+    # prefill-shaped (many rows per expert): y_perm[T*k, D] + H[T*k, F], bf16
+    rc, n = _ws(lib, _shape(T=4096))
     assert rc == L.MOE_OK
-    # y_perm[T*k, D] + H[T*k, F], bf16, 256-byte aligned pieces
+    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2
+    # decode-shaped (<= 16 rows per expert): grouped GEMM by default ...
+    rc, n = _ws(lib, _shape(T=64))
+    assert rc == L.MOE_OK
     assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2
+    # ... and with the fused decode kernel y_perm + fp32 partials of the F
+    # shards; 8 experts -> 32 shards wanted, reduced until F/shards is a
+    # multiple of 32 -> 8 shards of 32 columns
+    rc, n = _ws(lib, _shape(T=64, flags=L.MOE_FUSED_DECODE))
+    assert rc == L.MOE_OK
+    assert n == 64 * 2 * 128 * 2 + 8 * 64 * 2 * 128 * 4
     bad = [
         (dict(k=0), L.MOE_ERR_INVALID_ARG), (dict(k=9, N=16), L.MOE_ERR_UNSUPPORTED),
         (dict(k=9), L.MOE_ERR_INVALID_ARG), (dict(N=300, k=2), L.MOE_ERR_UNSUPPORTED),
         (dict(T=-1), L.MOE_ERR_INVALID_ARG), (dict(capacity=-2), L.MOE_ERR_INVALID_ARG),
         (dict(dtype=7), L.MOE_ERR_INVALID_ARG), (dict(act=5), L.MOE_ERR_INVALID_ARG),
         (dict(flags=1 << 7), L.MOE_ERR_INVALID_ARG), (dict(D=100), L.MOE_ERR_UNSUPPORTED),
+        (dict(flags=1 << 5), L.MOE_ERR_INVALID_ARG),
         (dict(F=96), L.MOE_ERR_UNSUPPORTED), (dict(flags=L.MOE_HAS_BIAS), L.MOE_ERR_UNSUPPORTED),
         (dict(T=2**31, D=4096), L.MOE_ERR_UNSUPPORTED),
     ]
