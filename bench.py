@@ -1,22 +1,28 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--cf 1.0]
+                    [--copies 3] [--no-graph] [--no-cpu-baseline]
+    python bench.py --copy-calibration     (plain copy of known size, for PMC scaling)
 
 One step is one whole layer forward (router, dispatch with capacity, expert
 MLPs, combine) over the workload's batch, inputs and weights already resident
-in HBM.  The step runs the C-ABI stage chain moe_route -> moe_dispatch ->
-moe_expert_ffn -> moe_combine (the same kernels, in the same order, as
-moe_forward) with HIP events between the stages on the launch stream, so the
-expert stage's duration is measured live inside the timed region.
+in HBM.  The step runs the C-ABI chain moe_route -> moe_dispatch ->
+moe_expert_up -> moe_expert_down -> moe_combine (the kernels of moe_forward,
+in the same order) with HIP events between the launches on the launch
+stream, so every launch's duration is measured live inside the timed region.
+Consecutive steps cycle over --copies separate copies of x and the weights,
+so that no step finds its weights in the 256 MB last-level cache from the
+step before.
 
-Prints one JSON line: tokens/s of the layer, the roofline of the expert stage
-(the dominant pair of grouped-GEMM launches: HBM-bound for weight-streaming
-workloads, MFMA-bound for large prefill), and the CPU oracle timed on the
-host on a bounded sample of the same workload.
+Prints one JSON line: tokens/s of the layer, the roofline of the dominant
+launch (HBM-bound for weight-streaming workloads, MFMA-bound for large
+prefill), the same steps replayed from HIP graphs, and the CPU oracle timed on
+the host on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +43,31 @@ METRIC = "MoE layer fwd tokens/s + TFLOP/s (% bf16 MFMA peak) or GB/s (% HBM pea
 CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128}
 
 
+# HBM traffic of the dominant launch, from two rocprofv3 --pmc runs of the
+# default command of each workload (FETCH_SIZE, then WRITE_SIZE: KiB per
+# dispatch, averaged over the dispatches of that launch), each scaled by the
+# ratio of known bytes to the counter's reading for a plain copy
+# (--copy-calibration).  A figure is used only while the kernel sources hash
+# to the value it was measured with; otherwise traffic is null.
+PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
+                      "mixture_experts_layer_expert_amd/csrc/moe_internal.h")
+PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
+    "c2": {"sources": "4873c62f5708d0bb",
+           "fc1": {"fetch_kib": 309387.8, "write_kib": 91944.4},  # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 3>
+           "fc2": {"fetch_kib": 344501.1, "write_kib": 22946.7},  # grouped_gemm_kernel<128, 256, 2, 4, 64, 0, 3>
+           },
+    "c4": {"sources": "4873c62f5708d0bb",
+           "fc1": {"fetch_kib": 3021457.9, "write_kib": 460131.2},  # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 2>
+           "fc2": {"fetch_kib": 1716290.7, "write_kib": 150362.4},  # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 2>
+           },
+    "c5": {"sources": "4873c62f5708d0bb",
+           "fc1": {"fetch_kib": 362303.8, "write_kib": 2112.4},  # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 4>
+           "fc2": {"fetch_kib": 181390.8, "write_kib": 3072.0},  # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 4>
+           },
+}
+PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -44,31 +75,72 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c1..c5 (default: c2, the Switch-style layer)")
     ap.add_argument("--cf", type=float, default=None, help="capacity factor override (<0: none)")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="copies of x and the weights cycled over consecutive steps")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for PMC counter scaling)")
     return ap.parse_args()
 
 
-def expert_stage_work(cfg, counts_kept, used_experts):
-    """Algorithmic FLOPs and bytes of the expert stage (fc1+act, fc2).
+def launch_work(cfg, kept, used):
+    """Algorithmic FLOPs and bytes of the two expert launches, per launch.
 
-    FLOPs: 2 per multiply-add over kept rows only: 2*K*D*F per projection
-    (two projections, three for SwiGLU).  Bytes: every used expert's weights
-    once, plus the kept rows of x read once (bf16/fp32 element size).
+    FLOPs: 2 per multiply-add over kept rows only (2*K*D*F per projection;
+    fc1 of SwiGLU has two).  Bytes: every used expert's weights (and biases)
+    once, the launch's activation rows read once and its output rows written
+    once: fc1 reads K rows of x (gathered) and writes H[K, F]; fc2 reads H and
+    writes y_perm[K, D].  Tile padding, re-reads and the (N/k)x dense work the
+    method avoids are not counted.
     """
     es = 2 if cfg.dtype == "bf16" else 4
-    nproj = 3 if cfg.act == "swiglu" else 2
-    K = int(counts_kept)
-    flops = 2.0 * K * cfg.D * cfg.F * nproj
-    w_bytes = used_experts * nproj * cfg.D * cfg.F * es
-    if cfg.expert_bias:
-        w_bytes += used_experts * (cfg.F + cfg.D) * es
-    bytes_ = w_bytes + K * cfg.D * es
-    return flops, bytes_
+    K = int(kept)
+    up_proj = 2 if cfg.act == "swiglu" else 1
+    fc1_w = used * (up_proj * cfg.F * cfg.D + (cfg.F if cfg.expert_bias else 0)) * es
+    fc2_w = used * (cfg.D * cfg.F + (cfg.D if cfg.expert_bias else 0)) * es
+    return {
+        "fc1": {"flops": 2.0 * K * cfg.D * cfg.F * up_proj,
+                "bytes": fc1_w + K * cfg.D * es + K * cfg.F * es},
+        "fc2": {"flops": 2.0 * K * cfg.F * cfg.D,
+                "bytes": fc2_w + K * cfg.F * es + K * cfg.D * es},
+    }
 
 
 def layer_flops(cfg, counts_kept):
     nproj = 3 if cfg.act == "swiglu" else 2
     return 2.0 * cfg.T * cfg.D * cfg.N + 2.0 * counts_kept * cfg.D * cfg.F * nproj
+
+
+def sources_sha():
+    h = hashlib.sha256()
+    for rel in PMC_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, launch):
+    rec = PMC_TRAFFIC.get(workload)
+    if rec is None or launch not in rec or rec["sources"] != sources_sha():
+        return None
+    return (rec[launch]["fetch_kib"] * 1024.0 * PMC_COPY_FACTOR["fetch"]
+            + rec[launch]["write_kib"] * 1024.0 * PMC_COPY_FACTOR["write"])
+
+
+def copy_calibration():
+    """A plain elementwise copy (torch.neg, out=) of a known size: reads and
+    writes COPY_BYTES each.  Under rocprofv3 --pmc its FETCH_SIZE/WRITE_SIZE
+    give the scale from counter KiB to HBM bytes."""
+    import torch
+    n = 1 << 28  # fp32 elements: 1 GiB read, 1 GiB written
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 5}),
+          flush=True)
 
 
 def cpu_baseline(cfg, inp, key):
@@ -109,6 +181,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -121,68 +196,110 @@ def main():
     torch.cuda.set_device(dev)
 
     inp = generate(cfg)
-    g = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
+    g0 = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
+    R = max(1, args.copies)
+    # copy 0 is the generated tensors; the others are device clones (same
+    # values, different addresses)
+    gs = [g0] + [{k: (None if v is None else v.clone()) for k, v in g0.items()} for _ in range(R - 1)]
     shape = api.MoeShape.from_config(cfg)
     buf = api.MoeBuffers(shape, device=dev)
     A = cfg.T * cfg.k
+    h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=dev)
     y_perm = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=dev)
     st = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(g, s, ev=None):
         if ev is not None:
-            ev[0].record(st)
-        api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, st)
-        api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, st)
+            ev[0].record(s)
+        api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s)
+        api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
         if ev is not None:
-            ev[1].record(st)
-        api.expert_ffn(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], g["w2"],
-                       g["b2"], y_perm, buf.ws, st)
+            ev[1].record(s)
+        api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, s)
         if ev is not None:
-            ev[2].record(st)
-        api.combine(shape, y_perm, buf.slot, buf.topk_gate, g["x"], buf.out, st)
+            ev[2].record(s)
+        api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_perm, s)
         if ev is not None:
-            ev[3].record(st)
+            ev[3].record(s)
+        api.combine(shape, y_perm, buf.slot, buf.topk_gate, g["x"], buf.out, s)
+        if ev is not None:
+            ev[4].record(s)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(gs[i % R], st)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(st)
     for i in range(args.steps):
-        step(evs[i])
+        step(gs[i % R], st, evs[i])
     t_end.record(st)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    route_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    ffn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    comb_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    def mean_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps
+
+    stages = {"route+dispatch": mean_ms(0, 1), "fc1": mean_ms(1, 2), "fc2": mean_ms(2, 3),
+              "combine": mean_ms(3, 4)}
 
     counts = buf.counts.cpu()
     offsets = buf.offsets.cpu()
     kept = int(offsets[-1])
     used = int(((offsets[1:] - offsets[:-1]) > 0).sum())
     n_dropped = int(buf.n_dropped.cpu())
-    flops, bytes_ = expert_stage_work(cfg, kept, used)
+    work = launch_work(cfg, kept, used)
     lflops = layer_flops(cfg, kept)
 
+    # the dominant launch: the longer of the two grouped-GEMM launches
+    launch = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
+    flops, bytes_ = work[launch]["flops"], work[launch]["bytes"]
+    t_s = stages[launch] / 1e3
     if cfg.dtype == "bf16":
-        intensity = flops / bytes_
         ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        bound = "hbm" if intensity < ridge else "mfma"
+        bound = "hbm" if flops / bytes_ < ridge else "mfma"
     else:
         bound = "alu"
-    ffn_s = ffn_ms / 1e3
     if bound == "hbm":
-        achieved, peak, unit = bytes_ / ffn_s / 1e9, PEAK_HBM_GBS, "GB/s"
+        achieved, peak, unit = bytes_ / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
     elif bound == "mfma":
-        achieved, peak, unit = flops / ffn_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = flops / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = flops / ffn_s / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = flops / t_s / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"
+    act_name = {"gelu": "GELU", "relu": "ReLU", "swiglu": "SwiGLU"}[cfg.act]
+
+    graph = None
+    if not args.no_graph:
+        # the same steps captured once per input copy and replayed; the
+        # library allocates nothing and records no memset, so the capture is
+        # a plain sequence of kernel nodes
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        graphs = []
+        with torch.cuda.stream(side):
+            for r in range(R):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=side):
+                    step(gs[r], side)
+                graphs.append(gr)
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        g_start = torch.cuda.Event(enable_timing=True)
+        g_end = torch.cuda.Event(enable_timing=True)
+        g_start.record(st)
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        g_end.record(st)
+        torch.cuda.synchronize()
+        g_ms = g_start.elapsed_time(g_end) / args.steps
+        graph = {"ms_per_step": g_ms, "tokens_per_s": cfg.T / (g_ms / 1e3)}
 
     tokens_per_s = cfg.T / (ms_step / 1e3)
     res = {
@@ -200,19 +317,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "D": cfg.D, "F": cfg.F, "experts": cfg.N,
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
-                   "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual},
+                   "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
+                   "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-        "stages_ms": {"route+dispatch": route_ms, "expert_ffn": ffn_ms, "combine": comb_ms},
+        "stages_ms": stages,
+        "graph": graph,
         "routing": {"kept_assignments": kept, "dropped": n_dropped, "experts_used": used,
                     "max_count": int(counts.max()), "imbalance": float(counts.max()) / (A / cfg.N)},
         "roofline": {
-            "kernel": "expert stage: grouped_gemm_kernel fc1(+act) and fc2 launches (moe_expert_ffn)",
+            "kernel": f"grouped_gemm_kernel, {launch} launch "
+                      f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "
+                      f"moe_expert_{'up' if launch == 'fc1' else 'down'})",
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": None,
+            "frac": achieved / peak,
+            "traffic": measured_traffic(args.workload, launch) if args.cf is None else None,
+            "launch_ms": stages[launch],
             "algorithmic": {"flops": flops, "bytes": bytes_,
-                            "rule": "weights of used experts once + kept x rows once; "
-                                    "2 flops per MAC over kept rows"},
+                            "rule": "used experts' weights once + activation rows in once + "
+                                    "output rows once; 2 flops per MAC over kept rows"},
         },
     }
     if not args.no_cpu_baseline:

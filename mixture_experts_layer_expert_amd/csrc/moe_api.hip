@@ -79,6 +79,52 @@ size_t forward_ws_bytes(const moe_shape& s) {
 
 // Expert stage.  With the decode path the fp32 shard partials stay in ws;
 // y_perm is produced from them only when y_perm is non-null (stage API).
+GemmAct up_act(const moe_shape& s) {
+  return s.act == MOE_ACT_GELU ? kActGelu : s.act == MOE_ACT_RELU ? kActRelu : kActSwiGLU;
+}
+
+// fc1 (+ activation): H[r] for every kept row r, gathered from x through perm.
+hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
+                     const void* w1, const void* b1, const void* w3, void* h, hipStream_t st) {
+  GroupedGemm g{};
+  g.A = x;
+  g.perm = perm;
+  g.topk = s.k;
+  g.offsets = offsets;
+  g.n_experts = s.N;
+  g.a_rows = s.T;
+  g.B = w1;
+  g.B2 = w3;
+  g.bias = (s.flags & MOE_HAS_BIAS) ? b1 : nullptr;
+  g.C = h;
+  g.K = s.D;
+  g.n_out = s.F;
+  g.act = up_act(s);
+  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
+                                   : launch_grouped_gemm_f32(g, st);
+}
+
+// fc2: y_perm[r] = H[r] . w2[e]^T (+ b2[e]).
+hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets, const void* w2,
+                       const void* b2, void* y_perm, hipStream_t st) {
+  GroupedGemm g{};
+  g.A = h;
+  g.perm = nullptr;
+  g.topk = 1;
+  g.offsets = offsets;
+  g.n_experts = s.N;
+  g.a_rows = s.T * s.k;
+  g.B = w2;
+  g.B2 = nullptr;
+  g.bias = (s.flags & MOE_HAS_BIAS) ? b2 : nullptr;
+  g.C = y_perm;
+  g.K = s.F;
+  g.n_out = s.D;
+  g.act = kActNone;
+  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
+                                   : launch_grouped_gemm_f32(g, st);
+}
+
 int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
                     const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
                     void* y_perm, void* ws, hipStream_t st) {
@@ -87,46 +133,8 @@ int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, cons
     if (e == hipSuccess && y_perm) e = launch_reduce_shards(s, (const float*)ws, offsets, y_perm, st);
     return hip_status(e);
   }
-  const bool bias = (s.flags & MOE_HAS_BIAS) != 0;
-  GroupedGemm fc1{};
-  fc1.A = x;
-  fc1.perm = perm;
-  fc1.topk = s.k;
-  fc1.offsets = offsets;
-  fc1.n_experts = s.N;
-  fc1.a_rows = s.T;
-  fc1.B = w1;
-  fc1.B2 = w3;
-  fc1.bias = bias ? b1 : nullptr;
-  fc1.C = ws;  // H
-  fc1.K = s.D;
-  fc1.n_out = s.F;
-  fc1.act = s.act == MOE_ACT_GELU ? kActGelu : s.act == MOE_ACT_RELU ? kActRelu : kActSwiGLU;
-
-  GroupedGemm fc2{};
-  fc2.A = ws;
-  fc2.perm = nullptr;
-  fc2.topk = 1;
-  fc2.offsets = offsets;
-  fc2.n_experts = s.N;
-  fc2.a_rows = s.T * s.k;
-  fc2.B = w2;
-  fc2.B2 = nullptr;
-  fc2.bias = bias ? b2 : nullptr;
-  fc2.C = y_perm;
-  fc2.K = s.F;
-  fc2.n_out = s.D;
-  fc2.act = kActNone;
-
-  hipError_t e;
-  if (s.dtype == MOE_DTYPE_BF16) {
-    const int64_t expect = expected_rows(s);
-    e = launch_grouped_gemm_bf16(fc1, expect, st);
-    if (e == hipSuccess) e = launch_grouped_gemm_bf16(fc2, expect, st);
-  } else {
-    e = launch_grouped_gemm_f32(fc1, st);
-    if (e == hipSuccess) e = launch_grouped_gemm_f32(fc2, st);
-  }
+  hipError_t e = launch_up(s, x, perm, offsets, w1, b1, w3, ws, st);
+  if (e == hipSuccess) e = launch_down(s, ws, offsets, w2, b2, y_perm, st);
   return hip_status(e);
 }
 
@@ -188,6 +196,29 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm, c
   if (!ws || ws_bytes < ffn_ws_bytes(s)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
   return expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, (hipStream_t)stream);
+}
+
+int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
+                  const void* w1, const void* b1, const void* w3, void* h, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !perm || !offsets || !w1 || !h) return MOE_ERR_INVALID_ARG;
+  if (s.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_HAS_BIAS) && !b1) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_up(s, x, perm, offsets, w1, b1, w3, h, (hipStream_t)stream));
+}
+
+int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* offsets, const void* w2,
+                    const void* b2, void* y_perm, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!h || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_HAS_BIAS) && !b2) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_down(s, h, offsets, w2, b2, y_perm, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* slot, const float* topk_gate,

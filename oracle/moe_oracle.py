@@ -205,11 +205,11 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def expert_mlp(X, act: str, w1, b1=None, w3=None, w2=None, b2=None) -> np.ndarray:
-    """One expert on rows X[m, D] -> Y[m, D].
+def expert_hidden(X, act: str, w1, b1=None, w3=None) -> np.ndarray:
+    """First half of one expert on rows X[m, D] -> H[m, F].
 
-    gelu/relu: Y = act(X w1^T + b1) w2^T + b2 (the notebook's Expert).
-    swiglu:    Y = (silu(X w1^T) * (X w3^T)) w2^T.
+    gelu/relu: H = act(X w1^T + b1) (the notebook's Expert: fc1, then the
+    activation).  swiglu: H = silu(X w1^T) * (X w3^T).
     Weights use the nn.Linear layout [out, in].
     """
     X = f64(X)
@@ -217,17 +217,26 @@ def expert_mlp(X, act: str, w1, b1=None, w3=None, w2=None, b2=None) -> np.ndarra
     if b1 is not None:
         Z = Z + f64(b1)[None, :]
     if act == "gelu":
-        H = gelu_erf(Z)
-    elif act == "relu":
-        H = relu(Z)
-    elif act == "swiglu":
-        H = silu(Z) * (X @ f64(w3).T)
-    else:
-        raise ValueError(f"unknown activation {act!r}")
-    Y = H @ f64(w2).T
+        return gelu_erf(Z)
+    if act == "relu":
+        return relu(Z)
+    if act == "swiglu":
+        return silu(Z) * (X @ f64(w3).T)
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def expert_output(H, w2, b2=None) -> np.ndarray:
+    """Second half of one expert (fc2 of the notebook's Expert):
+    Y[m, D] = H w2^T + b2."""
+    Y = f64(H) @ f64(w2).T
     if b2 is not None:
         Y = Y + f64(b2)[None, :]
     return Y
+
+
+def expert_mlp(X, act: str, w1, b1=None, w3=None, w2=None, b2=None) -> np.ndarray:
+    """One expert on rows X[m, D] -> Y[m, D]: expert_output of expert_hidden."""
+    return expert_output(expert_hidden(X, act, w1, b1, w3), w2, b2)
 
 
 def _expert_params(params: dict, e: int) -> dict:

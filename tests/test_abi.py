@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
+              "moe_combine", "moe_forward",
               "moe_capacity", "moe_workspace_bytes", "moe_status_string"):
         assert n in names
 
@@ -119,6 +120,12 @@ def test_entry_points_reject_null_pointers_before_launch(lib):
                               None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
     assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, fake, fake, None, fake, fake, 16,
                               None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, None, fake,
+                             None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(s, fake, fake, fake, None, None, None) == L.MOE_ERR_INVALID_ARG
+    sb = ctypes.byref(_shape(act=L.MOE_ACT_GELU, flags=L.MOE_HAS_BIAS))
+    assert lib.moe_expert_down(sb, fake, fake, fake, None, fake, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(_shape(flags=L.MOE_RESIDUAL)), fake, fake, fake, None, fake,
                            None) == L.MOE_ERR_INVALID_ARG
     args = [fake] * 16
@@ -140,6 +147,8 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
     assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None) == L.MOE_OK
     assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, None) == L.MOE_OK
+    assert lib.moe_expert_down(s, fake, fake, fake, None, fake, None) == L.MOE_OK
 
 
 def test_library_has_no_undefined_internal_symbols():

@@ -246,6 +246,56 @@ def test_stage_chain(gpu, key, scaled_cases):
     assert row_rel_err(out2.float().cpu().numpy().astype(np.float64), want) <= tol
 
 
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+def test_expert_up_down(gpu, key, scaled_cases):
+    """fc1(+act) and fc2 as separate launches: H against the oracle's hidden
+    rows, fc2 alone on the oracle's H, and up+down equal to moe_expert_ffn."""
+    cfg, inp, ref = _scaled(key, scaled_cases)
+    _say(f"expert up/down {key}: T={cfg.T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k} {cfg.act}")
+    g = to_gpu(inp)
+    shape = api.MoeShape.from_config(cfg)
+    buf = api.MoeBuffers(shape)
+    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
+    api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
+    A = cfg.T * cfg.k
+    h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=gpu)
+    y_ud = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
+    y_ffn = torch.empty_like(y_ud)
+    api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h)
+    api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_ud)
+    api.expert_ffn(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], g["w2"], g["b2"],
+                   y_ffn, buf.ws)
+    torch.cuda.synchronize()
+    check_routing(buf, ref, cfg)
+    off, perm = ref["offsets"], ref["perm"]
+    K = int(off[-1])
+    assert torch.equal(y_ud[:K], y_ffn[:K])
+    # oracle hidden rows, expert by expert in grouped order
+    h_ref = np.zeros((K, cfg.F))
+    for e in range(cfg.N):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            toks = perm[r0:r1] // cfg.k
+            sl = lambda n: None if inp.get(n) is None else inp[n][e]  # noqa: E731
+            h_ref[r0:r1] = oracle.expert_hidden(inp["x"][toks], cfg.act, sl("w1"), sl("b1"), sl("w3"))
+    hg = h[:K].float().cpu().numpy().astype(np.float64)
+    assert row_rel_err(hg, h_ref) <= TOL[cfg.dtype]
+    # fc2 alone, fed the oracle's H rounded to the layer dtype
+    h_in = torch.zeros(A, cfg.F, dtype=shape.torch_dtype)
+    h_in[:K] = torch.from_numpy(h_ref).to(shape.torch_dtype)
+    y2 = torch.empty_like(y_ud)
+    api.expert_down(shape, h_in.to(gpu), buf.offsets, g["w2"], g["b2"], y2)
+    torch.cuda.synchronize()
+    y2_ref = np.zeros((K, cfg.D))
+    h_in64 = h_in[:K].double().numpy()
+    for e in range(cfg.N):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            y2_ref[r0:r1] = oracle.expert_output(h_in64[r0:r1], inp["w2"][e],
+                                                 None if inp.get("b2") is None else inp["b2"][e])
+    assert row_rel_err(y2[:K].float().cpu().numpy().astype(np.float64), y2_ref) <= TOL[cfg.dtype]
+
+
 # ------------------------------------------ full-size layers, sampled rows
 FULL = ["c2", "c2cf15", "c3", "c4", "c5"]
 
@@ -271,3 +321,38 @@ def test_forward_full_size(gpu, key):
     y = buf.out.float().cpu().numpy().astype(np.float64)[sample]
     err = check_outputs(y, ref, cfg, inp["x"].double().numpy()[sample], tokens=sample)
     _say(f"  row-rel err {err:.3e} over {sample.size} sampled tokens, dropped {ref['n_dropped']}")
+
+
+# ------------------------------------------ HIP-graph capture of the layer
+@pytest.mark.parametrize("key", ["c2", "c5"])
+def test_graph_replay_matches_eager(gpu, key, scaled_cases):
+    """moe_forward captured into a HIP graph: every replay, with eager work
+    and synchronisations in between, equals the eager result bit for bit."""
+    cfg, inp, ref = _scaled(key, scaled_cases)
+    _say(f"graph replay {key}: T={cfg.T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k}")
+    g = to_gpu(inp)
+    shape = api.MoeShape.from_config(cfg)
+    eager = api.MoeBuffers(shape)
+    eager.forward(g["x"], g)
+    torch.cuda.synchronize()
+    want = eager.out.clone()
+    want_slot = eager.slot.clone()
+    cap = api.MoeBuffers(shape)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            cap.forward(g["x"], g, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        cap.out.fill_(0)
+        cap.slot.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cap.out, want), rep
+        assert torch.equal(cap.slot, want_slot), rep
+        eager.forward(g["x"], g)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager.out, want)
