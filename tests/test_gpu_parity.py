@@ -147,6 +147,12 @@ def test_dispatch_adversarial(gpu):
     # skewed (Zipf-like) routing
     p = 1.0 / np.arange(1, 17) ** 1.2
     _dispatch_case(gpu, _rand_idx(rng, 4096, 16, 2, p / p.sum()), 16, None)
+    # ids outside [0, N) are dropped and not counted
+    bad = _rand_idx(rng, 1200, 8, 2)
+    bad[::7, 0] = -1
+    bad[::11, 1] = 8
+    _dispatch_case(gpu, bad, 8, None)
+    _dispatch_case(gpu, bad, 8, 120)
 
 
 # ----------------------------------------------- scaled layers, every token
