@@ -10,8 +10,11 @@
 //     k+1 rounds of (value, index) arg-max over the group with xor shuffles.
 //     Larger value wins, equal values go to the lower expert index.
 //  3. If two of the top-(k+1) fp32 logits are closer than kRefineMargin, the
-//     whole block recomputes that token's logits in fp64 from exact products
-//     (bf16*bf16 and fp32*fp32 are exact in fp64) and ranks those instead.
+//     token is ranked again by its wave from exact logits: only the experts
+//     whose fp32 logit lies within the margin of the (k+1)-th value can change
+//     places (the fp32 error is far below half the margin), and only those
+//     are recomputed, in fp64 from exact products (bf16*bf16 and fp32*fp32
+//     are exact in fp64).  Near-ties are rare: a handful of tokens per batch.
 //  4. Gates are softmax probabilities of the chosen experts, optionally
 //     renormalised over the k choices.
 #include <float.h>
@@ -43,11 +46,8 @@ template <typename V>
 __device__ inline V neg_inf();
 template <>
 __device__ inline float neg_inf<float>() { return -FLT_MAX; }
-template <>
-__device__ inline double neg_inf<double>() { return -DBL_MAX; }
 
 __device__ inline float vexp(float v) { return expf(v); }
-__device__ inline double vexp(double v) { return exp(v); }
 
 // Ranks one token within a 16-lane group.  vals: LDS row of N logits.
 // Returns true when the top-(k+1) are separated by at least `margin`
@@ -128,11 +128,6 @@ __device__ bool group_rank(const V* vals, const RouteArgs& a, int64_t t, int l16
   }
   return true;
 }
-
-template <typename T>
-__device__ inline double to_f64(T v) { return (double)(float)v; }
-template <>
-__device__ inline double to_f64<float>(float v) { return (double)v; }
 
 // Chunk of 16 bytes of the input dtype.
 template <typename T>
@@ -249,56 +244,191 @@ __device__ void logits_f32(const RouteArgs& a, int64_t t0, int tid, float* lg, i
 __device__ inline double exact_product(float x, bf16 w) { return (double)(x * (float)w); }
 __device__ inline double exact_product(float x, float w) { return (double)x * (double)w; }
 
-// Exact-product fp64 logits of token t, computed by the whole block: thread
-// (expert e = tid % N, slice s = tid / N) sums its share of the D/8 (bf16) or
-// D/4 (fp32) 16-byte chunks of row e of the router against the token's row
-// (staged in LDS as fp32, which holds bf16 and fp32 values exactly, when xf
-// is given; else read from global memory); the slices are then added per
-// expert into dl.  Router chunks are loaded 8 at a time so the loads overlap;
-// four fp64 accumulators shorten the dependency chain.
-template <typename T>
-__device__ void refine_block(const RouteArgs& a, int64_t t, int tid, float* xf, double* dp,
-                             double* dl) {
+// Exact ranking of one near-tie token by one whole wave.  The token's fp32
+// logits (row lgrow, N values) locate the candidates: the experts whose fp32
+// logit is at least the (k+1)-th largest minus kRefineMargin.  Any other
+// expert lies, in exact arithmetic, below k+1 of the candidates, because the
+// fp32 logits differ from the exact ones by far less than half the margin.
+// Each candidate's logit is recomputed in fp64 from exact products (the wave
+// splits D into 16-byte chunks; butterfly sum, so identical router rows give
+// identical values) and the top k candidates by exact logit, ties to the
+// lower index, are the selection.  Gates: softmax over all N experts with the
+// exact values for the candidates and the fp32 values for the rest.
+// NJ = experts held per lane (expert e = lane + 64 j).
+template <typename T, int NJ>
+__device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t t, int lane) {
   constexpr int W = Chunk<T>::W;
   typedef typename Chunk<T>::type V;
-  const int D = a.D, N = a.N;
-  const T* xrow = (const T*)a.x + t * (int64_t)D;
-  if (xf) {
-    for (int d = tid; d < D; d += 256) xf[d] = (float)xrow[d];
-    __syncthreads();
-  }
-  const int S = (256 / N) > 0 ? 256 / N : 1;
-  const int e = tid % N, s = tid / N;
-  if (s < S) {
-    const int chunks = D / W;
-    const int c0 = chunks * s / S, c1 = chunks * (s + 1) / S;
-    const V* wv = (const V*)((const T*)a.wr + (int64_t)e * D);
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    auto add_chunk = [&](int c, const V& w) {
+  const int N = a.N, k = a.k, D = a.D;
+  float v[NJ];
 #pragma unroll
-      for (int v = 0; v < W; ++v) {
-        const float xx = xf ? xf[c * W + v] : (float)xrow[c * W + v];
-        acc[v & 3] += exact_product(xx, w[v]);
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = (e < N) ? lgrow[e] : -FLT_MAX;
+  }
+  // the (k+1)-th largest fp32 logit (or the N-th when k = N)
+  const int nsel = (k + 1 <= N) ? k + 1 : N;
+  uint32_t taken = 0;
+  float vk = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK + 1; ++r) {
+    if (r < nsel) {
+      float bv = -FLT_MAX;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        if (e < N && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
       }
-    };
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      V w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = wv[c + u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) add_chunk(c + u, w[u]);
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      vk = bv;
     }
-    for (; c < c1; ++c) add_chunk(c, wv[c]);
-    dp[s * N + e] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
-  __syncthreads();
-  if (tid < N) {
-    double sum = a.has_bias ? (double)a.br[tid] : 0.0;
-    for (int j = 0; j < S; ++j) sum += dp[j * N + tid];
-    dl[tid] = sum;
+  const float th = (nsel == N) ? -FLT_MAX : vk - kRefineMargin;
+  uint32_t cand = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < N && v[j] >= th) cand |= 1u << j;
   }
-  __syncthreads();
+  // exact logits of the candidates, one candidate at a time
+  const V* xv = (const V*)((const T*)a.x + t * (int64_t)D);
+  const int chunks = D / W;
+  double ex[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) ex[j] = -DBL_MAX;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    uint64_t m = __ballot((cand >> j) & 1u);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int e = l + 64 * j;
+      const V* wv = (const V*)((const T*)a.wr + (int64_t)e * D);
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int c0 = lane; c0 < chunks; c0 += 64 * 4) {
+        V xs[4], ws[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 64 * u;
+          if (c < chunks) {
+            xs[u] = xv[c];
+            ws[u] = wv[c];
+          }
+        }
+        // keep the loads together: otherwise each is sunk to its use
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (c0 + 64 * u < chunks) {
+#pragma unroll
+            for (int q = 0; q < W; ++q) acc[q & 3] += exact_product((float)xs[u][q], ws[u][q]);
+          }
+        }
+      }
+      double sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      if (a.has_bias) sum += (double)a.br[e];
+      if (lane == l) ex[j] = sum;
+    }
+  }
+  // top k of the candidates by exact logit; lane r keeps round r's choice
+  int my_i = 0;
+  double my_v = 0.0;
+  uint32_t used = 0;
+  for (int r = 0; r < k; ++r) {
+    double bv = -DBL_MAX;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (((cand >> j) & 1u) && !((used >> j) & 1u) && better(ex[j], e, bv, bi)) {
+        bv = ex[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) used |= 1u << (bi >> 6);
+    if (lane == r) {
+      my_i = bi;
+      my_v = bv;
+    }
+  }
+  const double vmax = __shfl(my_v, 0);
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < N) s += exp((((cand >> j) & 1u) ? ex[j] : (double)v[j]) - vmax);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  const double p = (lane < k) ? exp(my_v - vmax) / s : 0.0;
+  double ps = p;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+  if (lane < k) {
+    a.idx[t * k + lane] = my_i;
+    a.gate[t * k + lane] = (float)(a.renorm ? p / ps : p);
+  }
+  if (a.logits) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if ((cand >> j) & 1u) a.logits[t * N + e] = (float)ex[j];
+    }
+  }
+}
+
+// Ranks the rows r = it*16 + wave*4 + group of the block's logits (16-lane
+// groups, fp32); the tokens whose top-(k+1) fp32 logits are too close are
+// then ranked again, one after the other, by the whole wave.
+template <typename T, int NT, int ITERS>
+__device__ void rank_rows(const RouteArgs& a, const float* lg, int ldl, int64_t t0, int wave,
+                          int lane) {
+  constexpr int NJ = (16 * NT + 63) / 64;
+  const int grp = lane >> 4, l16 = lane & 15;
+  uint32_t marked = 0;
+#pragma unroll 1
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = it * 16 + wave * 4 + grp;
+    const int64_t t = t0 + r;
+    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
+    if (a.logits && t < a.T)
+      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
+    const uint64_t bad = __ballot(!ok && t < a.T);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if ((bad >> (16 * g)) & 1ull) marked |= 1u << (it * 4 + g);
+  }
+  marked = __builtin_amdgcn_readfirstlane(marked);
+  while (marked) {
+    const int m = __builtin_ctz(marked);
+    marked &= marked - 1;
+    const int r = (m / 4) * 16 + wave * 4 + (m % 4);
+    exact_rank_wave<T, NJ>(a, lg + r * ldl, t0 + r, lane);
+  }
 }
 
 // Block = 4 waves = 32 tokens.
@@ -308,14 +438,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // k steps whose operands are loaded together (loads in flight per wave)
   constexpr int U = NT >= 16 ? 2 : (NT >= 8 ? 3 : (NT >= 4 ? 6 : 8));
   __shared__ float lg[32 * ldl];  // logits of the block's 32 tokens
-  __shared__ double dp[256];
-  __shared__ double dl[16 * NT];
-  __shared__ int flagged[32];
-  __shared__ int nflag;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
-  if (tid == 0) nflag = 0;
 
   if constexpr (sizeof(T) == 2) {
     logits_bf16<NT, U>(a, t0, wave, lane, lg, ldl);
@@ -324,28 +449,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  const int grp = lane >> 4, l16 = lane & 15;
-  for (int it = 0; it < 2; ++it) {
-    const int r = it * 16 + wave * 4 + grp;
-    const int64_t t = t0 + r;
-    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
-    if (a.logits && t < a.T)
-      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
-    if (!ok && l16 == 0 && t < a.T) flagged[atomicAdd(&nflag, 1)] = r;
-  }
-  __syncthreads();
-  const int nf = nflag;  // block-uniform
-  for (int i = 0; i < nf; ++i) {
-    const int r = flagged[i];
-    const int64_t t = t0 + r;
-    refine_block<T>(a, t, tid, nullptr, dp, dl);
-    if (wave == 0 && grp == 0) {
-      group_rank<double, NT>(dl, a, t, l16, -1.0, true);
-      if (a.logits)
-        for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = (float)dl[e];
-    }
-    __syncthreads();
-  }
+  rank_rows<T, NT, 2>(a, lg, ldl, t0, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,7 +459,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 // the router matrix both split evenly over the 4 waves).  TB tokens per
 // block (64, 32 or 16): wave w computes m-tile w % (TB/16) over the k
 // sub-steps congruent to w / (TB/16); partial tiles are summed in LDS in
-// fixed wave order.  Selection and fp64 re-ranking as above.
+// fixed wave order.  Selection and near-tie marking as above.
 template <int NT, int TB>
 struct RouteRing {
   static constexpr int NP = 16 * NT;          // expert rows held (padded)
@@ -401,17 +505,12 @@ __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* ring = (bf16*)smem_raw;
   float* lg = (float*)smem_raw;  // logits tiles, after the ring is drained
-  __shared__ double dp[256];
-  __shared__ double dl[16 * NT];
-  __shared__ int flagged[TB];
-  __shared__ int nflag;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t t0 = (int64_t)blockIdx.x * TB;
   const int D = a.D;
   const int KT = D / 128;
-  if (tid == 0) nflag = 0;
 
   // dma sources: wave's instruction q covers 4 rows of A (x) or B (router)
   uint32_t src[R::NJ];
@@ -496,31 +595,7 @@ __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  const int grp = lane >> 4, l16 = lane & 15;
-  for (int it = 0; it < TB / 16; ++it) {
-    const int r = it * 16 + wave * 4 + grp;
-    const int64_t t = t0 + r;
-    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
-    if (a.logits && t < a.T)
-      for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
-    if (!ok && l16 == 0 && t < a.T) flagged[atomicAdd(&nflag, 1)] = r;
-  }
-  __syncthreads();
-  const int nf = nflag;
-  // fp32 copy of a flagged token's row goes after the logits tiles if it fits
-  constexpr int kLgBytes = (R::kLogitFloats * 4 + 15) / 16 * 16;
-  float* xd = (R::kBytes - kLgBytes >= 4 * D) ? (float*)(smem_raw + kLgBytes) : nullptr;
-  for (int i = 0; i < nf; ++i) {
-    const int r = flagged[i];
-    const int64_t t = t0 + r;
-    refine_block<bf16>(a, t, tid, xd, dp, dl);
-    if (wave == 0 && grp == 0) {
-      group_rank<double, NT>(dl, a, t, l16, -1.0, true);
-      if (a.logits)
-        for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = (float)dl[e];
-    }
-    __syncthreads();
-  }
+  rank_rows<bf16, NT, TB / 16>(a, lg, ldl, t0, wave, lane);
 }
 
 template <int NT, int TB>
