@@ -215,10 +215,10 @@ def main():
         api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
         if ev is not None:
             ev[1].record(s)
-        api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, s)
+        api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, buf.ws, s)
         if ev is not None:
             ev[2].record(s)
-        api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_perm, s)
+        api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_perm, buf.ws, s)
         if ev is not None:
             ev[3].record(s)
         api.combine(shape, y_perm, buf.slot, buf.topk_gate, g["x"], buf.out, s)

@@ -148,6 +148,11 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
 /* The two halves of moe_expert_ffn as separate launches, for callers that
  * keep the hidden activations themselves or time the projections apart.
  * Both always use the grouped GEMM (MOE_FUSED_DECODE is ignored here).
+ * ws: NULL, or scratch of at least moe_workspace_bytes(shape) bytes (256-byte
+ * aligned) that lets a bf16 projection split its last, partial round of
+ * tiles along K (fp32 partial sums, added in a fixed order by a second
+ * launch); results then equal those of moe_expert_ffn and moe_forward, which
+ * always split.  A too-small ws returns MOE_ERR_WORKSPACE.
  *
  * moe_expert_up: the expert's first projection and activation (the
  * notebook's Expert: fc1 then GELU or ReLU, biases with MOE_HAS_BIAS; for
@@ -158,13 +163,14 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
  * dtype after the activation.  w3 may be NULL unless the act is SwiGLU. */
 int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm,
                   const int32_t* offsets, const void* w1, const void* b1, const void* w3,
-                  void* h, moe_stream_t stream);
+                  void* h, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* moe_expert_down: the expert's second projection (fc2):
  *   y_perm[r, :] = h[r, :] . w2[e]^T + b2[e]                r in [offsets[e], offsets[e+1])
  * h as written by moe_expert_up; y_perm [T*k, D] in the shape's dtype. */
 int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* offsets,
-                    const void* w2, const void* b2, void* y_perm, moe_stream_t stream);
+                    const void* w2, const void* b2, void* y_perm, void* ws, size_t ws_bytes,
+                    moe_stream_t stream);
 
 /* Combine ("Dispatch and gather"): out[t] = (x[t] with MOE_RESIDUAL, else 0)
  * + sum over j = 0..k-1 with slot[t*k+j] >= 0 of topk_gate[t,j] *

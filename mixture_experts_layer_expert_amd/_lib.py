@@ -54,8 +54,9 @@ _SIGS = {
     "moe_dispatch": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_expert_ffn": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
-    "moe_expert_up": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_expert_down": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_expert_up": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                     _vp]),
+    "moe_expert_down": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_forward": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

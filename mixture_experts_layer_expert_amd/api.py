@@ -128,22 +128,33 @@ def expert_ffn(shape: MoeShape, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def expert_up(shape: MoeShape, x, perm, offsets, w1, b1, w3, h, stream=None):
+def _ws_arg(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws, None, "ws"), ws.numel() * ws.element_size()
+
+
+def expert_up(shape: MoeShape, x, perm, offsets, w1, b1, w3, h, ws=None, stream=None):
+    """fc1 + activation into h; ws (optional, >= workspace_bytes) allows the
+    split of the last round of tiles, as moe_expert_ffn does."""
     dt = shape.torch_dtype
     i32 = torch.int32
     sc = shape.c()
+    wp, wn = _ws_arg(ws)
     _check("moe_expert_up", L.load().moe_expert_up(
         ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(perm, i32, "perm"), _ptr(offsets, i32, "offsets"),
-        _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"), _ptr(w3, dt, "w3"), _ptr(h, dt, "h"),
+        _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"), _ptr(w3, dt, "w3"), _ptr(h, dt, "h"), wp, wn,
         _stream(stream)))
 
 
-def expert_down(shape: MoeShape, h, offsets, w2, b2, y_perm, stream=None):
+def expert_down(shape: MoeShape, h, offsets, w2, b2, y_perm, ws=None, stream=None):
+    """fc2 of the hidden rows into y_perm; ws as for expert_up."""
     dt = shape.torch_dtype
     sc = shape.c()
+    wp, wn = _ws_arg(ws)
     _check("moe_expert_down", L.load().moe_expert_down(
         ctypes.byref(sc), _ptr(h, dt, "h"), _ptr(offsets, torch.int32, "offsets"),
-        _ptr(w2, dt, "w2"), _ptr(b2, dt, "b2"), _ptr(y_perm, dt, "y_perm"), _stream(stream)))
+        _ptr(w2, dt, "w2"), _ptr(b2, dt, "b2"), _ptr(y_perm, dt, "y_perm"), wp, wn, _stream(stream)))
 
 
 def combine(shape: MoeShape, y_perm, slot, topk_gate, x_residual, out, stream=None):

@@ -80,8 +80,9 @@ struct Tile {
   static constexpr int kLdsA = BM * BK;     // bf16 elements per stage
   static constexpr int kLdsB = BNB * BK;
   static constexpr int kStageBytes = (kLdsA + kLdsB) * 2;
-  // as many stages (2..4) as fit in 150 KiB (room for the work list)
-  static constexpr int kStages = (4 * kStageBytes <= 150 * 1024) ? 4 : (3 * kStageBytes <= 150 * 1024) ? 3 : 2;
+  // as many stages (2..8) as fit in 150 KiB (room for the work list)
+  static constexpr int kFit = (150 * 1024) / kStageBytes;
+  static constexpr int kStages = kFit > 8 ? 8 : (kFit < 2 ? 2 : kFit);
   static constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
   static_assert(BK == 32 || BK == 64, "BK 32 or 64");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -102,22 +103,23 @@ struct Params {
   int K;
   int n_out;   // output columns of C (F for fc1, D for fc2)
   int act;
+  float* part; // split-K partial tiles of the last round, or nullptr: never split
 };
 
-// Waits until at most `younger` jobs' worth of DMA instructions (n per job)
-// are outstanding.  Loads return in issue order, so this means every older
-// job has landed in LDS.  Epilogue stores issued after a job only make the
-// wait stricter.
-template <int NJ>
+// Waits until at most `younger` jobs' worth of DMA instructions (NJ per job)
+// are outstanding (younger is clamped to K).  Loads return in issue order,
+// so this means every older job has landed in LDS.  Epilogue stores issued
+// after a job only make the wait stricter.
+template <int NJ, int K>
 __device__ inline void wait_dma(int younger) {
-  if (younger <= 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else if (younger == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NJ) : "memory");
-  } else if (younger == 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NJ) : "memory");
+  if constexpr (K > 0) {
+    if (younger >= K) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K * NJ) : "memory");
+      return;
+    }
+    wait_dma<NJ, K - 1>(younger);
   } else {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NJ) : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
@@ -132,8 +134,176 @@ __device__ inline void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Persistent grid of the grouped GEMM: one workgroup per CU, a multiple of 8
+// (the XCD count) so that every XCD gets the same number of workgroups.
+inline int gemm_grid() {
+  const int g = device_cu_count();
+  return (g + 7) / 8 * 8;
+}
+
 __device__ inline float fast_silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
+// ---- work list (shared by the GEMM and its split-K finishing kernel)
+//
+// Tiles per expert: ceil(rows / BM) row tiles x ceil(n_out / BN_OUT)
+// column tiles, numbered expert by expert, row tile fastest.  With G
+// persistent workgroups the first rounds*G tiles are full rounds: XCD x
+// (= workgroup id % 8) gets the contiguous block of rounds*(G/8) tiles and its
+// workgroups stride through it.  The R = total - rounds*G tiles left over
+// (dealt round-robin over the XCDs) would keep only R workgroups busy in a
+// last, partial round; when a
+// workspace for partial sums is given they are instead cut into S = G / R
+// chunks along K (S <= KT), one chunk per workgroup; chunks write fp32
+// partial tiles and a second kernel sums them in chunk order and applies the
+// epilogue.  Every workgroup then gets the same number of jobs to within one
+// chunk.
+struct TileInfo {
+  int e, row0, row_end, n0;
+};
+
+template <int BM, int BN_OUT>
+struct WorkList {
+  int total, rounds, R, S;
+
+  // Prefix sum of the tiles of each expert into tile_start[0..N]; called by
+  // every thread of the block (nthreads >= 64 threads, N <= 256 experts).
+  __device__ void build(const Params& p, int* tile_start, int* scan, int tid, int nthreads) {
+    constexpr int kPer = kMaxExperts / 64;  // experts per thread at 64 threads
+    const int N = p.n_experts;
+    const int ntiles = (p.n_out + BN_OUT - 1) / BN_OUT;
+    int my[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * nthreads;
+      my[u] = 0;
+      if (e < N) {
+        const int rows = p.offsets[e + 1] - p.offsets[e];
+        my[u] = ((rows + BM - 1) / BM) * ntiles;
+        scan[e] = my[u];
+      }
+    }
+    __syncthreads();
+    for (int d = 1; d < N; d <<= 1) {
+      int v[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * nthreads;
+        v[u] = (e < N && e >= d) ? scan[e - d] : 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * nthreads;
+        if (e < N && e >= d) scan[e] += v[u];
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * nthreads;
+      if (e < N) tile_start[e] = scan[e] - my[u];
+    }
+    if (tid == 0) tile_start[N] = (N > 0) ? scan[N - 1] : 0;
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(tile_start[N]);
+  }
+
+  __device__ void split(int G, int KT, bool can_split) {
+    rounds = total / G;
+    R = total - rounds * G;
+    int s = 1;
+    if (can_split && R > 0) {
+      s = G / R;
+      if (s > KT) s = KT;
+      if (s < 1) s = 1;
+    }
+    // block-uniform: keep them in scalar registers
+    rounds = __builtin_amdgcn_readfirstlane(rounds);
+    R = __builtin_amdgcn_readfirstlane(R);
+    S = __builtin_amdgcn_readfirstlane(s);
+  }
+
+  __device__ TileInfo info(const Params& p, const int* tile_start, int L) const {
+    const int N = p.n_experts;
+    int lo = 0, hi = N - 1;  // expert of tile L: last e with tile_start[e] <= L
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_start[mid] <= L) lo = mid; else hi = mid - 1;
+    }
+    TileInfo t;
+    t.e = lo;
+    const int row_begin = p.offsets[lo];
+    const int rows_e = p.offsets[lo + 1] - row_begin;
+    const int mtiles = (rows_e + BM - 1) / BM;
+    const int local = L - tile_start[lo];
+    t.row0 = row_begin + (local % mtiles) * BM;
+    t.row_end = row_begin + rows_e;
+    t.n0 = (local / mtiles) * BN_OUT;
+    return t;
+  }
+};
+
+// Epilogue of one output tile: acc (this wave's 32x32 sub-tiles, weight rows
+// x tokens) -> bias, activation, bf16 stores.  A lane owns token column
+// (lane & 31) of each 32x32 tile and output rows (r/4)*8 + (lane/32)*4 + r%4.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT>
+__device__ inline void store_tile(const Params& p, const TileInfo& tc,
+                                  f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][Tile<BM, BNB, WM, WN, BK>::FM],
+                                  int wm, int wn, int lane) {
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  constexpr bool kSwiGLU = (ACT == kActSwiGLU);
+#pragma unroll
+  for (int j = 0; j < TL::FM; ++j) {
+    const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
+    const bool live = r_out < tc.row_end;
+    bf16* crow = p.C + (size_t)r_out * p.n_out;
+    if constexpr (kSwiGLU) {
+#pragma unroll
+      for (int ip = 0; ip < TL::FN / 2; ++ip) {
+        const int fbase = tc.n0 + (wn * TL::TN / 64 + ip) * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = fbase + q * 8 + (lane >> 5) * 4;
+          bf16x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            v[u] = (bf16)(fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u]);
+          if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TL::FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = tc.n0 + wn * TL::TN + i * 32 + q * 8 + (lane >> 5) * 4;
+          bf16x4 bv = {};
+          if (p.bias && f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
+          bf16x4 v;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float z = acc[i][j][q * 4 + u] + (float)bv[u];
+            if constexpr (ACT == kActGelu) z = gelu_erf(z);
+            if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
+            v[u] = (bf16)z;
+          }
+          if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
+      }
+    }
+  }
+}
+
+// Partial tile q of the split last round: element (wave, i, j, r, lane) of
+// the accumulators at a fixed position, so that stores and loads are whole
+// 256-byte wave rows.
+template <int FN, int FM>
+__device__ inline float* part_ptr(const Params& p, int q, int nw, int wave, int lane) {
+  return p.part + ((size_t)q * nw + wave) * (FN * FM * 16 * 64) + lane;
 }
 
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, int STAGES>
@@ -143,8 +313,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
   constexpr int BN_OUT = kSwiGLU ? BNB / 2 : BNB;  // output columns per tile
   constexpr int NJ = TL::QA + TL::QB;               // dma instructions per job per wave
-  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
-  static_assert(3 * NJ <= 63, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
+  static_assert((STAGES - 1) * NJ <= 63, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* sA = (bf16*)smem_raw;                       // [STAGES][BM][BK]
@@ -156,69 +326,41 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
-  const int N = p.n_experts;
-  const int ntiles = (p.n_out + BN_OUT - 1) / BN_OUT;
-
-  // ---- work list: tiles per expert and their prefix sum
-  int my_tiles = 0;
-  if (tid < N) {
-    int rows = p.offsets[tid + 1] - p.offsets[tid];
-    my_tiles = ((rows + BM - 1) / BM) * ntiles;
-    s_scan[tid] = my_tiles;
-  }
-  __syncthreads();
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
-    int v = 0;
-    if (tid < N && tid >= d) v = s_scan[tid - d];
-    __syncthreads();
-    if (tid < N && tid >= d) s_scan[tid] += v;
-    __syncthreads();
-  }
-  if (tid < N) s_tile_start[tid] = s_scan[tid] - my_tiles;
-  if (tid == 0) s_tile_start[N] = (N > 0) ? s_scan[N - 1] : 0;
-  __syncthreads();
-  const int total = s_tile_start[N];
-
-  // ---- XCD-aware assignment of the list
-  const int G = gridDim.x;  // multiple of 8
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = G / 8;
-  const int span = (total + 7) / 8;
-  const int L_begin = xcd * span + slot;
-  const int L_end = min(total, (xcd + 1) * span);
-
   const int KT = p.K / BK;
+
+  WorkList<BM, BN_OUT> wl;
+  wl.build(p, s_tile_start, s_scan, tid, TL::THREADS);
+  const int G = gridDim.x;  // multiple of 8
+  wl.split(G, KT, p.part != nullptr);
+
+  // ---- this workgroup's tiles: `rounds` full ones, then at most one more
+  // (a whole left-over tile, or one K chunk of one)
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = G / 8;
+  const int full_base = xcd * wl.rounds * per_xcd + slot;
+  // index among the left-over work items: dealt round-robin over the XCDs so
+  // that a short last round still spreads over every XCD's memory path
+  const int q_rem = slot * 8 + xcd;
+  const bool has_rem = q_rem < wl.R * wl.S;
+  const int n_mine = wl.rounds + (has_rem ? 1 : 0);
+  const int L_rem = __builtin_amdgcn_readfirstlane(wl.rounds * G + q_rem / wl.S);
+  const int c_rem = __builtin_amdgcn_readfirstlane(q_rem % wl.S);
+  const int k0_rem = __builtin_amdgcn_readfirstlane(c_rem * KT / wl.S);
+  const int k1_rem = __builtin_amdgcn_readfirstlane((c_rem + 1) * KT / wl.S);
+  auto tile_L = [&](int i) { return i < wl.rounds ? full_base + i * per_xcd : L_rem; };
+  auto tile_k0 = [&](int i) { return i < wl.rounds ? 0 : k0_rem; };
+  auto tile_k1 = [&](int i) { return i < wl.rounds ? KT : k1_rem; };
+
   const int lrow = lane / CPR;    // row within the dma instruction's rows
   const int lchunk = lane % CPR;  // physical chunk this lane fills
-
-  struct TileInfo {
-    int e, row0, row_end, n0;
-  };
-  auto tile_info = [&](int L) {
-    int lo = 0, hi = N - 1;  // expert of tile L: last e with tile_start[e] <= L
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_tile_start[mid] <= L) lo = mid; else hi = mid - 1;
-    }
-    TileInfo t;
-    t.e = lo;
-    const int row_begin = p.offsets[lo];
-    const int rows_e = p.offsets[lo + 1] - row_begin;
-    const int mtiles = (rows_e + BM - 1) / BM;
-    const int local = L - s_tile_start[lo];
-    t.row0 = row_begin + (local % mtiles) * BM;
-    t.row_end = row_begin + rows_e;
-    t.n0 = (local / mtiles) * BN_OUT;
-    return t;
-  };
 
   // ---- DMA side: per-lane 32-bit byte offsets of the tile being loaded,
   // added to wave-uniform base pointers (saddr + voffset addressing).
   uint32_t offA[TL::QA], offB[TL::QB];
   const char* b1e = (const char*)p.B;
   const char* b2e = (const char*)p.B;
-  int L_dma = L_begin, kt_dma = 0, job_issued = 0;
-  auto setup_dma = [&](int L) {
-    const TileInfo t = tile_info(L);
+  int i_dma = 0, kt_dma = 0, k1_dma = 0, job_issued = 0;
+  auto setup_dma = [&](int i) {
+    const TileInfo t = wl.info(p, s_tile_start, tile_L(i));
 #pragma unroll
     for (int q = 0; q < TL::QA; ++q) {
       const int trow = (wave * TL::QA + q) * RPI + lrow;  // row within the A tile
@@ -237,9 +379,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     const size_t eoff = (size_t)t.e * p.n_out * p.K * 2;
     b1e = (const char*)p.B + eoff;
     b2e = kSwiGLU ? (const char*)p.B2 + eoff : b1e;
+    kt_dma = tile_k0(i);
+    k1_dma = tile_k1(i);
   };
   auto issue_next = [&]() {
-    if (L_dma >= L_end) return;
+    if (i_dma >= n_mine) return;
     const int stage = job_issued % STAGES;
     bf16* a_dst = sA + stage * TL::kLdsA;
     bf16* b_dst = sB + stage * TL::kLdsB;
@@ -257,16 +401,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       dma16(base + offB[q], (lds_ptr_t)(b_dst + (wave * TL::QB + q) * 512));
     }
     ++job_issued;
-    if (++kt_dma == KT) {
-      kt_dma = 0;
-      L_dma += per_xcd;
-      if (L_dma < L_end) setup_dma(L_dma);
+    if (++kt_dma == k1_dma) {
+      if (++i_dma < n_mine) setup_dma(i_dma);
     }
   };
 
   // Prologue: fill every stage.  At the barrier of job j the stage of job j
   // is refilled with job j + STAGES, and job j + 1 must already be in flight.
-  if (L_begin < L_end) setup_dma(L_begin);
+  if (n_mine > 0) setup_dma(0);
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_next();
 
@@ -277,8 +419,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   // the job, so the stage can be refilled, and the first fragments of the
   // next job are read while the last sub-step's MFMAs run.
   constexpr int KS = BK / 16;
-  const int n_tiles_mine = (L_end > L_begin) ? (L_end - L_begin + per_xcd - 1) / per_xcd : 0;
-  const int n_jobs = n_tiles_mine * KT;
+  const int n_jobs = wl.rounds * KT + (has_rem ? k1_rem - k0_rem : 0);
   bf16x8 bf[2][TL::FN], af[2][TL::FM];
   auto load_frags = [&](int stage, int ks, int buf) {
     const bf16* a_s = sA + stage * TL::kLdsA;
@@ -322,11 +463,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
   };
 
-  int L_cmp = L_begin, kt_cmp = 0;
+  int i_cmp = 0, kt_cmp = 0, len_cmp = 0;
   TileInfo tc;
   if (n_jobs > 0) {
-    tc = tile_info(L_cmp);
-    wait_dma<NJ>(job_issued - 1);
+    tc = wl.info(p, s_tile_start, tile_L(0));
+    len_cmp = tile_k1(0) - tile_k0(0);
+    wait_dma<NJ, STAGES - 1>(job_issued - 1);
     ring_barrier();
     load_frags(0, 0, 0);
   }
@@ -341,64 +483,91 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
     // all fragments of this job are in registers: refill its stage later
     const bool more = job + 1 < n_jobs;
-    wait_dma<NJ>(job_issued - (job + 1) - 1);
+    wait_dma<NJ, STAGES - 1>(job_issued - (job + 1) - 1);
     ring_barrier();
     issue_next();
     if (more) load_frags((job + 1) % STAGES, 0, KS & 1);
     mfmas((KS - 1) & 1);
     if (more) interleave();
-    if (++kt_cmp == KT) {
-      // ---- epilogue: lane owns token column (lane & 31) of each 32x32 tile
-      // and output rows (r/4)*8 + (lane/32)*4 + r%4 of it.
-#pragma unroll
-      for (int j = 0; j < TL::FM; ++j) {
-        const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
-        const bool live = r_out < tc.row_end;
-        bf16* crow = p.C + (size_t)r_out * p.n_out;
-        if constexpr (kSwiGLU) {
-#pragma unroll
-          for (int ip = 0; ip < TL::FN / 2; ++ip) {
-            const int fbase = tc.n0 + (wn * TL::TN / 64 + ip) * 32;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int f = fbase + q * 8 + (lane >> 5) * 4;
-              bf16x4 v;
-#pragma unroll
-              for (int u = 0; u < 4; ++u)
-                v[u] = (bf16)(fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u]);
-              if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < TL::FN; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int f = tc.n0 + wn * TL::TN + i * 32 + q * 8 + (lane >> 5) * 4;
-              bf16x4 bv = {};
-              if (p.bias && f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
-              bf16x4 v;
-#pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                float z = acc[i][j][q * 4 + u] + (float)bv[u];
-                if constexpr (ACT == kActGelu) z = gelu_erf(z);
-                if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
-                v[u] = (bf16)z;
-              }
-              if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
-          }
-        }
-      }
+    // a finished tile goes through the epilogue, except a K chunk of a split
+    // left-over tile (always this workgroup's last): its partial sums are
+    // stored after the loop
+    if (++kt_cmp == len_cmp && more) {
+      store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
       kt_cmp = 0;
-      L_cmp += per_xcd;
-      if (more) tc = tile_info(L_cmp);
+      ++i_cmp;
+      tc = wl.info(p, s_tile_start, tile_L(i_cmp));
+      len_cmp = tile_k1(i_cmp) - tile_k0(i_cmp);
       zero_acc();
     }
   }
+  if (n_jobs > 0) {
+    if (!has_rem || wl.S == 1) {
+      store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
+    } else {
+      float* dst = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, wave, lane);
+#pragma unroll
+      for (int i = 0; i < TL::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j) {
+          float* d = dst + (i * TL::FM + j) * 1024;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) d[r * 64] = acc[i][j][r];
+        }
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Second half of the split last round: tile r of the R left-over tiles is
+// the sum of its S partial tiles, in chunk order (deterministic), followed by
+// the epilogue.  One wave per block, block (r, w) finishes wave w's share of
+// tile r with the lane layout of the GEMM, so a lane reads back exactly the
+// accumulator elements it would have held; each chunk's 16*FN*FM values are
+// loaded together.  G: the GEMM's grid.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT>
+__global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  constexpr int BN_OUT = (ACT == kActSwiGLU) ? BNB / 2 : BNB;
+  __shared__ int s_tile_start[kMaxExperts + 1];
+  __shared__ int s_scan[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int wave = blockIdx.y;
+  const int wm = wave / WN, wn = wave % WN;
+  WorkList<BM, BN_OUT> wl;
+  wl.build(p, s_tile_start, s_scan, lane, 64);
+  wl.split(G, p.K / BK, true);
+  if (wl.S == 1) return;
+  for (int r = blockIdx.x; r < wl.R; r += gridDim.x) {
+    const TileInfo tc = wl.info(p, s_tile_start, wl.rounds * G + r);
+    f32x16 acc[TL::FN][TL::FM];
+#pragma unroll
+    for (int i = 0; i < TL::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int c = 0; c < wl.S; ++c) {
+      const float* src = part_ptr<TL::FN, TL::FM>(p, r * wl.S + c, TL::NW, wave, lane);
+      f32x16 v[TL::FN][TL::FM];
+#pragma unroll
+      for (int i = 0; i < TL::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j) {
+          const float* d = src + (i * TL::FM + j) * 1024;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[i][j][e] = d[e * 64];
+        }
+      __builtin_amdgcn_sched_barrier(0);  // all of the chunk's loads in flight together
+#pragma unroll
+      for (int i = 0; i < TL::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FM; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] += v[i][j][e];
+    }
+    store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
+  }
 }
 
 template <int BM, int BNB, int WM, int WN, int BK, int ACT>
@@ -410,9 +579,13 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
   static const hipError_t attr_err = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::kLdsBytes);
   if (attr_err != hipSuccess) return attr_err;
-  int grid = device_cu_count();
-  grid = (grid + 7) / 8 * 8;
+  const int grid = gemm_grid();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TL::THREADS), TL::kLdsBytes, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.part) return e;
+  // at most grid/2 left-over tiles are ever split (S >= 2); one wave per block
+  hipLaunchKernelGGL((splitk_finish_kernel<BM, BNB, WM, WN, BK, ACT>), dim3(grid / 2, TL::NW), dim3(64),
+                     0, st, p, grid);
   return hipGetLastError();
 }
 
@@ -428,6 +601,56 @@ hipError_t launch_act(const Params& p, hipStream_t st) {
 
 }  // namespace
 
+namespace {
+
+// The instantiated tile shapes (BM x BNB, waves, BK).
+enum TileCfg { k256x256w8k64, k256x256w8k32, k256x128w4k64, k256x128w8k64, k128x256w8k64,
+               k128x256w8k32, k128x128w4k64, k64x256w4k64, k32x256w4k64, kNumCfg };
+const char* const kCfgName[kNumCfg] = {"256x256w8k64", "256x256w8k32", "256x128w4k64", "256x128w8k64",
+                                       "128x256w8k64", "128x256w8k32", "128x128w4k64", "64x256w4k64",
+                                       "32x256w4k64"};
+const int kCfgBM[kNumCfg] = {256, 256, 256, 256, 128, 128, 128, 64, 32};
+const int kCfgBN[kNumCfg] = {256, 256, 128, 128, 256, 256, 128, 256, 256};
+
+// Tile choice from the mean rows per expert: large groups use 256x256
+// tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64),
+// small ones 32x256 (4 waves of 32x64).  Output columns per tile: 256 (128
+// for SwiGLU).  MOE_GEMM_TILE (tuning) forces one of the instantiated
+// shapes for both projections, MOE_GEMM_TILE_UP / MOE_GEMM_TILE_DOWN for one.
+TileCfg choose_cfg(int64_t expected_rows, bool up) {
+  static const char* forced_all = getenv("MOE_GEMM_TILE");
+  static const char* forced_up = getenv("MOE_GEMM_TILE_UP");
+  static const char* forced_down = getenv("MOE_GEMM_TILE_DOWN");
+  const char* forced = up ? (forced_up ? forced_up : forced_all) : (forced_down ? forced_down : forced_all);
+  if (forced)
+    for (int c = 0; c < kNumCfg; ++c)
+      if (!strcmp(forced, kCfgName[c])) return (TileCfg)c;
+  if (expected_rows >= 192) return k256x256w8k64;
+  if (expected_rows >= 48) return k128x256w8k64;
+  return k32x256w4k64;
+}
+
+// Whether to let the kernel split its last round (which costs a second
+// launch): only when the expected work is a few rounds of large tiles, where
+// a partial last round idles a sizeable share of the GPU.  The estimate uses
+// the mean rows per expert; a wrong guess costs time, never correctness
+// (without p.part the kernel never splits).
+bool allow_split(TileCfg c, const GroupedGemm& g, int64_t expected_rows) {
+  if (kCfgBM[c] < 64) return false;
+  const int bn_out = g.act == kActSwiGLU ? kCfgBN[c] / 2 : kCfgBN[c];
+  const int64_t est = (int64_t)g.n_experts * ((expected_rows + kCfgBM[c] - 1) / kCfgBM[c]) *
+                      ((g.n_out + bn_out - 1) / bn_out);
+  return est < 6 * (int64_t)gemm_grid();
+}
+
+}  // namespace
+
+size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows) {
+  const TileCfg u = choose_cfg(expected_rows, true), d = choose_cfg(expected_rows, false);
+  const int a = kCfgBM[u] * kCfgBN[u], b = kCfgBM[d] * kCfgBN[d];
+  return (size_t)gemm_grid() * (size_t)(a > b ? a : b) * sizeof(float);
+}
+
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows, hipStream_t st) {
   Params p;
   p.A = (const bf16*)g.A;
@@ -442,22 +665,19 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.K = g.K;
   p.n_out = g.n_out;
   p.act = g.act;
-  // Tile choice from the mean rows per expert: large groups use 256x256
-  // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64),
-  // small ones 32x256 (4 waves of 32x64).  Output columns per tile: 256 (128
-  // for SwiGLU).
-  // MOE_GEMM_TILE (tuning): force one of the instantiated tile shapes.
-  static const char* forced = getenv("MOE_GEMM_TILE");
-  if (forced) {
-    if (!strcmp(forced, "256x256w8k64")) return launch_act<256, 256, 2, 4, 64>(p, st);
-    if (!strcmp(forced, "256x256w8k32")) return launch_act<256, 256, 2, 4, 32>(p, st);
-    if (!strcmp(forced, "128x256w8k64")) return launch_act<128, 256, 2, 4, 64>(p, st);
-    if (!strcmp(forced, "128x256w8k32")) return launch_act<128, 256, 2, 4, 32>(p, st);
-    if (!strcmp(forced, "32x256w4k64")) return launch_act<32, 256, 1, 4, 64>(p, st);
+  const TileCfg cfg = choose_cfg(expected_rows, g.perm != nullptr);
+  p.part = (g.part && allow_split(cfg, g, expected_rows)) ? g.part : nullptr;
+  switch (cfg) {
+    case k256x256w8k64: return launch_act<256, 256, 2, 4, 64>(p, st);
+    case k256x256w8k32: return launch_act<256, 256, 2, 4, 32>(p, st);
+    case k256x128w4k64: return launch_act<256, 128, 2, 2, 64>(p, st);
+    case k256x128w8k64: return launch_act<256, 128, 4, 2, 64>(p, st);
+    case k128x256w8k64: return launch_act<128, 256, 2, 4, 64>(p, st);
+    case k128x256w8k32: return launch_act<128, 256, 2, 4, 32>(p, st);
+    case k128x128w4k64: return launch_act<128, 128, 2, 2, 64>(p, st);
+    case k64x256w4k64: return launch_act<64, 256, 1, 4, 64>(p, st);
+    default: return launch_act<32, 256, 1, 4, 64>(p, st);
   }
-  if (expected_rows >= 192) return launch_act<256, 256, 2, 4, 64>(p, st);
-  if (expected_rows >= 48) return launch_act<128, 256, 2, 4, 64>(p, st);
-  return launch_act<32, 256, 1, 4, 64>(p, st);
 }
 
 }  // namespace moe

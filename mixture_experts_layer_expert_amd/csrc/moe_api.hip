@@ -65,11 +65,19 @@ bool use_decode(const moe_shape& s) {
   return (s.flags & MOE_FUSED_DECODE) && decode_applicable(s, expected_rows(s));
 }
 
-// Workspace of the expert stage: hidden activations H[T*k, F] for the
-// grouped-GEMM path, fp32 shard partials for the fused decode path.
+// Split-K partial tiles of the grouped GEMMs (bf16): the last, partial round
+// of tiles is cut along K when this much workspace is given.
+size_t part_bytes(const moe_shape& s) {
+  if (s.dtype != MOE_DTYPE_BF16) return 0;
+  return align_up(grouped_gemm_bf16_part_bytes(expected_rows(s)));
+}
+
+// Workspace of the expert stage: hidden activations H[T*k, F] and the
+// split-K partials for the grouped-GEMM path, fp32 shard partials for the
+// fused decode path.
 size_t ffn_ws_bytes(const moe_shape& s) {
   if (use_decode(s)) return align_up(decode_part_bytes(s));
-  return align_up((size_t)s.T * s.k * s.F * elem_size(s));
+  return align_up((size_t)s.T * s.k * s.F * elem_size(s)) + part_bytes(s);
 }
 
 // Workspace of the whole layer: y_perm[T*k, D] followed by the expert stage.
@@ -85,7 +93,8 @@ GemmAct up_act(const moe_shape& s) {
 
 // fc1 (+ activation): H[r] for every kept row r, gathered from x through perm.
 hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
-                     const void* w1, const void* b1, const void* w3, void* h, hipStream_t st) {
+                     const void* w1, const void* b1, const void* w3, void* h, float* part,
+                     hipStream_t st) {
   GroupedGemm g{};
   g.A = x;
   g.perm = perm;
@@ -100,13 +109,14 @@ hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, con
   g.K = s.D;
   g.n_out = s.F;
   g.act = up_act(s);
+  g.part = part;
   return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
                                    : launch_grouped_gemm_f32(g, st);
 }
 
 // fc2: y_perm[r] = H[r] . w2[e]^T (+ b2[e]).
 hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets, const void* w2,
-                       const void* b2, void* y_perm, hipStream_t st) {
+                       const void* b2, void* y_perm, float* part, hipStream_t st) {
   GroupedGemm g{};
   g.A = h;
   g.perm = nullptr;
@@ -121,6 +131,7 @@ hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets
   g.K = s.F;
   g.n_out = s.D;
   g.act = kActNone;
+  g.part = part;
   return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
                                    : launch_grouped_gemm_f32(g, st);
 }
@@ -133,8 +144,10 @@ int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, cons
     if (e == hipSuccess && y_perm) e = launch_reduce_shards(s, (const float*)ws, offsets, y_perm, st);
     return hip_status(e);
   }
-  hipError_t e = launch_up(s, x, perm, offsets, w1, b1, w3, ws, st);
-  if (e == hipSuccess) e = launch_down(s, ws, offsets, w2, b2, y_perm, st);
+  float* part = (float*)((unsigned char*)ws + align_up((size_t)s.T * s.k * s.F * elem_size(s)));
+  if (s.dtype != MOE_DTYPE_BF16) part = nullptr;
+  hipError_t e = launch_up(s, x, perm, offsets, w1, b1, w3, ws, part, st);
+  if (e == hipSuccess) e = launch_down(s, ws, offsets, w2, b2, y_perm, part, st);
   return hip_status(e);
 }
 
@@ -198,8 +211,20 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm, c
   return expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, (hipStream_t)stream);
 }
 
+// Split-K workspace of the stand-alone projections: NULL (never split) or
+// at least moe_workspace_bytes(shape) bytes, 256-byte aligned.
+static int split_ws(const moe_shape& s, void* ws, size_t ws_bytes, float** part) {
+  *part = nullptr;
+  if (!ws || s.dtype != MOE_DTYPE_BF16) return MOE_OK;
+  if (ws_bytes < forward_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
+  *part = (float*)ws;
+  return MOE_OK;
+}
+
 int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
-                  const void* w1, const void* b1, const void* w3, void* h, moe_stream_t stream) {
+                  const void* w1, const void* b1, const void* w3, void* h, void* ws, size_t ws_bytes,
+                  moe_stream_t stream) {
   int v = validate(shape);
   if (v != MOE_OK) return v;
   const moe_shape& s = *shape;
@@ -207,18 +232,22 @@ int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm, co
   if (!x || !perm || !offsets || !w1 || !h) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && !w3) return MOE_ERR_INVALID_ARG;
   if ((s.flags & MOE_HAS_BIAS) && !b1) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_up(s, x, perm, offsets, w1, b1, w3, h, (hipStream_t)stream));
+  float* part;
+  if ((v = split_ws(s, ws, ws_bytes, &part)) != MOE_OK) return v;
+  return hip_status(launch_up(s, x, perm, offsets, w1, b1, w3, h, part, (hipStream_t)stream));
 }
 
 int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* offsets, const void* w2,
-                    const void* b2, void* y_perm, moe_stream_t stream) {
+                    const void* b2, void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
   int v = validate(shape);
   if (v != MOE_OK) return v;
   const moe_shape& s = *shape;
   if (s.T == 0) return MOE_OK;
   if (!h || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   if ((s.flags & MOE_HAS_BIAS) && !b2) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_down(s, h, offsets, w2, b2, y_perm, (hipStream_t)stream));
+  float* part;
+  if ((v = split_ws(s, ws, ws_bytes, &part)) != MOE_OK) return v;
+  return hip_status(launch_down(s, h, offsets, w2, b2, y_perm, part, (hipStream_t)stream));
 }
 
 int moe_combine(const moe_shape* shape, const void* y_perm, const int32_t* slot, const float* topk_gate,

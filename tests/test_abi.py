@@ -74,14 +74,22 @@ def _ws(lib, s):
 
 def test_workspace_bytes_and_validation(lib):
     from mixture_experts_layer_expert_amd import _lib as L
-    # prefill-shaped (many rows per expert): y_perm[T*k, D] + H[T*k, F], bf16
+    # prefill-shaped (many rows per expert): y_perm[T*k, D] + H[T*k, F], bf16,
+    # + fp32 split-K partial tiles, one 256x256 tile per workgroup of the
+    # persistent grid (one per CU; 256 without a device)
+    grid = 256
     rc, n = _ws(lib, _shape(T=4096))
     assert rc == L.MOE_OK
-    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2
-    # decode-shaped (<= 16 rows per expert): grouped GEMM by default ...
+    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2 + grid * 256 * 256 * 4
+    # decode-shaped (<= 16 rows per expert): grouped GEMM by default (32x256
+    # tiles) ...
     rc, n = _ws(lib, _shape(T=64))
     assert rc == L.MOE_OK
-    assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2
+    assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2 + grid * 32 * 256 * 4
+    # fp32 layers never split
+    rc, n = _ws(lib, _shape(T=64, dtype=L.MOE_DTYPE_F32, act=L.MOE_ACT_GELU))
+    assert rc == L.MOE_OK
+    assert n == 64 * 2 * 128 * 4 + 64 * 2 * 256 * 4
     # ... and with the fused decode kernel y_perm + fp32 partials of the F
     # shards; 8 experts -> 32 shards wanted, reduced until F/shards is a
     # multiple of 32 -> 8 shards of 32 columns
@@ -120,12 +128,18 @@ def test_entry_points_reject_null_pointers_before_launch(lib):
                               None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
     assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, fake, fake, None, fake, fake, 16,
                               None) == L.MOE_ERR_WORKSPACE
-    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, None, fake,
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, None, fake, None, 0,
                              None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
-    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_down(s, fake, fake, fake, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, None, None, 0,
+                             None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(s, fake, fake, fake, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
     sb = ctypes.byref(_shape(act=L.MOE_ACT_GELU, flags=L.MOE_HAS_BIAS))
-    assert lib.moe_expert_down(sb, fake, fake, fake, None, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_down(sb, fake, fake, fake, None, fake, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # an optional split-K workspace that is too small, or misaligned
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, fake, 16,
+                             None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_down(s, fake, fake, fake, None, fake, ctypes.c_void_p(0x1001), 1 << 40,
+                               None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(_shape(flags=L.MOE_RESIDUAL)), fake, fake, fake, None, fake,
                            None) == L.MOE_ERR_INVALID_ARG
     args = [fake] * 16
@@ -147,8 +161,8 @@ def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
     assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None) == L.MOE_OK
     assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK
-    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, None) == L.MOE_OK
-    assert lib.moe_expert_down(s, fake, fake, fake, None, fake, None) == L.MOE_OK
+    assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, None, 0, None) == L.MOE_OK
+    assert lib.moe_expert_down(s, fake, fake, fake, None, fake, None, 0, None) == L.MOE_OK
 
 
 def test_library_has_no_undefined_internal_symbols():

@@ -267,15 +267,22 @@ def test_expert_up_down(gpu, key, scaled_cases):
     h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=gpu)
     y_ud = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
     y_ffn = torch.empty_like(y_ud)
-    api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h)
-    api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_ud)
+    # with the workspace (split-K of a partial last round allowed, as in
+    # moe_expert_ffn) and without (never split)
+    api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, buf.ws)
+    api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y_ud, buf.ws)
     api.expert_ffn(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], g["w2"], g["b2"],
                    y_ffn, buf.ws)
+    h_ns = torch.empty_like(h)
+    y_ns = torch.empty_like(y_ud)
+    api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h_ns)
+    api.expert_down(shape, h_ns, buf.offsets, g["w2"], g["b2"], y_ns)
     torch.cuda.synchronize()
     check_routing(buf, ref, cfg)
     off, perm = ref["offsets"], ref["perm"]
     K = int(off[-1])
     assert torch.equal(y_ud[:K], y_ffn[:K])
+    assert row_rel_err(y_ns[:K].float().cpu().numpy().astype(np.float64), ref["y_perm"]) <= TOL[cfg.dtype]
     # oracle hidden rows, expert by expert in grouped order
     h_ref = np.zeros((K, cfg.F))
     for e in range(cfg.N):
@@ -290,7 +297,7 @@ def test_expert_up_down(gpu, key, scaled_cases):
     h_in = torch.zeros(A, cfg.F, dtype=shape.torch_dtype)
     h_in[:K] = torch.from_numpy(h_ref).to(shape.torch_dtype)
     y2 = torch.empty_like(y_ud)
-    api.expert_down(shape, h_in.to(gpu), buf.offsets, g["w2"], g["b2"], y2)
+    api.expert_down(shape, h_in.to(gpu), buf.offsets, g["w2"], g["b2"], y2, buf.ws)
     torch.cuda.synchronize()
     y2_ref = np.zeros((K, cfg.D))
     h_in64 = h_in[:K].double().numpy()
