@@ -169,7 +169,9 @@ struct WorkList {
 
   // Prefix sum of the tiles of each expert into tile_start[0..N]; called by
   // every thread of the block (nthreads >= 64 threads, N <= 256 experts).
-  __device__ void build(const Params& p, int* tile_start, int* scan, int tid, int nthreads) {
+  // The expert offsets are copied to off[0..N] (LDS) on the way: the tile
+  // lookups inside the pipelined loop then never wait for global memory.
+  __device__ void build(const Params& p, int* tile_start, int* scan, int* off, int tid, int nthreads) {
     constexpr int kPer = kMaxExperts / 64;  // experts per thread at 64 threads
     const int N = p.n_experts;
     const int ntiles = (p.n_out + BN_OUT - 1) / BN_OUT;
@@ -179,9 +181,11 @@ struct WorkList {
       const int e = tid + u * nthreads;
       my[u] = 0;
       if (e < N) {
-        const int rows = p.offsets[e + 1] - p.offsets[e];
-        my[u] = ((rows + BM - 1) / BM) * ntiles;
+        const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
+        my[u] = ((o1 - o0 + BM - 1) / BM) * ntiles;
         scan[e] = my[u];
+        off[e] = o0;
+        if (e == N - 1) off[N] = o1;
       }
     }
     __syncthreads();
@@ -225,7 +229,7 @@ struct WorkList {
     S = __builtin_amdgcn_readfirstlane(s);
   }
 
-  __device__ TileInfo info(const Params& p, const int* tile_start, int L) const {
+  __device__ TileInfo info(const Params& p, const int* tile_start, const int* off, int L) const {
     const int N = p.n_experts;
     int lo = 0, hi = N - 1;  // expert of tile L: last e with tile_start[e] <= L
     while (lo < hi) {
@@ -234,8 +238,8 @@ struct WorkList {
     }
     TileInfo t;
     t.e = lo;
-    const int row_begin = p.offsets[lo];
-    const int rows_e = p.offsets[lo + 1] - row_begin;
+    const int row_begin = off[lo];
+    const int rows_e = off[lo + 1] - row_begin;
     const int mtiles = (rows_e + BM - 1) / BM;
     const int local = L - tile_start[lo];
     t.row0 = row_begin + (local % mtiles) * BM;
@@ -245,15 +249,48 @@ struct WorkList {
   }
 };
 
+// Stores one 32-feature block of a token row held by lanes l and l+32: lane
+// l has features {0-3, 8-11, 16-19, 24-27}, lane l+32 {4-7, 12-15, 20-23,
+// 28-31}, as packed bf16 pairs d[q][0..1] (features 8q + 4h + 0..3, h =
+// lane / 32).  One cross-half shuffle per dword gives lane l features 16t..
+// 16t+7 and lane l+32 features 16t+8..16t+15 (t = 0, 1), so each store is
+// 16 bytes per lane and 32 bytes per row.
+__device__ inline void store_block32(bf16* crow, int fbase, bool ok, const uint32_t (&d)[4][2], int lane) {
+  const bool lower = lane < 32;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t s0 = lower ? d[2 * t + 1][0] : d[2 * t][0];
+    const uint32_t s1 = lower ? d[2 * t + 1][1] : d[2 * t][1];
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32);
+    const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32);
+    uint32_t w[4];
+    if (lower) {
+      w[0] = d[2 * t][0]; w[1] = d[2 * t][1]; w[2] = r0; w[3] = r1;
+    } else {
+      w[0] = r0; w[1] = r1; w[2] = d[2 * t + 1][0]; w[3] = d[2 * t + 1][1];
+    }
+    const int f = fbase + 16 * t + (lower ? 0 : 8);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    if (ok) *(u32x4*)(crow + f) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
 // Epilogue of one output tile: acc (this wave's 32x32 sub-tiles, weight rows
 // x tokens) -> bias, activation, bf16 stores.  A lane owns token column
-// (lane & 31) of each 32x32 tile and output rows (r/4)*8 + (lane/32)*4 + r%4.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT>
+// (lane & 31) of each 32x32 tile and output rows (r/4)*8 + (lane/32)*4 + r%4;
+// rows of one token are gathered into 16-byte stores by store_block32.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
 __device__ inline void store_tile(const Params& p, const TileInfo& tc,
                                   f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][Tile<BM, BNB, WM, WN, BK>::FM],
                                   int wm, int wn, int lane) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
+  const int h4 = (lane >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < TL::FM; ++j) {
     const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
@@ -263,35 +300,44 @@ __device__ inline void store_tile(const Params& p, const TileInfo& tc,
 #pragma unroll
       for (int ip = 0; ip < TL::FN / 2; ++ip) {
         const int fbase = tc.n0 + (wn * TL::TN / 64 + ip) * 32;
+        uint32_t d[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int f = fbase + q * 8 + (lane >> 5) * 4;
-          bf16x4 v;
+          float v[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            v[u] = (bf16)(fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u]);
-          if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+            v[u] = fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u];
+          d[q][0] = pack_bf16x2(v[0], v[1]);
+          d[q][1] = pack_bf16x2(v[2], v[3]);
         }
+        store_block32(crow, fbase, live && fbase < p.n_out, d, lane);
         __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
       }
     } else {
 #pragma unroll
       for (int i = 0; i < TL::FN; ++i) {
+        const int fbase = tc.n0 + wn * TL::TN + i * 32;
+        uint32_t d[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int f = tc.n0 + wn * TL::TN + i * 32 + q * 8 + (lane >> 5) * 4;
+          const int f = fbase + q * 8 + h4;
           bf16x4 bv = {};
-          if (p.bias && f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
-          bf16x4 v;
+          // (a bias-free launch has no global load here: the compiler's wait
+          // for one would also drain the DMA already in flight)
+          if constexpr (BIAS)
+            if (f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
+          float v[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             float z = acc[i][j][q * 4 + u] + (float)bv[u];
             if constexpr (ACT == kActGelu) z = gelu_erf(z);
             if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
-            v[u] = (bf16)z;
+            v[u] = z;
           }
-          if (live && f < p.n_out) *(bf16x4*)(crow + f) = v;
+          d[q][0] = pack_bf16x2(v[0], v[1]);
+          d[q][1] = pack_bf16x2(v[2], v[3]);
         }
+        store_block32(crow, fbase, live && fbase < p.n_out, d, lane);
         __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
       }
     }
@@ -306,7 +352,7 @@ __device__ inline float* part_ptr(const Params& p, int q, int nw, int wave, int 
   return p.part + ((size_t)q * nw + wave) * (FN * FM * 16 * 64) + lane;
 }
 
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, int STAGES>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int CPR = TL::CPR, RPI = TL::RPI;
@@ -321,6 +367,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   bf16* sB = sA + STAGES * TL::kLdsA;               // [STAGES][BNB][BK]
   __shared__ int s_tile_start[kMaxExperts + 1];
   __shared__ int s_scan[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  // per wave, two slots of the perm entries of its A rows (fc1 gather): the
+  // next tile's are brought in by DMA while the current tile is loading
+  constexpr int kRowsPerWave = TL::QA * RPI;
+  static_assert(kRowsPerWave <= 64, "one dword DMA per wave");
+  __shared__ int s_perm[TL::NW][2][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
@@ -329,7 +381,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   const int KT = p.K / BK;
 
   WorkList<BM, BN_OUT> wl;
-  wl.build(p, s_tile_start, s_scan, tid, TL::THREADS);
+  wl.build(p, s_tile_start, s_scan, s_off, tid, TL::THREADS);
   const int G = gridDim.x;  // multiple of 8
   wl.split(G, KT, p.part != nullptr);
 
@@ -359,16 +411,35 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   const char* b1e = (const char*)p.B;
   const char* b2e = (const char*)p.B;
   int i_dma = 0, kt_dma = 0, k1_dma = 0, job_issued = 0;
+  // perm DMA for tile i into slot i & 1: lane l fetches the entry of tile
+  // row wave*kRowsPerWave + l (clamped to the tile's last row, so always a
+  // valid entry); only the first kRowsPerWave lanes' values are used.
+  auto fetch_perm = [&](int i) {
+    if (!p.perm || i >= n_mine) return;
+    const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
+    int r = t.row0 + wave * kRowsPerWave + (lane < kRowsPerWave ? lane : 0);
+    if (r > t.row_end - 1) r = t.row_end - 1;
+    __builtin_amdgcn_global_load_lds(p.perm + r, (lds_ptr_t)&s_perm[wave][i & 1][0], 4, 0, 0);
+  };
+  int jobs_since_fetch = 0;  // DMA jobs issued after the last perm fetch
   auto setup_dma = [&](int i) {
-    const TileInfo t = wl.info(p, s_tile_start, tile_L(i));
+    const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
+    if (p.perm) {
+      // the fetch for tile i is older than every job issued since: wait for
+      // it to land (in steady state an earlier wait already covered it)
+      wait_dma<NJ, STAGES - 1>(jobs_since_fetch);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 #pragma unroll
     for (int q = 0; q < TL::QA; ++q) {
       const int trow = (wave * TL::QA + q) * RPI + lrow;  // row within the A tile
-      int r = t.row0 + trow;
-      if (r > t.row_end - 1) r = t.row_end - 1;  // tail rows re-load a valid row
-      const int src = p.perm ? (p.perm[r] / p.topk) : r;
+      int src = t.row0 + trow;
+      if (src > t.row_end - 1) src = t.row_end - 1;  // tail rows re-load a valid row
+      if (p.perm) src = s_perm[wave][i & 1][q * RPI + lrow] / p.topk;
       offA[q] = ((uint32_t)src * (uint32_t)p.K + (uint32_t)((lchunk ^ swz<CPR>(trow)) * 8)) * 2u;
     }
+    fetch_perm(i + 1);
+    jobs_since_fetch = 0;
 #pragma unroll
     for (int q = 0; q < TL::QB; ++q) {
       const int brow = (wave * TL::QB + q) * RPI + lrow;  // row within the B tile
@@ -401,6 +472,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       dma16(base + offB[q], (lds_ptr_t)(b_dst + (wave * TL::QB + q) * 512));
     }
     ++job_issued;
+    ++jobs_since_fetch;
     if (++kt_dma == k1_dma) {
       if (++i_dma < n_mine) setup_dma(i_dma);
     }
@@ -408,7 +480,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
 
   // Prologue: fill every stage.  At the barrier of job j the stage of job j
   // is refilled with job j + STAGES, and job j + 1 must already be in flight.
-  if (n_mine > 0) setup_dma(0);
+  if (n_mine > 0) {
+    fetch_perm(0);
+    setup_dma(0);
+  }
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) issue_next();
 
@@ -466,7 +541,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   int i_cmp = 0, kt_cmp = 0, len_cmp = 0;
   TileInfo tc;
   if (n_jobs > 0) {
-    tc = wl.info(p, s_tile_start, tile_L(0));
+    tc = wl.info(p, s_tile_start, s_off, tile_L(0));
     len_cmp = tile_k1(0) - tile_k0(0);
     wait_dma<NJ, STAGES - 1>(job_issued - 1);
     ring_barrier();
@@ -493,17 +568,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     // left-over tile (always this workgroup's last): its partial sums are
     // stored after the loop
     if (++kt_cmp == len_cmp && more) {
-      store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
+      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
       kt_cmp = 0;
       ++i_cmp;
-      tc = wl.info(p, s_tile_start, tile_L(i_cmp));
+      tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
       len_cmp = tile_k1(i_cmp) - tile_k0(i_cmp);
       zero_acc();
     }
   }
   if (n_jobs > 0) {
     if (!has_rem || wl.S == 1) {
-      store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
+      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
     } else {
       float* dst = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, wave, lane);
 #pragma unroll
@@ -525,21 +600,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
 // tile r with the lane layout of the GEMM, so a lane reads back exactly the
 // accumulator elements it would have held; each chunk's 16*FN*FM values are
 // loaded together.  G: the GEMM's grid.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
 __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int BN_OUT = (ACT == kActSwiGLU) ? BNB / 2 : BNB;
   __shared__ int s_tile_start[kMaxExperts + 1];
   __shared__ int s_scan[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int wm = wave / WN, wn = wave % WN;
   WorkList<BM, BN_OUT> wl;
-  wl.build(p, s_tile_start, s_scan, lane, 64);
+  wl.build(p, s_tile_start, s_scan, s_off, lane, 64);
   wl.split(G, p.K / BK, true);
   if (wl.S == 1) return;
   for (int r = blockIdx.x; r < wl.R; r += gridDim.x) {
-    const TileInfo tc = wl.info(p, s_tile_start, wl.rounds * G + r);
+    const TileInfo tc = wl.info(p, s_tile_start, s_off, wl.rounds * G + r);
     f32x16 acc[TL::FN][TL::FM];
 #pragma unroll
     for (int i = 0; i < TL::FN; ++i)
@@ -566,15 +642,15 @@ __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] += v[i][j][e];
     }
-    store_tile<BM, BNB, WM, WN, BK, ACT>(p, tc, acc, wm, wn, lane);
+    store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
   }
 }
 
-template <int BM, int BNB, int WM, int WN, int BK, int ACT>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int S = TL::kStages;
-  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, S>;
+  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, BIAS, S>;
   // once per process and instantiation (thread-safe static initialisation)
   static const hipError_t attr_err = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::kLdsBytes);
@@ -584,18 +660,25 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
   // at most grid/2 left-over tiles are ever split (S >= 2); one wave per block
-  hipLaunchKernelGGL((splitk_finish_kernel<BM, BNB, WM, WN, BK, ACT>), dim3(grid / 2, TL::NW), dim3(64),
+  hipLaunchKernelGGL((splitk_finish_kernel<BM, BNB, WM, WN, BK, ACT, BIAS>), dim3(grid / 2, TL::NW), dim3(64),
                      0, st, p, grid);
   return hipGetLastError();
 }
 
 template <int BM, int BNB, int WM, int WN, int BK>
 hipError_t launch_act(const Params& p, hipStream_t st) {
+  const bool bias = p.bias != nullptr;
   switch (p.act) {
-    case kActGelu: return launch_cfg<BM, BNB, WM, WN, BK, kActGelu>(p, st);
-    case kActRelu: return launch_cfg<BM, BNB, WM, WN, BK, kActRelu>(p, st);
-    case kActSwiGLU: return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU>(p, st);
-    default: return launch_cfg<BM, BNB, WM, WN, BK, kActNone>(p, st);
+    case kActGelu:
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActGelu, true>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActGelu, false>(p, st);
+    case kActRelu:
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false>(p, st);
+    case kActSwiGLU: return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false>(p, st);
+    default:
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false>(p, st);
   }
 }
 
@@ -604,13 +687,10 @@ hipError_t launch_act(const Params& p, hipStream_t st) {
 namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
-enum TileCfg { k256x256w8k64, k256x256w8k32, k256x128w4k64, k256x128w8k64, k128x256w8k64,
-               k128x256w8k32, k128x128w4k64, k64x256w4k64, k32x256w4k64, kNumCfg };
-const char* const kCfgName[kNumCfg] = {"256x256w8k64", "256x256w8k32", "256x128w4k64", "256x128w8k64",
-                                       "128x256w8k64", "128x256w8k32", "128x128w4k64", "64x256w4k64",
-                                       "32x256w4k64"};
-const int kCfgBM[kNumCfg] = {256, 256, 256, 256, 128, 128, 128, 64, 32};
-const int kCfgBN[kNumCfg] = {256, 256, 128, 128, 256, 256, 128, 256, 256};
+enum TileCfg { k256x256w8k64, k128x256w8k64, k32x256w4k64, kNumCfg };
+const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "32x256w4k64"};
+const int kCfgBM[kNumCfg] = {256, 128, 32};
+const int kCfgBN[kNumCfg] = {256, 256, 256};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64),
@@ -669,13 +749,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.part = (g.part && allow_split(cfg, g, expected_rows)) ? g.part : nullptr;
   switch (cfg) {
     case k256x256w8k64: return launch_act<256, 256, 2, 4, 64>(p, st);
-    case k256x256w8k32: return launch_act<256, 256, 2, 4, 32>(p, st);
-    case k256x128w4k64: return launch_act<256, 128, 2, 2, 64>(p, st);
-    case k256x128w8k64: return launch_act<256, 128, 4, 2, 64>(p, st);
     case k128x256w8k64: return launch_act<128, 256, 2, 4, 64>(p, st);
-    case k128x256w8k32: return launch_act<128, 256, 2, 4, 32>(p, st);
-    case k128x128w4k64: return launch_act<128, 128, 2, 2, 64>(p, st);
-    case k64x256w4k64: return launch_act<64, 256, 1, 4, 64>(p, st);
     default: return launch_act<32, 256, 1, 4, 64>(p, st);
   }
 }
