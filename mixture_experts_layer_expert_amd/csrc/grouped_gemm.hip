@@ -284,10 +284,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // x tokens) -> bias, activation, bf16 stores.  A lane owns token column
 // (lane & 31) of each 32x32 tile and output rows (r/4)*8 + (lane/32)*4 + r%4;
 // rows of one token are gathered into 16-byte stores by store_block32.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
+// LDS_BIAS: bias_lds holds this wave's TN bias values of the tile (the
+// pipelined kernel); otherwise they are read from global memory.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, bool LDS_BIAS>
 __device__ inline void store_tile(const Params& p, const TileInfo& tc,
                                   f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][Tile<BM, BNB, WM, WN, BK>::FM],
-                                  int wm, int wn, int lane) {
+                                  int wm, int wn, int lane, const bf16* bias_lds) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
   const int h4 = (lane >> 5) * 4;
@@ -322,9 +324,10 @@ __device__ inline void store_tile(const Params& p, const TileInfo& tc,
         for (int q = 0; q < 4; ++q) {
           const int f = fbase + q * 8 + h4;
           bf16x4 bv = {};
-          // (a bias-free launch has no global load here: the compiler's wait
-          // for one would also drain the DMA already in flight)
-          if constexpr (BIAS)
+          // (no global load in the pipelined kernel: the compiler's wait for
+          // one would also drain the DMA already in flight)
+          if constexpr (BIAS && LDS_BIAS) bv = *(const bf16x4*)(bias_lds + i * 32 + q * 8 + h4);
+          if constexpr (BIAS && !LDS_BIAS)
             if (f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
           float v[4];
 #pragma unroll
@@ -373,6 +376,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   constexpr int kRowsPerWave = TL::QA * RPI;
   static_assert(kRowsPerWave <= 64, "one dword DMA per wave");
   __shared__ int s_perm[TL::NW][2][64];
+  // per wave, a ring of the bias values of its TN columns of a tile: filled by
+  // DMA when the tile's loads start, read by its epilogue.  The DMA side is at
+  // most STAGES jobs (so STAGES tiles) ahead, hence STAGES + 1 slots.
+  constexpr int kBiasSlots = BIAS ? STAGES + 1 : 1;
+  static_assert(!BIAS || TL::TN == 64, "bias slice of 64 columns per wave");
+  __shared__ uint32_t s_bias[BIAS ? TL::NW : 1][kBiasSlots][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
@@ -440,6 +449,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
     fetch_perm(i + 1);
     jobs_since_fetch = 0;
+    if constexpr (BIAS) {
+      // lane l fetches dword min(l, 31) of the slice; a wave past the last
+      // column keeps a valid address (its values are never used)
+      int c0 = t.n0 + wn * TL::TN;
+      if (c0 > p.n_out - TL::TN) c0 = 0;
+      const uint32_t* src = (const uint32_t*)(p.bias + (size_t)t.e * p.n_out + c0) + (lane < 32 ? lane : 31);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&s_bias[wave][i % kBiasSlots][0], 4, 0, 0);
+    }
 #pragma unroll
     for (int q = 0; q < TL::QB; ++q) {
       const int brow = (wave * TL::QB + q) * RPI + lrow;  // row within the B tile
@@ -568,7 +585,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     // left-over tile (always this workgroup's last): its partial sums are
     // stored after the loop
     if (++kt_cmp == len_cmp && more) {
-      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
+      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
+                                                       (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
       kt_cmp = 0;
       ++i_cmp;
       tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
@@ -578,7 +596,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   }
   if (n_jobs > 0) {
     if (!has_rem || wl.S == 1) {
-      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
+      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
+                                                       (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
     } else {
       float* dst = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, wave, lane);
 #pragma unroll
@@ -642,7 +661,7 @@ __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[i][j][e] += v[i][j][e];
     }
-    store_tile<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc, wm, wn, lane);
+    store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, false>(p, tc, acc, wm, wn, lane, nullptr);
   }
 }
 
