@@ -52,17 +52,29 @@ CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128}
 PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
                       "mixture_experts_layer_expert_amd/csrc/moe_internal.h")
 PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
-    "c2": {"sources": "4873c62f5708d0bb",
-           "fc1": {"fetch_kib": 309387.8, "write_kib": 91944.4},  # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 3>
-           "fc2": {"fetch_kib": 344501.1, "write_kib": 22946.7},  # grouped_gemm_kernel<128, 256, 2, 4, 64, 0, 3>
+    "c2": {"sources": "71a869a347bd3511",
+           "fc1": {"fetch_kib": 309436.7, "write_kib": 91818.5},
+           # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 0, 3>
+           "fc2": {"fetch_kib": 389921.7, "write_kib": 55726.7},
+           # grouped_gemm_kernel<128, 256, 2, 4, 64, 0, 0, 3> + splitk_finish_kernel<128, 256, 2, 4, 64, 0, 0>
            },
-    "c4": {"sources": "4873c62f5708d0bb",
-           "fc1": {"fetch_kib": 3021457.9, "write_kib": 460131.2},  # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 2>
-           "fc2": {"fetch_kib": 1716290.7, "write_kib": 150362.4},  # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 2>
+    "c4": {"sources": "71a869a347bd3511",
+           "fc1": {"fetch_kib": 3149833.8, "write_kib": 458910.8},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2>
+           "fc2": {"fetch_kib": 1646148.6, "write_kib": 199651.2},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
-    "c5": {"sources": "4873c62f5708d0bb",
-           "fc1": {"fetch_kib": 362303.8, "write_kib": 2112.4},  # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 4>
-           "fc2": {"fetch_kib": 181390.8, "write_kib": 3072.0},  # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 4>
+    "c5": {"sources": "71a869a347bd3511",
+           "fc1": {"fetch_kib": 363845.5, "write_kib": 2116.0},
+           # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 0, 4>
+           "fc2": {"fetch_kib": 181437.6, "write_kib": 3072.1},
+           # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 0, 4>
+           },
+    "c3": {"sources": "71a869a347bd3511",
+           "fc1": {"fetch_kib": 251129.0, "write_kib": 143179.3},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 1, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 1, 1>
+           "fc2": {"fetch_kib": 299485.6, "write_kib": 89850.4},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 1>
            },
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
@@ -328,7 +340,8 @@ def main():
         "roofline": {
             "kernel": f"grouped_gemm_kernel, {launch} launch "
                       f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "
-                      f"moe_expert_{'up' if launch == 'fc1' else 'down'})",
+                      f"moe_expert_{'up' if launch == 'fc1' else 'down'}; with the split-K "
+                      f"finishing kernel when its last round of tiles is split)",
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak,
             "traffic": measured_traffic(args.workload, launch) if args.cf is None else None,
