@@ -380,7 +380,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   // DMA when the tile's loads start, read by its epilogue.  The DMA side is at
   // most STAGES jobs (so STAGES tiles) ahead, hence STAGES + 1 slots.
   constexpr int kBiasSlots = BIAS ? STAGES + 1 : 1;
-  static_assert(!BIAS || TL::TN == 64, "bias slice of 64 columns per wave");
+  static_assert(!BIAS || TL::TN <= 128, "bias slice of at most 128 columns per wave");
   __shared__ uint32_t s_bias[BIAS ? TL::NW : 1][kBiasSlots][64];
 
   const int tid = threadIdx.x;
@@ -450,11 +450,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     fetch_perm(i + 1);
     jobs_since_fetch = 0;
     if constexpr (BIAS) {
-      // lane l fetches dword min(l, 31) of the slice; a wave past the last
-      // column keeps a valid address (its values are never used)
+      // lane l fetches dword min(l, TN/2 - 1) of the slice; a wave past the
+      // last column keeps a valid address (its values are never used)
       int c0 = t.n0 + wn * TL::TN;
       if (c0 > p.n_out - TL::TN) c0 = 0;
-      const uint32_t* src = (const uint32_t*)(p.bias + (size_t)t.e * p.n_out + c0) + (lane < 32 ? lane : 31);
+      const uint32_t* src =
+          (const uint32_t*)(p.bias + (size_t)t.e * p.n_out + c0) + (lane < TL::TN / 2 ? lane : TL::TN / 2 - 1);
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&s_bias[wave][i % kBiasSlots][0], 4, 0, 0);
     }
 #pragma unroll
