@@ -22,6 +22,7 @@ the host on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -87,6 +88,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c1..c5 (default: c2, the Switch-style layer)")
     ap.add_argument("--cf", type=float, default=None, help="capacity factor override (<0: none)")
+    ap.add_argument("--priority", choices=("token", "choice"), default="token",
+                    help="capacity priority: token order, or (choice, token) (MOE_SLOT_MAJOR)")
     ap.add_argument("--copies", type=int, default=3,
                     help="copies of x and the weights cycled over consecutive steps")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay")
@@ -213,7 +216,7 @@ def main():
     # copy 0 is the generated tensors; the others are device clones (same
     # values, different addresses)
     gs = [g0] + [{k: (None if v is None else v.clone()) for k, v in g0.items()} for _ in range(R - 1)]
-    shape = api.MoeShape.from_config(cfg)
+    shape = dataclasses.replace(api.MoeShape.from_config(cfg), slot_major=args.priority == "choice")
     buf = api.MoeBuffers(shape, device=dev)
     A = cfg.T * cfg.k
     h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=dev)
@@ -330,7 +333,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "D": cfg.D, "F": cfg.F, "experts": cfg.N,
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
                    "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
-                   "input_copies": R},
+                   "capacity_priority": args.priority, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stages,
@@ -344,7 +347,8 @@ def main():
                       f"finishing kernel when its last round of tiles is split)",
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak,
-            "traffic": measured_traffic(args.workload, launch) if args.cf is None else None,
+            "traffic": (measured_traffic(args.workload, launch)
+                        if args.cf is None and args.priority == "token" else None),
             "launch_ms": stages[launch],
             "algorithmic": {"flops": flops, "bytes": bytes_,
                             "rule": "used experts' weights once + activation rows in once + "

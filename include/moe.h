@@ -79,7 +79,12 @@ enum moe_flags {
    * weights into registers and writes fp32 shard partials, instead of the
    * two grouped-GEMM launches.  Same results within the bf16 tolerance;
    * ignored where it does not apply.  Off by default (slower on MI355X). */
-  MOE_FUSED_DECODE = 16u
+  MOE_FUSED_DECODE = 16u,
+  /* Capacity priority by choice: each expert keeps its assignments in the
+   * order (choice j, token t), so every token's first choice is kept before
+   * any second choice (the GShard top-2 pattern named among the notebook's
+   * references); without it the order is the flat index t*k+j. */
+  MOE_SLOT_MAJOR = 32u
 };
 
 typedef struct moe_shape {
@@ -118,8 +123,8 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
 
 /* Dispatch ("Dispatch and gather", "Capacity factor"): counts[e] = number of
  * assignments to expert e (before the capacity cut).  The assignments of
- * expert e are ranked in increasing flat index; the first min(counts[e],
- * capacity) are kept.  offsets[N+1] is the exclusive scan of the kept counts,
+ * expert e are ranked in increasing flat index (with MOE_SLOT_MAJOR: in
+ * increasing (j, t)); the first min(counts[e], capacity) are kept.  offsets[N+1] is the exclusive scan of the kept counts,
  * perm[offsets[e] .. offsets[e+1]) lists expert e's kept assignments in rank
  * order, slot[a] is the row of assignment a in that grouped order or -1 if it
  * was dropped, and *n_dropped = T*k - offsets[N].  perm must hold T*k

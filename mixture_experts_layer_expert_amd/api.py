@@ -41,6 +41,7 @@ class MoeShape:
     has_bias: bool = False
     router_bias: bool = False
     fused_decode: bool = False  # MOE_FUSED_DECODE algorithm choice
+    slot_major: bool = False    # MOE_SLOT_MAJOR capacity priority (choice, token)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -50,7 +51,8 @@ class MoeShape:
         flags = ((L.MOE_RENORM if self.renorm else 0) | (L.MOE_RESIDUAL if self.residual else 0)
                  | (L.MOE_HAS_BIAS if self.has_bias else 0)
                  | (L.MOE_ROUTER_BIAS if self.router_bias else 0)
-                 | (L.MOE_FUSED_DECODE if self.fused_decode else 0))
+                 | (L.MOE_FUSED_DECODE if self.fused_decode else 0)
+                 | (L.MOE_SLOT_MAJOR if self.slot_major else 0))
         return L.MoeShapeC(self.T, self.D, self.F, self.N, self.k, self.capacity,
                            _DT[self.dtype][0], _ACT[self.act], flags)
 

@@ -4,10 +4,11 @@
 // expert is trick 2 of "MoE Parallelism for Inference: Tricks and PyTorch
 // Deep Dive").
 //
-// One workgroup of 1024 threads (16 waves).  The T*k assignments are split
-// into 16 contiguous segments, one per wave, so that the result is the
-// stable order (segments, 64-wide chunks inside a segment and lanes inside
-// a chunk all follow increasing flat index a = t*k + j):
+// One workgroup of 1024 threads (16 waves).  The T*k assignments, taken in
+// priority order i (i = a = t*k + j by token, or i = j*T + t by choice, the
+// GShard order), are split into 16 contiguous segments, one per wave, so
+// that the result is the stable order (segments, 64-wide chunks inside a
+// segment and lanes inside a chunk all follow increasing i):
 //  A. each wave walks its segment chunk by chunk; the lanes holding the same
 //     expert are found with one ballot per bit of the expert id, a lane's
 //     rank inside its wave is the wave's running count of that expert plus
@@ -29,8 +30,16 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPrefetch = 8;  // chunks whose ids are loaded ahead
 
+// Flat index a = t*k + j of the i-th assignment in priority order.
+__device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
+  if (!by_choice) return i;
+  const int64_t j = i / T;
+  return (i - j * T) * k + j;
+}
+
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
-                                                            int64_t A, int N, int C,
+                                                            int64_t A, int64_t T, int k, int by_choice,
+                                                            int N, int C,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
@@ -59,14 +68,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     int ev[kPrefetch];
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t a = b0 + c * kWave + lane;
-      ev[c] = (a < a_end) ? idx[a] : -1;
+      const int64_t i = b0 + c * kWave + lane;
+      ev[c] = (i < a_end) ? idx[flat_of(i, T, k, by_choice)] : -1;
     }
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t a = b0 + c * kWave + lane;
+      const int64_t i = b0 + c * kWave + lane;
+      const int64_t a = flat_of(i, T, k, by_choice);
       const int e = ev[c];
-      const bool valid = a < a_end && e >= 0 && e < N;
+      const bool valid = i < a_end && e >= 0 && e < N;
       uint64_t same = __ballot(valid);
       for (int b = 0; b < bits; ++b) {
         const bool bit = valid && ((e >> b) & 1);
@@ -121,14 +131,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     int ev[kPrefetch], rv[kPrefetch];
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t a = b0 + c * kWave + lane;
-      ev[c] = (a < a_end) ? idx[a] : -1;
-      rv[c] = (a < a_end) ? slot[a] : 0;
+      const int64_t i = b0 + c * kWave + lane;
+      const int64_t a = flat_of(i, T, k, by_choice);
+      ev[c] = (i < a_end) ? idx[a] : -1;
+      rv[c] = (i < a_end) ? slot[a] : 0;
     }
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t a = b0 + c * kWave + lane;
-      if (a >= a_end) continue;
+      const int64_t i = b0 + c * kWave + lane;
+      const int64_t a = flat_of(i, T, k, by_choice);
+      if (i >= a_end) continue;
       const int e = ev[c];
       if (e < 0 || e >= N) {
         slot[a] = -1;
@@ -152,8 +164,9 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
                            int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                            hipStream_t st) {
   const int64_t A = s.T * (int64_t)s.k;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, st, idx, A, s.N, s.capacity,
-                     counts, offsets, perm, slot, n_dropped);
+  const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
+                     s.capacity, counts, offsets, perm, slot, n_dropped);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ int validate(const moe_shape* sp) {
   if (s.k > s.N || s.capacity < -1) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.act != MOE_ACT_GELU && s.act != MOE_ACT_RELU && s.act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  const uint32_t known = MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE;
+  const uint32_t known =
+      MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE | MOE_SLOT_MAJOR;
   if (s.flags & ~known) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && (s.flags & MOE_HAS_BIAS)) return MOE_ERR_UNSUPPORTED;
   if (s.N > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;

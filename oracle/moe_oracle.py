@@ -139,23 +139,40 @@ def capacity(T: int, k: int, N: int, cf: Optional[float]) -> Optional[int]:
     return int(T * k / N * cf)
 
 
-def dispatch(idx: np.ndarray, N: int, C: Optional[int]) -> dict:
+def dispatch(idx: np.ndarray, N: int, C: Optional[int], priority: str = "token") -> dict:
     """Group assignments by expert, keep the first C of each.
 
-    Assignment a = t*k + j.  For expert e its assignments are listed in
-    ascending a; the first min(count_e, C) are kept.  ``perm`` lists the
-    kept assignments expert by expert, ``offsets`` delimits each expert's
-    rows, ``slot[a]`` is the row of assignment a or -1 when dropped.
+    Assignment a = t*k + j (token t, choice j).  For expert e its assignments
+    are listed in priority order and the first min(count_e, C) are kept:
+    ``priority="token"`` orders them by ascending a (token order, the reading
+    used for the notebook's capacity cut); ``priority="choice"`` orders them
+    by (j, t), i.e. every token's first choice before any second choice (the
+    GShard top-2 pattern named in the notebook's references).  ``perm`` lists
+    the kept assignments (as flat indices a) expert by expert in that order,
+    ``offsets`` delimits each expert's rows, ``slot[a]`` is the row of
+    assignment a or -1 when dropped.
     """
-    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    idx = np.asarray(idx, dtype=np.int64)
+    if idx.ndim == 1:
+        idx = idx[:, None]
+    T, k = idx.shape
+    flat = idx.reshape(-1)
     A = flat.size
+    a_all = np.arange(A)
+    if priority == "token":
+        key = a_all
+    elif priority == "choice":
+        key = (a_all % k) * T + a_all // k  # j*T + t
+    else:
+        raise ValueError(f"unknown priority {priority!r}")
     counts = expert_counts(flat, N)
     slot = np.full(A, -1, dtype=np.int64)
     offsets = np.zeros(N + 1, dtype=np.int64)
     perm_parts = []
     row = 0
     for e in range(N):
-        mine = np.nonzero(flat == e)[0]  # ascending flat index
+        mine = np.nonzero(flat == e)[0]
+        mine = mine[np.argsort(key[mine], kind="stable")]  # priority order
         kept = mine if C is None else mine[:C]
         slot[kept] = row + np.arange(kept.size)
         perm_parts.append(kept)
@@ -313,15 +330,16 @@ def combine_rows(y_perm, slot, gate, k: int, x=None) -> np.ndarray:
 
 def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                 capacity_slots: Optional[int] = None, residual: bool = False,
-                tokens: Optional[Sequence[int]] = None) -> dict:
+                tokens: Optional[Sequence[int]] = None, priority: str = "token") -> dict:
     """Whole layer: route, dispatch with capacity, experts, combine.
 
     ``params`` holds w_router, b_router, w1, b1, w3, w2, b2 (numpy arrays or
-    CPU tensors in the C-ABI layouts; absent entries are None).
+    CPU tensors in the C-ABI layouts; absent entries are None).  ``priority``
+    is the capacity order of ``dispatch``.
     """
     r = route(x, params["w_router"], params.get("b_router"), k, renorm)
     N = r["logits"].shape[1]
-    d = dispatch(r["idx"], N, capacity_slots)
+    d = dispatch(r["idx"], N, capacity_slots, priority)
     c = combine_from_experts(x, params, act, k, r["gate"], d, residual, tokens)
     out = dict(r)
     out.update(d)
@@ -330,13 +348,15 @@ def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
 
 
 def brute_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
-                  capacity_slots: Optional[int] = None, residual: bool = False) -> np.ndarray:
+                  capacity_slots: Optional[int] = None, residual: bool = False,
+                  priority: str = "token") -> np.ndarray:
     """Second formulation for tiny inputs: every expert on every token.
 
     Builds the sparse gate matrix G[t, e] (the gate of each kept assignment,
     zero elsewhere) and contracts it with the dense stack of all experts'
     outputs.  Kept assignments are found by counting, for each (t, j), the
-    earlier assignments to the same expert (O(A^2)).
+    assignments to the same expert that come before it in the priority order
+    (O(A^2)): earlier flat index (token order) or earlier (choice, token).
     """
     X = f64(x)
     T = X.shape[0]
@@ -356,7 +376,12 @@ def brute_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
     flat = idx.reshape(-1)
     G = np.zeros((T, N))
     for a in range(flat.size):
-        rank = int((flat[:a] == flat[a]).sum())
+        t, j = divmod(a, k)
+        if priority == "token":
+            rank = int((flat[:a] == flat[a]).sum())
+        else:
+            rank = sum(1 for b in range(flat.size)
+                       if flat[b] == flat[a] and (b % k, b // k) < (j, t))
         if capacity_slots is None or rank < capacity_slots:
             G[a // k, flat[a]] += g[a // k, a % k]
     Yall = np.stack([expert_mlp(X, act, **_expert_params(params, e)) for e in range(N)])

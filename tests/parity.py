@@ -4,6 +4,8 @@ Inputs come from ``workloads``; expected values come from ``oracle`` only.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -30,9 +32,10 @@ def capacity_of(cfg):
     return oracle.capacity(cfg.T, cfg.k, cfg.N, cfg.cf)
 
 
-def oracle_layer(cfg, inp, tokens=None) -> dict:
+def oracle_layer(cfg, inp, tokens=None, priority="token") -> dict:
     return oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, renorm=cfg.renorm,
-                              capacity_slots=capacity_of(cfg), residual=cfg.residual, tokens=tokens)
+                              capacity_slots=capacity_of(cfg), residual=cfg.residual, tokens=tokens,
+                              priority=priority)
 
 
 def row_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
@@ -74,8 +77,8 @@ def check_outputs(y_gpu: np.ndarray, ref: dict, cfg, x_rows: np.ndarray, tokens=
     return err
 
 
-def run_forward(cfg, g: dict, T=None, fused_decode=False) -> api.MoeBuffers:
-    shape = api.MoeShape.from_config(cfg, T, fused_decode)
+def run_forward(cfg, g: dict, T=None, fused_decode=False, slot_major=False) -> api.MoeBuffers:
+    shape = dataclasses.replace(api.MoeShape.from_config(cfg, T, fused_decode), slot_major=slot_major)
     buf = api.MoeBuffers(shape)
     buf.forward(g["x"], g)
     torch.cuda.synchronize()

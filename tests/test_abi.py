@@ -102,7 +102,7 @@ def test_workspace_bytes_and_validation(lib):
         (dict(T=-1), L.MOE_ERR_INVALID_ARG), (dict(capacity=-2), L.MOE_ERR_INVALID_ARG),
         (dict(dtype=7), L.MOE_ERR_INVALID_ARG), (dict(act=5), L.MOE_ERR_INVALID_ARG),
         (dict(flags=1 << 7), L.MOE_ERR_INVALID_ARG), (dict(D=100), L.MOE_ERR_UNSUPPORTED),
-        (dict(flags=1 << 5), L.MOE_ERR_INVALID_ARG),
+        (dict(flags=1 << 6), L.MOE_ERR_INVALID_ARG),
         (dict(F=96), L.MOE_ERR_UNSUPPORTED), (dict(flags=L.MOE_HAS_BIAS), L.MOE_ERR_UNSUPPORTED),
         (dict(T=2**31, D=4096), L.MOE_ERR_UNSUPPORTED),
     ]

@@ -96,9 +96,10 @@ def test_route_shapes(gpu, N, k):
 
 
 # ------------------------------------------------------------- dispatch
-def _dispatch_case(gpu, idx_np, N, C):
+def _dispatch_case(gpu, idx_np, N, C, priority="token"):
     T, k = idx_np.shape
-    shape = api.MoeShape(T=T, D=64, F=64, N=N, k=k, capacity=-1 if C is None else C, act="relu")
+    shape = api.MoeShape(T=T, D=64, F=64, N=N, k=k, capacity=-1 if C is None else C, act="relu",
+                         slot_major=(priority == "choice"))
     i32 = dict(dtype=torch.int32, device=gpu)
     idx = torch.from_numpy(idx_np.astype(np.int32)).to(gpu)
     counts = torch.full((N,), -7, **i32)
@@ -108,7 +109,7 @@ def _dispatch_case(gpu, idx_np, N, C):
     nd = torch.full((1,), -7, **i32)
     api.dispatch(shape, idx, counts, offsets, perm, slot, nd)
     torch.cuda.synchronize()
-    ref = oracle.dispatch(idx_np, N, C)
+    ref = oracle.dispatch(idx_np, N, C, priority)
     assert np.array_equal(counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
     K = int(ref["offsets"][-1])
@@ -153,6 +154,18 @@ def test_dispatch_adversarial(gpu):
     bad[::11, 1] = 8
     _dispatch_case(gpu, bad, 8, None)
     _dispatch_case(gpu, bad, 8, 120)
+
+
+@pytest.mark.parametrize("T,N,k,C", [
+    (1, 4, 4, None), (777, 8, 2, 150), (3001, 16, 2, 1), (5000, 64, 6, 60), (2000, 128, 1, 15),
+    (4096, 16, 2, 300), (40000, 256, 2, 300), (999, 6, 6, 500),
+])
+def test_dispatch_choice_priority(gpu, T, N, k, C):
+    """MOE_SLOT_MAJOR: each expert keeps assignments in (choice, token) order."""
+    rng = np.random.default_rng(3 * T + N + k)
+    _dispatch_case(gpu, _rand_idx(rng, T, N, k), N, C, "choice")
+    p = 1.0 / np.arange(1, N + 1) ** 1.2
+    _dispatch_case(gpu, _rand_idx(rng, T, N, k, p / p.sum()), N, C, "choice")
 
 
 # ----------------------------------------------- scaled layers, every token
@@ -307,6 +320,22 @@ def test_expert_up_down(gpu, key, scaled_cases):
             y2_ref[r0:r1] = oracle.expert_output(h_in64[r0:r1], inp["w2"][e],
                                                  None if inp.get("b2") is None else inp["b2"][e])
     assert row_rel_err(y2[:K].float().cpu().numpy().astype(np.float64), y2_ref) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("key,T", [("c3", 1500), ("c5", None), ("c1", None)])
+def test_forward_choice_priority(gpu, key, T):
+    """Whole layer with MOE_SLOT_MAJOR and a capacity that drops: routing
+    bit-exact and outputs within tolerance of the oracle's choice order."""
+    base = get_config(key, cf=1.0)
+    cfg = base if T is None else scaled_config(base, T=T)
+    _say(f"forward choice priority {cfg.name}: T={cfg.T} k={cfg.k} cf={cfg.cf}")
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp, priority="choice")
+    assert ref["n_dropped"] > 0
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g, slot_major=True)
+    check_routing(buf, ref, cfg)
+    check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
 
 
 # ------------------------------------------ full-size layers, sampled rows

@@ -121,3 +121,84 @@ def test_imbalance_and_aux_loss_closed_forms():
     probs2 = np.zeros((T, N))
     probs2[:, :2] = 0.5
     assert oracle.switch_aux_loss(idx2, probs2, N) == pytest.approx(N, abs=1e-12)
+
+
+# --------------------------------------------- choice-major (GShard) priority
+def test_choice_priority_hand_example():
+    # 4 tokens, top-2, 3 experts, capacity 2.  Expert 0 receives (t0,j0),
+    # (t1,j1), (t2,j0), (t3,j1): token order keeps t0,t1; choice order keeps
+    # the first choices t0,t2.
+    idx = np.array([[0, 1], [2, 0], [0, 2], [1, 0]])
+    d = oracle.dispatch(idx, 3, 2, priority="choice")
+    assert d["counts"].tolist() == [4, 2, 2]
+    assert d["offsets"].tolist() == [0, 2, 4, 6]
+    # expert 0: a=0 (t0,j0), a=4 (t2,j0); expert 1: a=6 (t3,j0), a=1 (t0,j1);
+    # expert 2: a=2 (t1,j0), a=5 (t2,j1)
+    assert d["perm"].tolist() == [0, 4, 6, 1, 2, 5]
+    assert d["slot"].tolist() == [0, 3, 4, -1, 1, 5, 2, -1]
+    assert d["n_dropped"] == 2
+    dt = oracle.dispatch(idx, 3, 2, priority="token")
+    assert dt["perm"].tolist()[:2] == [0, 3]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_choice_priority_against_lexsort_and_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(2, 10))
+    k = int(rng.integers(1, min(N, 4) + 1))
+    T = int(rng.integers(1, 120))
+    idx = _random_idx(rng, T, N, k)
+    C = int(rng.integers(0, T))
+    d = oracle.dispatch(idx, N, C, priority="choice")
+    flat = idx.reshape(-1)
+    a = np.arange(flat.size)
+    # library: sort by (expert, choice, token); keep each expert's first C
+    order = np.lexsort((a // k, a % k, flat))
+    want = []
+    for e in range(N):
+        mine = [x for x in order if flat[x] == e]
+        want += mine[:C]
+    assert d["perm"].tolist() == want
+    # brute force rank of every assignment
+    for x in range(flat.size):
+        t, j = divmod(x, k)
+        rank = sum(1 for y in range(flat.size) if flat[y] == flat[x] and (y % k, y // k) < (j, t))
+        assert (d["slot"][x] >= 0) == (rank < C)
+    # k = 1: choice order is token order
+    i1 = idx[:, :1]
+    d1c, d1t = oracle.dispatch(i1, N, C, "choice"), oracle.dispatch(i1, N, C, "token")
+    for key in ("counts", "offsets", "perm", "slot"):
+        assert np.array_equal(d1c[key], d1t[key])
+
+
+def test_choice_priority_keeps_first_choices_first():
+    # GShard guarantee: an expert never keeps a second choice while it drops a
+    # first choice; under token order it can
+    rng = np.random.default_rng(7)
+    T, N, k = 400, 6, 2
+    p = np.array([0.5, 0.2, 0.1, 0.1, 0.05, 0.05])
+    idx = np.stack([rng.choice(N, size=k, replace=False, p=p) for _ in range(T)])
+    C = oracle.capacity(T, k, N, 1.0)
+    d = oracle.dispatch(idx, N, C, priority="choice")
+    flat = idx.reshape(-1)
+    for e in range(N):
+        mine = np.nonzero(flat == e)[0]
+        j_kept = mine[d["slot"][mine] >= 0] % k
+        j_drop = mine[d["slot"][mine] < 0] % k
+        if j_drop.size and j_kept.size:
+            assert j_drop.min() >= j_kept.max()
+    # more first choices survive than under token order
+    dt = oracle.dispatch(idx, N, C, priority="token")
+    first = np.arange(T) * k
+    assert (d["slot"][first] >= 0).sum() > (dt["slot"][first] >= 0).sum()
+
+
+def test_choice_priority_layer_matches_brute_force():
+    from workloads import generate, get_config, scaled_config
+    cfg = scaled_config(get_config("c1"), T=48, D=32, F=64, N=4, k=2)
+    inp = generate(cfg)
+    C = oracle.capacity(cfg.T, cfg.k, cfg.N, 0.75)
+    ref = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, priority="choice")
+    y_b = oracle.brute_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, priority="choice")
+    assert np.allclose(ref["y"], y_b, rtol=1e-12, atol=1e-12)
+    assert ref["n_dropped"] > 0
