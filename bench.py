@@ -41,7 +41,7 @@ METRIC = "MoE layer fwd tokens/s + TFLOP/s (% bf16 MFMA peak) or GB/s (% HBM pea
 # CPU-baseline sample (tokens) per workload: the oracle in fp64 on the host's
 # cores for roughly 5-30 s.  The sample is the first T_s tokens of the same
 # batch, with the capacity recomputed for T_s tokens.
-CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128}
+CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, "c6": 512}
 
 
 # HBM traffic of the dominant launch, from two rocprofv3 --pmc runs of the
@@ -219,8 +219,8 @@ def main():
     shape = dataclasses.replace(api.MoeShape.from_config(cfg), slot_major=args.priority == "choice")
     buf = api.MoeBuffers(shape, device=dev)
     A = cfg.T * cfg.k
-    h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=dev)
-    y_perm = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=dev)
+    h = torch.empty(shape.group_rows, cfg.F, dtype=shape.torch_dtype, device=dev)
+    y_perm = torch.empty(shape.group_rows, cfg.D, dtype=shape.torch_dtype, device=dev)
     st = torch.cuda.current_stream()
 
     def step(g, s, ev=None):

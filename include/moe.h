@@ -97,7 +97,21 @@ typedef struct moe_shape {
   int32_t dtype;    /* enum moe_dtype */
   int32_t act;      /* enum moe_act */
   uint32_t flags;   /* enum moe_flags, or-ed */
+  int32_t n_shared; /* always-on experts S (0 = none), see below */
 } moe_shape;
+
+/* Shared (always-on) experts, the notebook's "Exercises" section (a few
+ * experts every token goes through, next to the routed ones): with
+ * n_shared = S > 0 the expert stacks w1/w3/w2/b1/b2 hold S + N experts, the
+ * S shared ones first (slots 0..S-1) and routed expert e in slot S + e; the
+ * router (w_router [N, D]) ranks the routed experts only, topk_idx stays in
+ * [0, N).  Every token goes to every shared expert with gate 1, uncapped.
+ * The grouped rows then hold the shared rows first: row s*T + t is token t
+ * of shared expert s (perm = t*k there), then the routed rows, so offsets
+ * has S + N + 1 entries (offsets[s] = s*T for s <= S), routed slots are
+ * shifted by S*T, perm and the row buffers (y_perm, the hidden rows) hold
+ * S*T + T*k rows, and the combine adds the shared rows with gate 1.  counts
+ * and n_dropped stay those of the N routed experts. */
 
 /* Per-expert slot budget of the notebook's "Capacity factor" section:
  * int(T*k/N * cf), evaluated left to right in double and truncated.
@@ -124,20 +138,24 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
 /* Dispatch ("Dispatch and gather", "Capacity factor"): counts[e] = number of
  * assignments to expert e (before the capacity cut).  The assignments of
  * expert e are ranked in increasing flat index (with MOE_SLOT_MAJOR: in
- * increasing (j, t)); the first min(counts[e], capacity) are kept.  offsets[N+1] is the exclusive scan of the kept counts,
- * perm[offsets[e] .. offsets[e+1]) lists expert e's kept assignments in rank
- * order, slot[a] is the row of assignment a in that grouped order or -1 if it
- * was dropped, and *n_dropped = T*k - offsets[N].  perm must hold T*k
- * entries; entries past offsets[N] are left untouched.  Expert ids outside
- * [0, N) are treated as dropped and not counted.  Bit-exact, deterministic. */
+ * increasing (j, t)); the first min(counts[e], capacity) are kept.
+ * offsets[N+1] is the exclusive scan of the kept counts, perm[offsets[e] ..
+ * offsets[e+1]) lists expert e's kept assignments in rank order, slot[a] is
+ * the row of assignment a in that grouped order or -1 if it was dropped,
+ * and *n_dropped = T*k - offsets[N].  perm must hold T*k entries; entries
+ * past offsets[N] are left untouched.  With n_shared = S the S shared groups
+ * come first (offsets[S+N+1], perm of S*T + T*k entries, routed rows and
+ * slots shifted by S*T; see moe_shape).  Expert ids outside [0, N) are
+ * treated as dropped and not counted.  Bit-exact, deterministic. */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                  moe_stream_t stream);
 
 /* Expert MLPs on the grouped rows: for every expert e and every row r in
  * [offsets[e], offsets[e+1]), token t = perm[r] / k,
- *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [T*k, D])
- * Rows past offsets[N] are left untouched.  One launch per layer (fc1+act)
+ *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [T*k, D];
+ *                                        [S*T + T*k, D] with S shared experts)
+ * Rows past the last offset are left untouched.  One launch per layer (fc1+act)
  * and one for fc2, each a persistent grouped GEMM whose work list covers
  * column shards of w1/w3 and row shards of w2 for all experts at once (the
  * row/column expert decomposition of "Accelerating MoE Model Inference with

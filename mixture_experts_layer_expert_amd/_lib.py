@@ -43,6 +43,7 @@ class MoeShapeC(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("act", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("n_shared", ctypes.c_int32),
     ]
 
 

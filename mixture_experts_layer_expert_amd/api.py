@@ -42,10 +42,16 @@ class MoeShape:
     router_bias: bool = False
     fused_decode: bool = False  # MOE_FUSED_DECODE algorithm choice
     slot_major: bool = False    # MOE_SLOT_MAJOR capacity priority (choice, token)
+    n_shared: int = 0           # always-on experts (expert slots 0..n_shared-1)
 
     @property
     def torch_dtype(self) -> torch.dtype:
         return _DT[self.dtype][1]
+
+    @property
+    def group_rows(self) -> int:
+        """Rows of the grouped buffers (perm, y_perm, hidden rows)."""
+        return self.T * (self.k + self.n_shared)
 
     def c(self) -> L.MoeShapeC:
         flags = ((L.MOE_RENORM if self.renorm else 0) | (L.MOE_RESIDUAL if self.residual else 0)
@@ -54,7 +60,7 @@ class MoeShape:
                  | (L.MOE_FUSED_DECODE if self.fused_decode else 0)
                  | (L.MOE_SLOT_MAJOR if self.slot_major else 0))
         return L.MoeShapeC(self.T, self.D, self.F, self.N, self.k, self.capacity,
-                           _DT[self.dtype][0], _ACT[self.act], flags)
+                           _DT[self.dtype][0], _ACT[self.act], flags, self.n_shared)
 
     @staticmethod
     def from_config(cfg, T: Optional[int] = None, fused_decode: bool = False) -> "MoeShape":
@@ -63,7 +69,7 @@ class MoeShape:
         return MoeShape(T=T, D=cfg.D, F=cfg.F, N=cfg.N, k=cfg.k, capacity=cap, dtype=cfg.dtype,
                         act=cfg.act, renorm=cfg.renorm, residual=cfg.residual,
                         has_bias=cfg.expert_bias, router_bias=cfg.router_bias is not None,
-                        fused_decode=fused_decode)
+                        fused_decode=fused_decode, n_shared=getattr(cfg, "n_shared", 0))
 
 
 def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "") -> Optional[int]:
@@ -195,8 +201,8 @@ class MoeBuffers:
         self.topk_idx = torch.empty(shape.T, shape.k, **i32)
         self.topk_gate = torch.empty(shape.T, shape.k, dtype=torch.float32, device=device)
         self.counts = torch.empty(shape.N, **i32)
-        self.offsets = torch.empty(shape.N + 1, **i32)
-        self.perm = torch.empty(max(A, 1), **i32)
+        self.offsets = torch.empty(shape.n_shared + shape.N + 1, **i32)
+        self.perm = torch.empty(max(shape.group_rows, 1), **i32)
         self.slot = torch.empty(max(A, 1), **i32)
         self.n_dropped = torch.empty(1, **i32)
         self.ws = torch.empty(max(workspace_bytes(shape), 256), dtype=torch.uint8, device=device)

@@ -2,7 +2,8 @@
 // token order ("Dispatch and gather" section of the notebook
 // "Mixture-of-experts and expert parallelism": the output starts at zero and
 // receives every chosen expert's output scaled by its gate).  With a
-// residual the start value is x instead (dropped tokens pass through).
+// residual the start value is x instead (dropped tokens pass through).  The
+// rows s*T + t of S shared (always-on) experts are added with gate 1.
 //
 // Memory-bound: each token reads k rows of y_perm (+ x) and writes one row.
 // Every thread handles one 16-byte chunk of one token at a time.
@@ -29,7 +30,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot,
                                                       const float* __restrict__ gate,
                                                       const T* __restrict__ x, T* __restrict__ out,
-                                                      int64_t T_, int D, int k) {
+                                                      int64_t T_, int D, int k, int S) {
   constexpr int W = Vec<T>::W;
   typedef typename Vec<T>::type V;
   const int chunks = D / W;
@@ -46,6 +47,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
     } else {
 #pragma unroll
       for (int u = 0; u < W; ++u) acc[u] = 0.f;
+    }
+    for (int sh = 0; sh < S; ++sh) {
+      V yv = *(const V*)(y + ((int64_t)sh * T_ + t) * D + c * W);
+#pragma unroll
+      for (int u = 0; u < W; ++u) acc[u] += (float)yv[u];
     }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
@@ -136,10 +142,10 @@ hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t*
   const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
   if (s.dtype == MOE_DTYPE_BF16)
     hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)y_perm, slot, gate,
-                       (const bf16*)xr, (bf16*)out, s.T, s.D, s.k);
+                       (const bf16*)xr, (bf16*)out, s.T, s.D, s.k, s.n_shared);
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, (const float*)y_perm, slot, gate,
-                       (const float*)xr, (float*)out, s.T, s.D, s.k);
+                       (const float*)xr, (float*)out, s.T, s.D, s.k, s.n_shared);
   return hipGetLastError();
 }
 

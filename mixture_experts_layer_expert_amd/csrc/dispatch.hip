@@ -21,6 +21,9 @@
 //  C. each wave re-walks its segment: rank = wave base + in-wave rank; a
 //     rank below the capacity gets slot[a] = offsets[e] + rank and
 //     perm[slot] = a, the rest slot[a] = -1.
+// With S shared (always-on) experts their S*T rows come first: offsets[s] =
+// s*T for s <= S, perm[s*T + t] = t*k, and every routed offset and slot is
+// shifted by S*T.
 #include "moe_internal.h"
 
 namespace moe {
@@ -39,7 +42,7 @@ __device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                             int64_t A, int64_t T, int k, int by_choice,
-                                                            int N, int C,
+                                                            int N, int C, int S,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
@@ -114,16 +117,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
     if (tid < N && tid >= d) scan[tid] += v;
     __syncthreads();
   }
+  const int ST = S * (int)T;  // rows of the shared experts, in front
   if (tid < N) {
-    off[tid] = scan[tid] - kept;
-    offsets[tid] = scan[tid] - kept;
+    off[tid] = ST + scan[tid] - kept;
+    offsets[S + tid] = ST + scan[tid] - kept;
   }
+  if (tid < S) offsets[tid] = tid * (int)T;
   if (tid == 0) {
     const int total = N > 0 ? scan[N - 1] : 0;
-    off[N] = total;
-    offsets[N] = total;
+    off[N] = ST + total;
+    offsets[S + N] = ST + total;
     *n_dropped = (int32_t)(A - total);
   }
+  // shared rows: token t of shared expert s is row s*T + t, assignment t*k
+  for (int64_t r = tid; r < (int64_t)ST; r += kThreads) perm[r] = (int32_t)((r % T) * k);
   __syncthreads();
 
   // ---- C: final ranks -> slot and perm
@@ -166,7 +173,7 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
   const int64_t A = s.T * (int64_t)s.k;
   const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
-                     s.capacity, counts, offsets, perm, slot, n_dropped);
+                     s.capacity, s.n_shared, counts, offsets, perm, slot, n_dropped);
   return hipGetLastError();
 }
 

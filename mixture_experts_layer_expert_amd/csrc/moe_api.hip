@@ -41,12 +41,13 @@ int validate(const moe_shape* sp) {
       MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE | MOE_SLOT_MAJOR;
   if (s.flags & ~known) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && (s.flags & MOE_HAS_BIAS)) return MOE_ERR_UNSUPPORTED;
-  if (s.N > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (s.n_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (s.N + s.n_shared > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   const int mult = (s.dtype == MOE_DTYPE_BF16) ? 64 : 16;
   if (s.D % mult || s.F % mult) return MOE_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside the kernels
   const double lim = 4294967295.0;
-  const double A = (double)s.T * s.k;
+  const double A = (double)s.T * s.k + (double)s.T * s.n_shared;  // grouped rows
   if (A > 2147483647.0) return MOE_ERR_UNSUPPORTED;
   if ((double)s.T * s.D * 4 > lim || A * s.F * 4 > lim || A * s.D * 4 > lim || (double)s.F * s.D * 4 > lim)
     return MOE_ERR_UNSUPPORTED;
@@ -54,6 +55,10 @@ int validate(const moe_shape* sp) {
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Rows of the grouped buffers (perm, y_perm, hidden rows): the S*T rows of
+// the shared experts, then room for all T*k routed assignments.
+inline int64_t group_rows(const moe_shape& s) { return s.T * (int64_t)(s.k + s.n_shared); }
 
 // Mean rows per expert, capped by the capacity: picks the kernel shape.
 int64_t expected_rows(const moe_shape& s) {
@@ -63,7 +68,7 @@ int64_t expected_rows(const moe_shape& s) {
 }
 
 bool use_decode(const moe_shape& s) {
-  return (s.flags & MOE_FUSED_DECODE) && decode_applicable(s, expected_rows(s));
+  return (s.flags & MOE_FUSED_DECODE) && s.n_shared == 0 && decode_applicable(s, expected_rows(s));
 }
 
 // Split-K partial tiles of the grouped GEMMs (bf16): the last, partial round
@@ -78,12 +83,12 @@ size_t part_bytes(const moe_shape& s) {
 // fused decode path.
 size_t ffn_ws_bytes(const moe_shape& s) {
   if (use_decode(s)) return align_up(decode_part_bytes(s));
-  return align_up((size_t)s.T * s.k * s.F * elem_size(s)) + part_bytes(s);
+  return align_up((size_t)group_rows(s) * s.F * elem_size(s)) + part_bytes(s);
 }
 
 // Workspace of the whole layer: y_perm[T*k, D] followed by the expert stage.
 size_t forward_ws_bytes(const moe_shape& s) {
-  return align_up((size_t)s.T * s.k * s.D * elem_size(s)) + ffn_ws_bytes(s);
+  return align_up((size_t)group_rows(s) * s.D * elem_size(s)) + ffn_ws_bytes(s);
 }
 
 // Expert stage.  With the decode path the fp32 shard partials stay in ws;
@@ -101,7 +106,7 @@ hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, con
   g.perm = perm;
   g.topk = s.k;
   g.offsets = offsets;
-  g.n_experts = s.N;
+  g.n_experts = s.N + s.n_shared;  // the shared groups come first
   g.a_rows = s.T;
   g.B = w1;
   g.B2 = w3;
@@ -123,8 +128,8 @@ hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets
   g.perm = nullptr;
   g.topk = 1;
   g.offsets = offsets;
-  g.n_experts = s.N;
-  g.a_rows = s.T * s.k;
+  g.n_experts = s.N + s.n_shared;  // the shared groups come first
+  g.a_rows = group_rows(s);
   g.B = w2;
   g.B2 = nullptr;
   g.bias = (s.flags & MOE_HAS_BIAS) ? b2 : nullptr;
@@ -145,7 +150,7 @@ int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, cons
     if (e == hipSuccess && y_perm) e = launch_reduce_shards(s, (const float*)ws, offsets, y_perm, st);
     return hip_status(e);
   }
-  float* part = (float*)((unsigned char*)ws + align_up((size_t)s.T * s.k * s.F * elem_size(s)));
+  float* part = (float*)((unsigned char*)ws + align_up((size_t)group_rows(s) * s.F * elem_size(s)));
   if (s.dtype != MOE_DTYPE_BF16) part = nullptr;
   hipError_t e = launch_up(s, x, perm, offsets, w1, b1, w3, ws, part, st);
   if (e == hipSuccess) e = launch_down(s, ws, offsets, w2, b2, y_perm, part, st);
@@ -281,7 +286,7 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   void* y_perm = ws;
-  void* ffn_ws = (unsigned char*)ws + align_up((size_t)s.T * s.k * s.D * elem_size(s));
+  void* ffn_ws = (unsigned char*)ws + align_up((size_t)group_rows(s) * s.D * elem_size(s));
   hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, st);
   if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -184,6 +184,27 @@ def dispatch(idx: np.ndarray, N: int, C: Optional[int], priority: str = "token")
             "n_dropped": int(n_dropped)}
 
 
+def with_shared(disp: dict, T: int, k: int, n_shared: int) -> dict:
+    """Dispatch of a layer with ``n_shared`` always-on experts (the notebook's
+    "Exercises" section: shared experts next to the routed ones).  Every
+    token goes to every shared expert, uncapped, with gate 1.  Their rows come
+    first: row s*T + t belongs to token t of shared expert s (``perm`` holds
+    t*k there, the assignment index of the token's first choice, so that
+    perm // k is the token), then the routed rows of ``disp`` shifted by
+    n_shared*T.  ``offsets`` gains the n_shared groups in front; ``counts``
+    and ``n_dropped`` stay those of the routed assignments.
+    """
+    if n_shared == 0:
+        return disp
+    ST = n_shared * T
+    offsets = np.concatenate([np.arange(n_shared) * T, disp["offsets"] + ST])
+    perm = np.concatenate([np.tile(np.arange(T) * k, n_shared), disp["perm"]])
+    slot = np.where(disp["slot"] >= 0, disp["slot"] + ST, -1)
+    out = dict(disp)
+    out.update({"offsets": offsets, "perm": perm, "slot": slot})
+    return out
+
+
 def drop_rate(counts: np.ndarray, C: Optional[int]) -> float:
     """Summed overflow max(0, count - C) over summed counts."""
     counts = np.asarray(counts, dtype=np.int64)
@@ -266,15 +287,18 @@ def _expert_params(params: dict, e: int) -> dict:
 # ----------------------------------------------------------------- forward
 def combine_from_experts(x, params: dict, act: str, k: int, gate: np.ndarray,
                          disp: dict, residual: bool,
-                         tokens: Optional[Sequence[int]] = None) -> dict:
+                         tokens: Optional[Sequence[int]] = None, n_shared: int = 0) -> dict:
     """Per-expert loop of "Dispatch and gather" over the kept assignments.
 
     out starts at zero (or at x with ``residual``); for each expert e the
     rows of its kept assignments are gathered, run through expert e, scaled
-    by their gates and added to their tokens' outputs.  With ``tokens`` only
-    those tokens' outputs are produced (rows of other tokens are skipped).
-    Returns ``y`` (float64, [T, D] or [len(tokens), D]) and ``y_perm``
-    (ungated expert output of every computed kept row; NaN elsewhere).
+    by their gates and added to their tokens' outputs.  With ``n_shared``
+    (``disp`` from ``with_shared``) the first n_shared groups are the shared
+    experts, weight slots 0..n_shared-1, gate 1; routed expert e is weight
+    slot n_shared + e.  With ``tokens`` only those tokens' outputs are
+    produced (rows of other tokens are skipped).  Returns ``y`` (float64,
+    [T, D] or [len(tokens), D]) and ``y_perm`` (ungated expert output of
+    every computed kept row; NaN elsewhere).
     """
     xs = x
     T = xs.shape[0]
@@ -307,20 +331,24 @@ def combine_from_experts(x, params: dict, act: str, k: int, gate: np.ndarray,
         j = a % k
         Ye = expert_mlp(f64(xs[t]), act, **_expert_params(params, e))
         y_perm[rows] = Ye
-        np.add.at(out, where[t], Ye * gate[t, j][:, None])
+        g = np.ones(t.size) if e < n_shared else gate[t, j]
+        np.add.at(out, where[t], Ye * g[:, None])
     return {"y": out, "y_perm": y_perm}
 
 
-def combine_rows(y_perm, slot, gate, k: int, x=None) -> np.ndarray:
+def combine_rows(y_perm, slot, gate, k: int, x=None, n_shared: int = 0) -> np.ndarray:
     """Aggregation alone, from given expert output rows: out[t] is the sum
     over choices j whose assignment t*k+j was kept of gate[t, j] times row
-    slot[t*k+j] of y_perm, plus x[t] when x is given."""
+    slot[t*k+j] of y_perm, plus rows s*T + t of the n_shared shared experts
+    (gate 1), plus x[t] when x is given."""
     y_perm = f64(y_perm)
     slot = np.asarray(slot).reshape(-1)
     gate = np.asarray(gate, dtype=np.float64)
     T = gate.shape[0]
     out = np.zeros((T, y_perm.shape[1])) if x is None else f64(x).copy()
     for t in range(T):
+        for s_ in range(n_shared):
+            out[t] += y_perm[s_ * T + t]
         for j in range(k):
             s = slot[t * k + j]
             if s >= 0:
@@ -330,17 +358,19 @@ def combine_rows(y_perm, slot, gate, k: int, x=None) -> np.ndarray:
 
 def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                 capacity_slots: Optional[int] = None, residual: bool = False,
-                tokens: Optional[Sequence[int]] = None, priority: str = "token") -> dict:
+                tokens: Optional[Sequence[int]] = None, priority: str = "token",
+                n_shared: int = 0) -> dict:
     """Whole layer: route, dispatch with capacity, experts, combine.
 
     ``params`` holds w_router, b_router, w1, b1, w3, w2, b2 (numpy arrays or
-    CPU tensors in the C-ABI layouts; absent entries are None).  ``priority``
-    is the capacity order of ``dispatch``.
+    CPU tensors in the C-ABI layouts; absent entries are None); the expert
+    stacks hold n_shared shared experts first, then the routed ones.
+    ``priority`` is the capacity order of ``dispatch``.
     """
     r = route(x, params["w_router"], params.get("b_router"), k, renorm)
     N = r["logits"].shape[1]
-    d = dispatch(r["idx"], N, capacity_slots, priority)
-    c = combine_from_experts(x, params, act, k, r["gate"], d, residual, tokens)
+    d = with_shared(dispatch(r["idx"], N, capacity_slots, priority), f64(x).shape[0], k, n_shared)
+    c = combine_from_experts(x, params, act, k, r["gate"], d, residual, tokens, n_shared)
     out = dict(r)
     out.update(d)
     out.update(c)
@@ -349,7 +379,7 @@ def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
 
 def brute_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                   capacity_slots: Optional[int] = None, residual: bool = False,
-                  priority: str = "token") -> np.ndarray:
+                  priority: str = "token", n_shared: int = 0) -> np.ndarray:
     """Second formulation for tiny inputs: every expert on every token.
 
     Builds the sparse gate matrix G[t, e] (the gate of each kept assignment,
@@ -384,8 +414,10 @@ def brute_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                        if flat[b] == flat[a] and (b % k, b // k) < (j, t))
         if capacity_slots is None or rank < capacity_slots:
             G[a // k, flat[a]] += g[a // k, a % k]
-    Yall = np.stack([expert_mlp(X, act, **_expert_params(params, e)) for e in range(N)])
+    Yall = np.stack([expert_mlp(X, act, **_expert_params(params, n_shared + e)) for e in range(N)])
     y = np.einsum("te,ted->td", G, Yall.transpose(1, 0, 2))
+    for s_ in range(n_shared):  # always-on experts, gate 1
+        y = y + expert_mlp(X, act, **_expert_params(params, s_))
     if residual:
         y = y + X
     return y

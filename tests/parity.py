@@ -35,7 +35,7 @@ def capacity_of(cfg):
 def oracle_layer(cfg, inp, tokens=None, priority="token") -> dict:
     return oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, renorm=cfg.renorm,
                               capacity_slots=capacity_of(cfg), residual=cfg.residual, tokens=tokens,
-                              priority=priority)
+                              priority=priority, n_shared=cfg.n_shared)
 
 
 def row_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
@@ -62,13 +62,14 @@ def check_routing(buf: api.MoeBuffers, ref: dict, cfg):
 
 
 def check_outputs(y_gpu: np.ndarray, ref: dict, cfg, x_rows: np.ndarray, tokens=None):
-    """Tolerance on every row; exactness on rows whose assignments all dropped."""
+    """Tolerance on every row; exactness on rows whose assignments all dropped
+    (without shared experts: with them such a row still gets their output)."""
     y_ref = ref["y"]
     k = cfg.k
     slot = ref["slot"].reshape(-1, k)
     rows = np.arange(y_ref.shape[0]) if tokens is None else np.asarray(tokens)
     all_dropped = (slot[rows] < 0).all(axis=1)
-    if all_dropped.any():
+    if all_dropped.any() and cfg.n_shared == 0:
         want = x_rows[all_dropped] if cfg.residual else 0.0
         assert np.array_equal(y_gpu[all_dropped], np.broadcast_to(want, y_gpu[all_dropped].shape)), \
             "dropped tokens must pass through exactly"

@@ -86,6 +86,12 @@ def test_workspace_bytes_and_validation(lib):
     rc, n = _ws(lib, _shape(T=64))
     assert rc == L.MOE_OK
     assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2 + grid * 32 * 256 * 4
+    # two shared experts: the grouped rows grow by 2*T
+    rc, n = _ws(lib, _shape(T=4096, n_shared=2))
+    assert rc == L.MOE_OK
+    assert n == 4096 * 4 * 128 * 2 + 4096 * 4 * 256 * 2 + grid * 256 * 256 * 4
+    assert _ws(lib, _shape(n_shared=-1))[0] == L.MOE_ERR_INVALID_ARG
+    assert _ws(lib, _shape(N=250, n_shared=7))[0] == L.MOE_ERR_UNSUPPORTED
     # fp32 layers never split
     rc, n = _ws(lib, _shape(T=64, dtype=L.MOE_DTYPE_F32, act=L.MOE_ACT_GELU))
     assert rc == L.MOE_OK

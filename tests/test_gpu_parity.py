@@ -176,6 +176,10 @@ SCALED = {
     "c3": scaled_config(get_config("c3"), T=1500),
     "c4": scaled_config(get_config("c4"), T=700, D=1024, F=2048),
     "c5": get_config("c5"),
+    # shared (always-on) experts next to the routed ones
+    "c6": scaled_config(get_config("c6"), T=600, D=1024, F=512),
+    "c6cf": scaled_config(get_config("c6", cf=1.0), T=300, D=512, F=256, N=16, k=2, n_shared=1),
+    "c1sh": scaled_config(get_config("c1"), T=256, init="normal0.02", n_shared=2, name="c1_shared"),
     # few rows per expert -> fused weight-streaming path
     "c3dec": scaled_config(get_config("c3"), T=64, name="c3_skew_decode"),
     "c2dec": scaled_config(get_config("c2"), T=1000, name="c2_switch_decode"),
@@ -216,7 +220,8 @@ def test_forward_scaled(gpu, key, scaled_cases):
     assert torch.equal(out1, buf.out)
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5", "c3dec", "c2dec", "c5:fused", "c3dec:fused"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5", "c6", "c6cf", "c1sh", "c3dec", "c2dec",
+                                 "c5:fused", "c3dec:fused"])
 def test_stage_chain(gpu, key, scaled_cases):
     """route -> dispatch -> expert_ffn -> combine, each stage also checked
     alone against the oracle with oracle-made inputs."""
@@ -228,7 +233,7 @@ def test_stage_chain(gpu, key, scaled_cases):
     buf = api.MoeBuffers(shape)
     api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
     api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
-    A = cfg.T * cfg.k
+    A = shape.group_rows
     y_perm = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
     api.expert_ffn(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], g["w2"], g["b2"],
                    y_perm, buf.ws)
@@ -260,12 +265,12 @@ def test_stage_chain(gpu, key, scaled_cases):
     api.combine(shape, y_in.to(gpu), slot.to(gpu), gate.to(gpu), g["x"], out2)
     torch.cuda.synchronize()
     want = oracle.combine_rows(y_in.double().numpy(), ref["slot"], gate.double().numpy(), cfg.k,
-                               inp["x"] if cfg.residual else None)
+                               inp["x"] if cfg.residual else None, n_shared=cfg.n_shared)
     tol = 1e-6 if cfg.dtype == "fp32" else 8e-3  # one final rounding to the layer dtype
     assert row_rel_err(out2.float().cpu().numpy().astype(np.float64), want) <= tol
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5", "c6", "c1sh"])
 def test_expert_up_down(gpu, key, scaled_cases):
     """fc1(+act) and fc2 as separate launches: H against the oracle's hidden
     rows, fc2 alone on the oracle's H, and up+down equal to moe_expert_ffn."""
@@ -276,7 +281,7 @@ def test_expert_up_down(gpu, key, scaled_cases):
     buf = api.MoeBuffers(shape)
     api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
     api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
-    A = cfg.T * cfg.k
+    A = shape.group_rows
     h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=gpu)
     y_ud = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
     y_ffn = torch.empty_like(y_ud)
@@ -298,7 +303,7 @@ def test_expert_up_down(gpu, key, scaled_cases):
     assert row_rel_err(y_ns[:K].float().cpu().numpy().astype(np.float64), ref["y_perm"]) <= TOL[cfg.dtype]
     # oracle hidden rows, expert by expert in grouped order
     h_ref = np.zeros((K, cfg.F))
-    for e in range(cfg.N):
+    for e in range(cfg.n_shared + cfg.N):  # groups = expert weight slots
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 > r0:
             toks = perm[r0:r1] // cfg.k
@@ -314,7 +319,7 @@ def test_expert_up_down(gpu, key, scaled_cases):
     torch.cuda.synchronize()
     y2_ref = np.zeros((K, cfg.D))
     h_in64 = h_in[:K].double().numpy()
-    for e in range(cfg.N):
+    for e in range(cfg.n_shared + cfg.N):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 > r0:
             y2_ref[r0:r1] = oracle.expert_output(h_in64[r0:r1], inp["w2"][e],
@@ -339,7 +344,7 @@ def test_forward_choice_priority(gpu, key, T):
 
 
 # ------------------------------------------ full-size layers, sampled rows
-FULL = ["c2", "c2cf15", "c3", "c4", "c5"]
+FULL = ["c2", "c2cf15", "c3", "c4", "c5", "c6"]
 
 
 def _full_cfg(key):

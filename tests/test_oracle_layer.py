@@ -210,3 +210,79 @@ def test_combine_rows_hand_example_and_consistency():
     r = oracle.moe_forward(xx, p, k=k, act="gelu", capacity_slots=9, residual=True)
     y = oracle.combine_rows(r["y_perm"], r["slot"], r["gate"], k, xx)
     assert np.allclose(y, r["y"], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------ shared (always-on) experts
+def _shared_params(rng, S, N, D, F, act, bias):
+    """Stacks of S shared experts followed by N routed ones; router over N."""
+    p = _params(rng, S + N, D, F, act, bias)
+    p["w_router"] = rng.standard_normal((N, D))
+    return p
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("act", ["gelu", "relu", "swiglu"])
+def test_shared_experts_match_dense_brute_force(seed, act):
+    rng = np.random.default_rng(300 + seed)
+    T = int(rng.integers(1, 16))
+    N = int(rng.integers(1, 6))
+    S = int(rng.integers(1, 3))
+    k = int(rng.integers(1, N + 1))
+    D, F = 5, 7
+    p = _shared_params(rng, S, N, D, F, act, act != "swiglu")
+    x = rng.standard_normal((T, D))
+    for C in (None, 0, 2):
+        for residual in (False, True):
+            a = oracle.moe_forward(x, p, k=k, act=act, capacity_slots=C, residual=residual, n_shared=S)["y"]
+            b = oracle.brute_forward(x, p, k=k, act=act, capacity_slots=C, residual=residual, n_shared=S)
+            assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_one_routed_one_shared_equals_torch_modules():
+    """N = 1, k = 1: the routed gate is exactly 1, so the layer is the sum of
+    two plain MLPs (torch CPU Linear + GELU), the routed one in slot 1."""
+    rng = np.random.default_rng(17)
+    T, D, F = 23, 12, 20
+    p = _shared_params(rng, 1, 1, D, F, "gelu", True)
+    x = rng.standard_normal((T, D))
+    r = oracle.moe_forward(x, p, k=1, act="gelu", n_shared=1)
+    xt = torch.from_numpy(x)
+
+    def mlp(e):
+        fc1 = torch.nn.Linear(D, F).double()
+        fc2 = torch.nn.Linear(F, D).double()
+        with torch.no_grad():
+            fc1.weight.copy_(torch.from_numpy(p["w1"][e])); fc1.bias.copy_(torch.from_numpy(p["b1"][e]))
+            fc2.weight.copy_(torch.from_numpy(p["w2"][e])); fc2.bias.copy_(torch.from_numpy(p["b2"][e]))
+            return fc2(Fnn.gelu(fc1(xt))).numpy()
+    assert np.allclose(r["gate"], 1.0)
+    assert np.allclose(r["y"], mlp(0) + mlp(1), rtol=1e-12, atol=1e-12)
+
+
+def test_shared_rows_and_gate_one_pinned_by_unique_biases():
+    """W2 = 0: every expert outputs its own b2, so y[t] = sum over shared s of
+    b2[s] + sum over kept choices of g[t,j] * b2[S + idx[t,j]], exactly."""
+    rng = np.random.default_rng(18)
+    T, D, F, N, S, k = 41, 6, 9, 5, 2, 2
+    p = _shared_params(rng, S, N, D, F, "gelu", True)
+    p["w2"][:] = 0.0
+    p["b2"] = np.arange((S + N) * D, dtype=np.float64).reshape(S + N, D) + 1.0
+    x = rng.standard_normal((T, D))
+    for C in (None, 7, 0):
+        r = oracle.moe_forward(x, p, k=k, act="gelu", capacity_slots=C, n_shared=S)
+        want = np.tile(p["b2"][:S].sum(0), (T, 1))
+        flat = r["idx"].reshape(-1)
+        for a in range(T * k):
+            t, j = divmod(a, k)
+            rank = int((flat[:a] == flat[a]).sum())
+            if C is None or rank < C:
+                want[t] += r["gate"][t, j] * p["b2"][S + flat[a]]
+        assert np.allclose(r["y"], want, rtol=1e-14, atol=1e-13)
+        # rows: shared expert s, token t at s*T + t; routed rows after S*T
+        assert r["offsets"][:S + 1].tolist() == [s * T for s in range(S + 1)]
+        assert (r["perm"][:S * T] == np.tile(np.arange(T) * k, S)).all()
+        kept = r["slot"] >= 0
+        assert (r["slot"][kept] >= S * T).all()
+        # combine_rows over the same rows reproduces the layer output
+        y2 = oracle.combine_rows(r["y_perm"], r["slot"], r["gate"], k, None, n_shared=S)
+        assert np.allclose(y2, r["y"], rtol=1e-13, atol=1e-12)

@@ -39,12 +39,18 @@ class MoeConfig:
     init: str         # "p5" (notebook recipe) | "normal0.02"
     seed: int         # base seed for every stream of this config
     x_seed: int = 0   # x stream seed offset (near-tie rule)
+    n_shared: int = 0  # always-on experts, applied to every token with gate 1
     description: str = ""
 
     @property
     def A(self) -> int:
         """Number of (token, choice) assignments, T*k."""
         return self.T * self.k
+
+    @property
+    def n_slots(self) -> int:
+        """Expert weight slots: the shared experts first, then the N routed."""
+        return self.n_shared + self.N
 
     def with_cf(self, cf: Optional[float]) -> "MoeConfig":
         return dataclasses.replace(self, cf=cf)
@@ -81,6 +87,13 @@ CONFIGS: dict[str, MoeConfig] = {
         init="normal0.02", seed=5, x_seed=0,
         description="Decode-regime fine-grained MoE: 128 tokens, D=2048, d_ff=1408, 64 experts, "
                     "top-6, SwiGLU experts; weight-streaming"),
+    "c6": MoeConfig(
+        name="c6_shared_bf16", T=4096, D=2048, F=1408, N=64, k=6, act="swiglu", dtype="bf16",
+        expert_bias=False, renorm=False, router_bias=None, cf=None, residual=False,
+        init="normal0.02", seed=6, x_seed=1, n_shared=2,
+        description="Fine-grained MoE with always-on experts (the notebook's shared-experts "
+                    "exercise, DeepSeek-V2-Lite-shaped): 4096 tokens, D=2048, d_ff=1408, 2 shared "
+                    "+ 64 routed experts, top-6, SwiGLU"),
 }
 
 

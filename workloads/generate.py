@@ -18,7 +18,9 @@ Two recipes:
 
 bf16 tensors are drawn in fp32 and rounded to nearest-even.  All tensors are
 CPU tensors in the layouts of the C ABI: x[T,D], w_router[N,D], b_router[N],
-w1[N,F,D], b1[N,F], w3[N,F,D], w2[N,D,F], b2[N,D].
+w1[S+N,F,D], b1[S+N,F], w3[S+N,F,D], w2[S+N,D,F], b2[S+N,D]; with S shared
+(always-on) experts they take the first S expert slots and routed expert r
+is slot S + r.
 """
 from __future__ import annotations
 
@@ -87,6 +89,8 @@ def expert_slice(cfg: MoeConfig, tensor: str, e: int) -> torch.Tensor:
 def _gen_p5(cfg: MoeConfig, parts: Iterable[str]) -> dict:
     if cfg.dtype != "fp32":
         raise ValueError("the notebook recipe is fp32")
+    if cfg.n_shared:
+        raise ValueError("the notebook recipe has no shared experts")
     out: dict = {}
     with torch.random.fork_rng(devices=[]):
         torch.manual_seed(cfg.seed)
@@ -133,9 +137,9 @@ def _gen_normal(cfg: MoeConfig, parts: Iterable[str]) -> dict:
         specs = _expert_tensor_specs(cfg)
         jobs = []
         for name, shape in specs:
-            t = torch.empty((cfg.N,) + shape, dtype=dt)
+            t = torch.empty((cfg.n_slots,) + shape, dtype=dt)
             out[name] = t
-            for e in range(cfg.N):
+            for e in range(cfg.n_slots):
                 jobs.append((t[e], shape, _stream_seed(cfg.seed, name, e)))
         with ThreadPoolExecutor(max_workers=_threads()) as ex:
             list(ex.map(lambda j: _normal(j[1], j[2], _STD_W, dt, out=j[0]), jobs))
