@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--cf", type=float, default=None, help="capacity factor override (<0: none)")
     ap.add_argument("--priority", choices=("token", "choice"), default="token",
                     help="capacity priority: token order, or (choice, token) (MOE_SLOT_MAJOR)")
+    ap.add_argument("--layout", choices=("compact", "padded"), default="compact",
+                    help="grouped rows sized by the counts, or N*capacity rows (MOE_PADDED)")
     ap.add_argument("--copies", type=int, default=3,
                     help="copies of x and the weights cycled over consecutive steps")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay")
@@ -216,7 +218,10 @@ def main():
     # copy 0 is the generated tensors; the others are device clones (same
     # values, different addresses)
     gs = [g0] + [{k: (None if v is None else v.clone()) for k, v in g0.items()} for _ in range(R - 1)]
-    shape = dataclasses.replace(api.MoeShape.from_config(cfg), slot_major=args.priority == "choice")
+    shape = dataclasses.replace(api.MoeShape.from_config(cfg), slot_major=args.priority == "choice",
+                                padded=args.layout == "padded")
+    if shape.padded and shape.capacity < 0:
+        raise SystemExit("--layout padded needs a capacity factor (--cf >= 0)")
     buf = api.MoeBuffers(shape, device=dev)
     A = cfg.T * cfg.k
     h = torch.empty(shape.group_rows, cfg.F, dtype=shape.torch_dtype, device=dev)
@@ -263,9 +268,11 @@ def main():
               "combine": mean_ms(3, 4)}
 
     counts = buf.counts.cpu()
-    offsets = buf.offsets.cpu()
-    kept = int(offsets[-1])
-    used = int(((offsets[1:] - offsets[:-1]) > 0).sum())
+    # useful rows and experts (the padded layout's padding rows are excluded)
+    kept_r = counts.clamp(max=shape.capacity) if shape.capacity >= 0 else counts
+    n_sh = cfg.n_shared if cfg.T > 0 else 0
+    kept = cfg.n_shared * cfg.T + int(kept_r.sum())
+    used = n_sh + int((kept_r > 0).sum())
     n_dropped = int(buf.n_dropped.cpu())
     work = launch_work(cfg, kept, used)
     lflops = layer_flops(cfg, kept)
@@ -333,7 +340,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "D": cfg.D, "F": cfg.F, "experts": cfg.N,
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
                    "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
-                   "capacity_priority": args.priority, "input_copies": R},
+                   "capacity_priority": args.priority, "layout": args.layout, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stages,
@@ -348,7 +355,8 @@ def main():
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak,
             "traffic": (measured_traffic(args.workload, launch)
-                        if args.cf is None and args.priority == "token" else None),
+                        if args.cf is None and args.priority == "token" and args.layout == "compact"
+                        else None),
             "launch_ms": stages[launch],
             "algorithmic": {"flops": flops, "bytes": bytes_,
                             "rule": "used experts' weights once + activation rows in once + "

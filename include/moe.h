@@ -84,7 +84,14 @@ enum moe_flags {
    * order (choice j, token t), so every token's first choice is kept before
    * any second choice (the GShard top-2 pattern named among the notebook's
    * references); without it the order is the flat index t*k+j. */
-  MOE_SLOT_MAJOR = 32u
+  MOE_SLOT_MAJOR = 32u,
+  /* Static capacity layout: every routed expert owns exactly `capacity`
+   * rows, expert e rows [S*T + e*C, S*T + (e+1)*C), kept assignments first
+   * and padding after; the experts' MLPs run on all N*C rows (padding rows
+   * re-use assignment 0 and their outputs are never read).  Without it the
+   * rows are sized by the actual counts (the compact, "dynamic gating"
+   * layout of "Towards MoE Deployment", abstract).  Needs capacity >= 0. */
+  MOE_PADDED = 64u
 };
 
 typedef struct moe_shape {
@@ -145,7 +152,8 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
  * and *n_dropped = T*k - offsets[N].  perm must hold T*k entries; entries
  * past offsets[N] are left untouched.  With n_shared = S the S shared groups
  * come first (offsets[S+N+1], perm of S*T + T*k entries, routed rows and
- * slots shifted by S*T; see moe_shape).  Expert ids outside [0, N) are
+ * slots shifted by S*T; see moe_shape).  With MOE_PADDED expert e's rows
+ * start at S*T + e*C and perm holds S*T + N*C entries, padding included.  Expert ids outside [0, N) are
  * treated as dropped and not counted.  Bit-exact, deterministic. */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,

@@ -27,6 +27,7 @@ MOE_HAS_BIAS = 4
 MOE_ROUTER_BIAS = 8
 MOE_FUSED_DECODE = 16
 MOE_SLOT_MAJOR = 32
+MOE_PADDED = 64
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
             "moe_combine", "moe_forward", "moe_status_string")

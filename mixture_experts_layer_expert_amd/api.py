@@ -43,6 +43,7 @@ class MoeShape:
     fused_decode: bool = False  # MOE_FUSED_DECODE algorithm choice
     slot_major: bool = False    # MOE_SLOT_MAJOR capacity priority (choice, token)
     n_shared: int = 0           # always-on experts (expert slots 0..n_shared-1)
+    padded: bool = False        # MOE_PADDED static capacity layout (N*capacity rows)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -51,14 +52,16 @@ class MoeShape:
     @property
     def group_rows(self) -> int:
         """Rows of the grouped buffers (perm, y_perm, hidden rows)."""
-        return self.T * (self.k + self.n_shared)
+        routed = self.N * self.capacity if self.padded else self.T * self.k
+        return self.T * self.n_shared + routed
 
     def c(self) -> L.MoeShapeC:
         flags = ((L.MOE_RENORM if self.renorm else 0) | (L.MOE_RESIDUAL if self.residual else 0)
                  | (L.MOE_HAS_BIAS if self.has_bias else 0)
                  | (L.MOE_ROUTER_BIAS if self.router_bias else 0)
                  | (L.MOE_FUSED_DECODE if self.fused_decode else 0)
-                 | (L.MOE_SLOT_MAJOR if self.slot_major else 0))
+                 | (L.MOE_SLOT_MAJOR if self.slot_major else 0)
+                 | (L.MOE_PADDED if self.padded else 0))
         return L.MoeShapeC(self.T, self.D, self.F, self.N, self.k, self.capacity,
                            _DT[self.dtype][0], _ACT[self.act], flags, self.n_shared)
 

@@ -23,7 +23,9 @@
 //     perm[slot] = a, the rest slot[a] = -1.
 // With S shared (always-on) experts their S*T rows come first: offsets[s] =
 // s*T for s <= S, perm[s*T + t] = t*k, and every routed offset and slot is
-// shifted by S*T.
+// shifted by S*T.  In the padded layout expert e's rows start at S*T + e*C
+// and its C - kept padding rows get perm = 0 (a valid gather row whose
+// output nobody reads).
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,7 +44,7 @@ __device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
                                                             int64_t A, int64_t T, int k, int by_choice,
-                                                            int N, int C, int S,
+                                                            int N, int C, int S, int pad,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
@@ -119,18 +121,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
   }
   const int ST = S * (int)T;  // rows of the shared experts, in front
   if (tid < N) {
-    off[tid] = ST + scan[tid] - kept;
-    offsets[S + tid] = ST + scan[tid] - kept;
+    const int o = ST + (pad ? tid * C : scan[tid] - kept);
+    off[tid] = o;
+    offsets[S + tid] = o;
   }
   if (tid < S) offsets[tid] = tid * (int)T;
   if (tid == 0) {
-    const int total = N > 0 ? scan[N - 1] : 0;
-    off[N] = ST + total;
-    offsets[S + N] = ST + total;
+    const int total = N > 0 ? scan[N - 1] : 0;  // kept assignments
+    off[N] = ST + (pad ? N * C : total);
+    offsets[S + N] = ST + (pad ? N * C : total);
     *n_dropped = (int32_t)(A - total);
   }
   // shared rows: token t of shared expert s is row s*T + t, assignment t*k
   for (int64_t r = tid; r < (int64_t)ST; r += kThreads) perm[r] = (int32_t)((r % T) * k);
+  if (pad) {
+    // padding rows after each expert's kept rows (kept_e = scan[e] - scan[e-1])
+    for (int64_t i = tid; i < (int64_t)N * C; i += kThreads) {
+      const int e = (int)(i / C), r = (int)(i - (int64_t)e * C);
+      const int kept_e = scan[e] - (e > 0 ? scan[e - 1] : 0);
+      if (r >= kept_e) perm[ST + i] = 0;
+    }
+  }
   __syncthreads();
 
   // ---- C: final ranks -> slot and perm
@@ -173,7 +184,8 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
   const int64_t A = s.T * (int64_t)s.k;
   const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
   hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
-                     s.capacity, s.n_shared, counts, offsets, perm, slot, n_dropped);
+                     s.capacity, s.n_shared, (s.flags & MOE_PADDED) ? 1 : 0, counts, offsets, perm, slot,
+                     n_dropped);
   return hipGetLastError();
 }
 

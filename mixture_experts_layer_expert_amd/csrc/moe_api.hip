@@ -37,17 +37,19 @@ int validate(const moe_shape* sp) {
   if (s.k > s.N || s.capacity < -1) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.act != MOE_ACT_GELU && s.act != MOE_ACT_RELU && s.act != MOE_ACT_SWIGLU) return MOE_ERR_INVALID_ARG;
-  const uint32_t known =
-      MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE | MOE_SLOT_MAJOR;
+  const uint32_t known = MOE_RENORM | MOE_RESIDUAL | MOE_HAS_BIAS | MOE_ROUTER_BIAS | MOE_FUSED_DECODE |
+                         MOE_SLOT_MAJOR | MOE_PADDED;
   if (s.flags & ~known) return MOE_ERR_INVALID_ARG;
   if (s.act == MOE_ACT_SWIGLU && (s.flags & MOE_HAS_BIAS)) return MOE_ERR_UNSUPPORTED;
   if (s.n_shared < 0) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_PADDED) && s.capacity < 0) return MOE_ERR_INVALID_ARG;
   if (s.N + s.n_shared > kMaxExperts || s.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   const int mult = (s.dtype == MOE_DTYPE_BF16) ? 64 : 16;
   if (s.D % mult || s.F % mult) return MOE_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside the kernels
   const double lim = 4294967295.0;
-  const double A = (double)s.T * s.k + (double)s.T * s.n_shared;  // grouped rows
+  const double A = (double)s.T * s.k + (double)s.T * s.n_shared +
+                   ((s.flags & MOE_PADDED) ? (double)s.N * s.capacity : 0.0);  // grouped rows (bound)
   if (A > 2147483647.0) return MOE_ERR_UNSUPPORTED;
   if ((double)s.T * s.D * 4 > lim || A * s.F * 4 > lim || A * s.D * 4 > lim || (double)s.F * s.D * 4 > lim)
     return MOE_ERR_UNSUPPORTED;
@@ -57,18 +59,25 @@ int validate(const moe_shape* sp) {
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Rows of the grouped buffers (perm, y_perm, hidden rows): the S*T rows of
-// the shared experts, then room for all T*k routed assignments.
-inline int64_t group_rows(const moe_shape& s) { return s.T * (int64_t)(s.k + s.n_shared); }
+// the shared experts, then room for all T*k routed assignments (N*C rows in
+// the padded layout).
+inline int64_t group_rows(const moe_shape& s) {
+  const int64_t routed = (s.flags & MOE_PADDED) ? (int64_t)s.N * s.capacity : s.T * (int64_t)s.k;
+  return s.T * (int64_t)s.n_shared + routed;
+}
 
-// Mean rows per expert, capped by the capacity: picks the kernel shape.
+// Mean rows per expert, capped by the capacity (exactly the capacity in the
+// padded layout): picks the kernel shape.
 int64_t expected_rows(const moe_shape& s) {
+  if (s.flags & MOE_PADDED) return s.capacity;
   int64_t expect = (s.T * s.k + s.N - 1) / s.N;
   if (s.capacity >= 0 && expect > s.capacity) expect = s.capacity;
   return expect;
 }
 
 bool use_decode(const moe_shape& s) {
-  return (s.flags & MOE_FUSED_DECODE) && s.n_shared == 0 && decode_applicable(s, expected_rows(s));
+  return (s.flags & MOE_FUSED_DECODE) && s.n_shared == 0 && !(s.flags & MOE_PADDED) &&
+         decode_applicable(s, expected_rows(s));
 }
 
 // Split-K partial tiles of the grouped GEMMs (bf16): the last, partial round

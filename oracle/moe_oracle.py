@@ -184,6 +184,29 @@ def dispatch(idx: np.ndarray, N: int, C: Optional[int], priority: str = "token")
             "n_dropped": int(n_dropped)}
 
 
+def padded(disp: dict, N: int, C: int) -> dict:
+    """The static capacity layout: every expert owns exactly C rows, expert e
+    rows e*C .. e*C + C - 1, its kept assignments first in rank order and
+    padding after (the fixed per-expert buffer the notebook's "Capacity
+    factor" section sizes; the compact, count-sized layout of ``dispatch``
+    is the "dynamic gating" alternative of "Towards MoE Deployment").
+    ``perm`` holds -1 on padding rows; ``slot`` and ``offsets`` follow the
+    new rows; counts and drops are unchanged.
+    """
+    if C is None:
+        raise ValueError("the padded layout needs a capacity")
+    off = disp["offsets"]
+    perm = np.full(N * C, -1, dtype=np.int64)
+    slot = np.full_like(disp["slot"], -1)
+    for e in range(N):
+        kept = disp["perm"][off[e]:off[e + 1]]
+        perm[e * C:e * C + kept.size] = kept
+        slot[kept] = e * C + np.arange(kept.size)
+    out = dict(disp)
+    out.update({"offsets": np.arange(N + 1) * C, "perm": perm, "slot": slot})
+    return out
+
+
 def with_shared(disp: dict, T: int, k: int, n_shared: int) -> dict:
     """Dispatch of a layer with ``n_shared`` always-on experts (the notebook's
     "Exercises" section: shared experts next to the routed ones).  Every
@@ -323,6 +346,7 @@ def combine_from_experts(x, params: dict, act: str, k: int, gate: np.ndarray,
     for e in range(N):
         rows = np.arange(offsets[e], offsets[e + 1])
         a = perm[rows]
+        rows, a = rows[a >= 0], a[a >= 0]  # padding rows of the static layout carry nothing
         t = a // k
         sel = want[t]
         if not sel.any():
@@ -359,17 +383,24 @@ def combine_rows(y_perm, slot, gate, k: int, x=None, n_shared: int = 0) -> np.nd
 def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                 capacity_slots: Optional[int] = None, residual: bool = False,
                 tokens: Optional[Sequence[int]] = None, priority: str = "token",
-                n_shared: int = 0) -> dict:
+                n_shared: int = 0, layout: str = "compact") -> dict:
     """Whole layer: route, dispatch with capacity, experts, combine.
 
     ``params`` holds w_router, b_router, w1, b1, w3, w2, b2 (numpy arrays or
     CPU tensors in the C-ABI layouts; absent entries are None); the expert
     stacks hold n_shared shared experts first, then the routed ones.
-    ``priority`` is the capacity order of ``dispatch``.
+    ``priority`` is the capacity order of ``dispatch``; ``layout`` is
+    "compact" (rows sized by the counts) or "padded" (``padded``: C rows
+    per expert).
     """
     r = route(x, params["w_router"], params.get("b_router"), k, renorm)
     N = r["logits"].shape[1]
-    d = with_shared(dispatch(r["idx"], N, capacity_slots, priority), f64(x).shape[0], k, n_shared)
+    d = dispatch(r["idx"], N, capacity_slots, priority)
+    if layout == "padded":
+        d = padded(d, N, capacity_slots)
+    elif layout != "compact":
+        raise ValueError(f"unknown layout {layout!r}")
+    d = with_shared(d, f64(x).shape[0], k, n_shared)
     c = combine_from_experts(x, params, act, k, r["gate"], d, residual, tokens, n_shared)
     out = dict(r)
     out.update(d)

@@ -32,10 +32,10 @@ def capacity_of(cfg):
     return oracle.capacity(cfg.T, cfg.k, cfg.N, cfg.cf)
 
 
-def oracle_layer(cfg, inp, tokens=None, priority="token") -> dict:
+def oracle_layer(cfg, inp, tokens=None, priority="token", layout="compact") -> dict:
     return oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, renorm=cfg.renorm,
                               capacity_slots=capacity_of(cfg), residual=cfg.residual, tokens=tokens,
-                              priority=priority, n_shared=cfg.n_shared)
+                              priority=priority, n_shared=cfg.n_shared, layout=layout)
 
 
 def row_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> float:
@@ -56,7 +56,10 @@ def check_routing(buf: api.MoeBuffers, ref: dict, cfg):
     assert np.array_equal(buf.counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(buf.offsets.cpu().numpy(), ref["offsets"])
     K = int(ref["offsets"][-1])
-    assert np.array_equal(buf.perm.cpu().numpy()[:K], ref["perm"])
+    # padding rows of the static layout: -1 in the oracle, assignment 0 (a
+    # valid gather row whose output is never read) on the GPU
+    want_perm = np.where(ref["perm"] < 0, 0, ref["perm"])
+    assert np.array_equal(buf.perm.cpu().numpy()[:K], want_perm)
     assert np.array_equal(buf.slot.cpu().numpy()[: T * k], ref["slot"])
     assert int(buf.n_dropped.cpu().item()) == ref["n_dropped"]
 
@@ -78,8 +81,9 @@ def check_outputs(y_gpu: np.ndarray, ref: dict, cfg, x_rows: np.ndarray, tokens=
     return err
 
 
-def run_forward(cfg, g: dict, T=None, fused_decode=False, slot_major=False) -> api.MoeBuffers:
-    shape = dataclasses.replace(api.MoeShape.from_config(cfg, T, fused_decode), slot_major=slot_major)
+def run_forward(cfg, g: dict, T=None, fused_decode=False, slot_major=False, padded=False) -> api.MoeBuffers:
+    shape = dataclasses.replace(api.MoeShape.from_config(cfg, T, fused_decode), slot_major=slot_major,
+                                padded=padded)
     buf = api.MoeBuffers(shape)
     buf.forward(g["x"], g)
     torch.cuda.synchronize()

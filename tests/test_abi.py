@@ -90,6 +90,10 @@ def test_workspace_bytes_and_validation(lib):
     rc, n = _ws(lib, _shape(T=4096, n_shared=2))
     assert rc == L.MOE_OK
     assert n == 4096 * 4 * 128 * 2 + 4096 * 4 * 256 * 2 + grid * 256 * 256 * 4
+    # padded layout, capacity 1536: N*C = 12288 grouped rows instead of T*k
+    rc, n = _ws(lib, _shape(T=4096, capacity=1536, flags=L.MOE_PADDED))
+    assert rc == L.MOE_OK
+    assert n == 12288 * 128 * 2 + 12288 * 256 * 2 + grid * 256 * 256 * 4
     assert _ws(lib, _shape(n_shared=-1))[0] == L.MOE_ERR_INVALID_ARG
     assert _ws(lib, _shape(N=250, n_shared=7))[0] == L.MOE_ERR_UNSUPPORTED
     # fp32 layers never split
@@ -108,7 +112,7 @@ def test_workspace_bytes_and_validation(lib):
         (dict(T=-1), L.MOE_ERR_INVALID_ARG), (dict(capacity=-2), L.MOE_ERR_INVALID_ARG),
         (dict(dtype=7), L.MOE_ERR_INVALID_ARG), (dict(act=5), L.MOE_ERR_INVALID_ARG),
         (dict(flags=1 << 7), L.MOE_ERR_INVALID_ARG), (dict(D=100), L.MOE_ERR_UNSUPPORTED),
-        (dict(flags=1 << 6), L.MOE_ERR_INVALID_ARG),
+        (dict(flags=L.MOE_PADDED), L.MOE_ERR_INVALID_ARG),  # padded layout without a capacity
         (dict(F=96), L.MOE_ERR_UNSUPPORTED), (dict(flags=L.MOE_HAS_BIAS), L.MOE_ERR_UNSUPPORTED),
         (dict(T=2**31, D=4096), L.MOE_ERR_UNSUPPORTED),
     ]

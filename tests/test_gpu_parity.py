@@ -96,25 +96,28 @@ def test_route_shapes(gpu, N, k):
 
 
 # ------------------------------------------------------------- dispatch
-def _dispatch_case(gpu, idx_np, N, C, priority="token"):
+def _dispatch_case(gpu, idx_np, N, C, priority="token", padded=False):
     T, k = idx_np.shape
     shape = api.MoeShape(T=T, D=64, F=64, N=N, k=k, capacity=-1 if C is None else C, act="relu",
-                         slot_major=(priority == "choice"))
+                         slot_major=(priority == "choice"), padded=padded)
     i32 = dict(dtype=torch.int32, device=gpu)
     idx = torch.from_numpy(idx_np.astype(np.int32)).to(gpu)
     counts = torch.full((N,), -7, **i32)
     offsets = torch.full((N + 1,), -7, **i32)
-    perm = torch.full((T * k,), -7, **i32)
+    perm = torch.full((max(shape.group_rows, 1) + 5,), -7, **i32)
     slot = torch.full((T * k,), -7, **i32)
     nd = torch.full((1,), -7, **i32)
     api.dispatch(shape, idx, counts, offsets, perm, slot, nd)
     torch.cuda.synchronize()
     ref = oracle.dispatch(idx_np, N, C, priority)
+    if padded:
+        ref = oracle.padded(ref, N, C)
     assert np.array_equal(counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
     K = int(ref["offsets"][-1])
     p = perm.cpu().numpy()
-    assert np.array_equal(p[:K], ref["perm"])
+    # padding rows (oracle -1) hold assignment 0 on the GPU
+    assert np.array_equal(p[:K], np.where(ref["perm"] < 0, 0, ref["perm"]))
     assert np.all(p[K:] == -7), "entries past offsets[N] must stay untouched"
     assert np.array_equal(slot.cpu().numpy(), ref["slot"])
     assert int(nd.item()) == ref["n_dropped"]
@@ -341,6 +344,36 @@ def test_forward_choice_priority(gpu, key, T):
     buf = run_forward(cfg, g, slot_major=True)
     check_routing(buf, ref, cfg)
     check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
+
+
+@pytest.mark.parametrize("T,N,k,C", [
+    (1, 1, 1, 0), (1, 4, 4, 1), (777, 8, 2, 150), (777, 8, 2, 400), (2000, 128, 1, 15), (2000, 128, 1, 0),
+    (5000, 64, 6, 700), (16384, 128, 1, 192),
+])
+def test_dispatch_padded(gpu, T, N, k, C):
+    rng = np.random.default_rng(T + 3 * N + k)
+    _dispatch_case(gpu, _rand_idx(rng, T, N, k), N, C, padded=True)
+
+
+@pytest.mark.parametrize("key,T,cf", [("c2", 2048, 1.5), ("c3", 1500, 1.0), ("c6", 1024, 1.0),
+                                      ("c1", None, 2.0)])
+def test_forward_padded_layout(gpu, key, T, cf):
+    """Whole layer in the static capacity layout (MOE_PADDED): routing and
+    row layout bit-exact against the oracle's padded dispatch, outputs within
+    tolerance, and equal to the compact layout's outputs."""
+    base = get_config(key, cf=cf)
+    cfg = base if T is None else scaled_config(base, T=T)
+    _say(f"forward padded {cfg.name}: T={cfg.T} k={cfg.k} cf={cfg.cf} shared={cfg.n_shared}")
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp, layout="padded")
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g, padded=True)
+    check_routing(buf, ref, cfg)
+    y = buf.out.float().cpu().numpy().astype(np.float64)
+    check_outputs(y, ref, cfg, inp["x"].double().numpy())
+    compact = run_forward(cfg, g)
+    y_c = compact.out.float().cpu().numpy().astype(np.float64)
+    assert row_rel_err(y, y_c) <= TOL[cfg.dtype]
 
 
 # ------------------------------------------ full-size layers, sampled rows

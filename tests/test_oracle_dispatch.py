@@ -202,3 +202,41 @@ def test_choice_priority_layer_matches_brute_force():
     y_b = oracle.brute_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, priority="choice")
     assert np.allclose(ref["y"], y_b, rtol=1e-12, atol=1e-12)
     assert ref["n_dropped"] > 0
+
+
+# ------------------------------------------------- static padded layout
+def test_padded_layout_hand_example_and_invariants():
+    # same hand case as the choice test: 4 tokens, top-2, 3 experts, C = 2
+    idx = np.array([[0, 1], [2, 0], [0, 2], [1, 0]])
+    d = oracle.padded(oracle.dispatch(idx, 3, 2), 3, 2)
+    assert d["offsets"].tolist() == [0, 2, 4, 6]
+    # token order: expert 0 keeps a=0,3; expert 1 a=1,6; expert 2 a=2,5
+    assert d["perm"].tolist() == [0, 3, 1, 6, 2, 5]
+    rng = np.random.default_rng(5)
+    T, N, k = 300, 7, 2
+    idx = _random_idx(rng, T, N, k)
+    for C in (0, 10, 90, 200):
+        dc = oracle.dispatch(idx, N, C)
+        dp = oracle.padded(dc, N, C)
+        assert dp["offsets"].tolist() == [e * C for e in range(N + 1)]
+        assert np.array_equal(dp["counts"], dc["counts"]) and dp["n_dropped"] == dc["n_dropped"]
+        kept = np.minimum(dc["counts"], C)
+        for e in range(N):
+            rows = dp["perm"][e * C:(e + 1) * C]
+            assert np.array_equal(rows[:kept[e]], dc["perm"][dc["offsets"][e]:dc["offsets"][e + 1]])
+            assert (rows[kept[e]:] == -1).all()
+        # every kept assignment's slot points at its own row
+        k_a = np.nonzero(dp["slot"] >= 0)[0]
+        assert np.array_equal(dp["perm"][dp["slot"][k_a]], k_a)
+        assert np.array_equal(dp["slot"] >= 0, dc["slot"] >= 0)
+
+
+def test_padded_layout_layer_equals_compact():
+    from workloads import generate, get_config, scaled_config
+    cfg = scaled_config(get_config("c1"), T=64, D=32, F=48, N=4, k=2)
+    inp = generate(cfg)
+    for cf in (0.5, 1.0, 2.0):
+        C = oracle.capacity(cfg.T, cfg.k, cfg.N, cf)
+        a = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C)
+        b = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, layout="padded")
+        assert np.allclose(a["y"], b["y"], rtol=1e-14, atol=1e-14)
