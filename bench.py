@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--cf", type=float, default=None, help="capacity factor override (<0: none)")
     ap.add_argument("--priority", choices=("token", "choice"), default="token",
                     help="capacity priority: token order, or (choice, token) (MOE_SLOT_MAJOR)")
+    ap.add_argument("--router-stats", action="store_true",
+                    help="also compute the router's load statistics (moe_route_stats + moe_router_stats)")
     ap.add_argument("--layout", choices=("compact", "padded"), default="compact",
                     help="grouped rows sized by the counts, or N*capacity rows (MOE_PADDED)")
     ap.add_argument("--copies", type=int, default=3,
@@ -227,12 +229,24 @@ def main():
     h = torch.empty(shape.group_rows, cfg.F, dtype=shape.torch_dtype, device=dev)
     y_perm = torch.empty(shape.group_rows, cfg.D, dtype=shape.torch_dtype, device=dev)
     st = torch.cuda.current_stream()
+    rstats = args.router_stats
+    if rstats:
+        stats_ws = torch.empty(api.stats_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        prob_mean = torch.empty(cfg.N, dtype=torch.float64, device=dev)
+        frac = torch.empty(cfg.N, dtype=torch.float64, device=dev)
+        summary = torch.empty(3, dtype=torch.float64, device=dev)
 
     def step(g, s, ev=None):
         if ev is not None:
             ev[0].record(s)
-        api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s)
+        if rstats:
+            api.route_stats(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate,
+                            stats_ws, None, s)
+        else:
+            api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s)
         api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
+        if rstats:
+            api.router_stats(shape, stats_ws, buf.counts, buf.n_dropped, prob_mean, frac, summary, s)
         if ev is not None:
             ev[1].record(s)
         api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, buf.ws, s)
@@ -340,13 +354,16 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "D": cfg.D, "F": cfg.F, "experts": cfg.N,
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
                    "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
-                   "capacity_priority": args.priority, "layout": args.layout, "input_copies": R},
+                   "capacity_priority": args.priority, "layout": args.layout,
+                   "router_stats": args.router_stats, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stages,
         "graph": graph,
         "routing": {"kept_assignments": kept, "dropped": n_dropped, "experts_used": used,
                     "max_count": int(counts.max()), "imbalance": float(counts.max()) / (A / cfg.N)},
+        "router_stats": ({"aux_loss": float(summary[0]), "imbalance": float(summary[1]),
+                          "drop_rate": float(summary[2])} if rstats else None),
         "roofline": {
             "kernel": f"grouped_gemm_kernel, {launch} launch "
                       f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "

@@ -142,6 +142,49 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               const float* b_router, int32_t* topk_idx, float* topk_gate,
               float* logits_opt, moe_stream_t stream);
 
+/* Router load statistics, the notebook's "Switch Transformer auxiliary loss"
+ * and "Capacity factor" sections, computed in two steps.
+ *
+ * moe_route_stats does what moe_route does, with identical outputs. In the
+ * same launch, each router block also adds up every expert's softmax
+ * probability over the block's tokens. It uses the fp32 logits the ranking
+ * used, bias included. The partial sums go to stats_ws, which the caller
+ * owns and which must hold moe_stats_workspace_bytes(shape) bytes, 256-byte
+ * aligned. The sizes depend on the shape and on the current device's CU
+ * count, so query the size on the device that runs the calls. stats_ws also
+ * holds a counter that moe_route_stats clears and moe_router_stats advances.
+ * Calls that share a stats_ws must therefore be ordered on one stream, and
+ * moe_router_stats must follow a moe_route_stats on that stats_ws. It may
+ * be repeated, though, without routing again.
+ *
+ * moe_router_stats runs after moe_dispatch of the same batch. It reads
+ * stats_ws, counts and n_dropped and writes device outputs:
+ *   prob_mean[e] = P_e = mean over the T tokens of softmax(l_t)[e].
+ *     The partials are summed in fp64 in a fixed order, so repeated runs
+ *     give the same result.
+ *   frac[e] = f_e = counts[e] / T, the share of tokens with expert e among
+ *     their choices. This holds because the k choices of a token are
+ *     distinct. frac may be NULL.
+ *   summary[0] = N * sum_e f_e * P_e, the Switch auxiliary loss. It equals k
+ *     for a perfectly balanced router.
+ *   summary[1] = max_e counts[e] / (T*k/N), the imbalance.
+ *   summary[2] = n_dropped / (T*k), the share of assignments dropped by the
+ *     capacity.
+ * prob_mean, frac and summary are fp64: N, N and 3 entries.
+ *
+ * Errors, for both calls:
+ *   MOE_ERR_WORKSPACE: stats_ws is NULL or too small.
+ *   MOE_ERR_INVALID_ARG: stats_ws is misaligned, or a required pointer is NULL.
+ * T = 0 is a no-op. */
+int moe_stats_workspace_bytes(const moe_shape* shape, size_t* bytes);
+int moe_route_stats(const moe_shape* shape, const void* x, const void* w_router,
+                    const float* b_router, int32_t* topk_idx, float* topk_gate,
+                    float* logits_opt, void* stats_ws, size_t stats_ws_bytes,
+                    moe_stream_t stream);
+int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_ws_bytes,
+                     const int32_t* counts, const int32_t* n_dropped, double* prob_mean,
+                     double* frac, double* summary, moe_stream_t stream);
+
 /* Dispatch ("Dispatch and gather", "Capacity factor"): counts[e] = number of
  * assignments to expert e (before the capacity cut).  The assignments of
  * expert e are ranked in increasing flat index (with MOE_SLOT_MAJOR: in

@@ -30,7 +30,8 @@ MOE_SLOT_MAJOR = 32
 MOE_PADDED = 64
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
-            "moe_combine", "moe_forward", "moe_status_string")
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_stats_workspace_bytes",
+            "moe_route_stats", "moe_router_stats", "moe_status_string")
 
 
 class MoeShapeC(ctypes.Structure):
@@ -54,6 +55,9 @@ _SIGS = {
     "moe_capacity": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]),
     "moe_workspace_bytes": (ctypes.c_int, [_shape_p, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_stats_workspace_bytes": (ctypes.c_int, [_shape_p, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_route_stats": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "moe_router_stats": (ctypes.c_int, [_shape_p, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_dispatch": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_expert_ffn": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_size_t, _vp]),

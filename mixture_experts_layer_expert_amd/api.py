@@ -119,6 +119,33 @@ def route(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, logits=No
         _stream(stream)))
 
 
+def stats_workspace_bytes(shape: MoeShape) -> int:
+    n = ctypes.c_size_t(0)
+    sc = shape.c()
+    _check("moe_stats_workspace_bytes", L.load().moe_stats_workspace_bytes(ctypes.byref(sc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def route_stats(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, stats_ws, logits=None,
+                stream=None):
+    dt = shape.torch_dtype
+    sc = shape.c()
+    _check("moe_route_stats", L.load().moe_route_stats(
+        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(logits, torch.float32, "logits"),
+        *_ws_arg(stats_ws), _stream(stream)))
+
+
+def router_stats(shape: MoeShape, stats_ws, counts, n_dropped, prob_mean, frac, summary, stream=None):
+    i32, f64 = torch.int32, torch.float64
+    sc = shape.c()
+    _check("moe_router_stats", L.load().moe_router_stats(
+        ctypes.byref(sc), *_ws_arg(stats_ws), _ptr(counts, i32, "counts"),
+        _ptr(n_dropped, i32, "n_dropped"), _ptr(prob_mean, f64, "prob_mean"), _ptr(frac, f64, "frac"),
+        _ptr(summary, f64, "summary"), _stream(stream)))
+
+
 def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None):
     i32 = torch.int32
     sc = shape.c()

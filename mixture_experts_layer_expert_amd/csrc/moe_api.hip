@@ -196,8 +196,50 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router, const
   if (s.T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt,
+  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, nullptr,
                                  (hipStream_t)stream));
+}
+
+static size_t stats_ws_bytes(const moe_shape& s) {
+  // per-block partial sums, then the 8-byte ticket of the second pass
+  return align_up((size_t)route_blocks(s) * (size_t)s.N * sizeof(float)) + kAlign;
+}
+
+int moe_stats_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = stats_ws_bytes(*shape);
+  return MOE_OK;
+}
+
+int moe_route_stats(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                    int32_t* topk_idx, float* topk_gate, float* logits_opt, void* stats_ws,
+                    size_t stats_ws_bytes_, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
+  if (!stats_ws || stats_ws_bytes_ < stats_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)stats_ws % kAlign) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt,
+                                 (float*)stats_ws, (hipStream_t)stream));
+}
+
+int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_ws_bytes_,
+                     const int32_t* counts, const int32_t* n_dropped, double* prob_mean, double* frac,
+                     double* summary, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if (!counts || !n_dropped || !prob_mean || !summary) return MOE_ERR_INVALID_ARG;
+  if (!stats_ws || stats_ws_bytes_ < stats_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)stats_ws % kAlign) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_router_stats(s, (const float*)stats_ws, counts, n_dropped, prob_mean, frac,
+                                        summary, (hipStream_t)stream));
 }
 
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -296,7 +338,7 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   hipStream_t st = (hipStream_t)stream;
   void* y_perm = ws;
   void* ffn_ws = (unsigned char*)ws + align_up((size_t)group_rows(s) * s.D * elem_size(s));
-  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, st);
+  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, st);
   if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool decode = use_decode(s);

@@ -30,7 +30,16 @@ int device_cu_count();
 
 // ---- launchers (stream-ordered, no synchronisation, return hipError_t) ----
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,
-                        int32_t* idx, float* gate, float* logits, hipStream_t st);
+                        int32_t* idx, float* gate, float* logits, float* prob_part, hipStream_t st);
+
+// Router blocks of a launch (tokens per block depend on the shape and the
+// device's CU count); prob_part holds N * route_blocks(s) floats.
+int route_rows_per_block(const moe_shape& s);
+int64_t route_blocks(const moe_shape& s);
+unsigned long long* stats_ticket(const moe_shape& s, const float* prob_part);
+hipError_t launch_router_stats(const moe_shape& s, const float* prob_part, const int32_t* counts,
+                               const int32_t* n_dropped, double* prob_mean, double* frac, double* summary,
+                               hipStream_t st);
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,

@@ -35,6 +35,8 @@ struct RouteArgs {
   int32_t* idx;
   float* gate;
   float* logits;
+  float* prob_part;  // optional: [N][blocks] per-block probability sums
+  unsigned long long* stats_ticket;  // with prob_part: cleared by block 0
 };
 
 template <typename V>
@@ -52,10 +54,12 @@ __device__ inline float vexp(float v) { return expf(v); }
 // Ranks one token within a 16-lane group.  vals: LDS row of N logits.
 // Returns true when the top-(k+1) are separated by at least `margin`
 // (always true for fp64 ranking, margin = -1).  On success (or when
-// `force`), lane 0 of the group writes idx/gate for token t.
+// `force`), lane 0 of the group writes idx/gate for token t.  With `stats`
+// (load statistics), every valid token's softmax probabilities of the lane's
+// experts l16 + 16 i are added to pacc[i], near-tie tokens included.
 template <typename V, int NV>
-__device__ bool group_rank(const V* vals, const RouteArgs& a, int64_t t, int l16, V margin,
-                           bool force) {
+__device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, int64_t t, int l16, V margin,
+                                           bool force, bool stats, V (&pacc)[NV]) {
   const int N = a.N, k = a.k;
   V v[NV];
 #pragma unroll
@@ -99,17 +103,25 @@ __device__ bool group_rank(const V* vals, const RouteArgs& a, int64_t t, int l16
 #pragma unroll
   for (int r = 0; r < kMaxTopK; ++r)
     if (r < ngap) ok = ok && (tv[r] - tv[r + 1] >= margin);
-  if (!ok && !force) return false;
+  if (!ok && !force && !stats) return false;
   // softmax denominator over all N experts
   const V vmax = tv[0];
   V s = 0;
+  V ex[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int e = l16 + 16 * i;
-    if (e < N) s += vexp(v[i] - vmax);
+    ex[i] = (e < N) ? vexp(v[i] - vmax) : V(0);
+    s += ex[i];
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  if (stats && t < a.T) {
+    const V inv = V(1) / s;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) pacc[i] += ex[i] * inv;
+  }
+  if (!ok && !force) return false;
   if (l16 == 0 && t < a.T) {
     V p[kMaxTopK];
     V ps = 0;
@@ -401,6 +413,31 @@ __device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t 
   }
 }
 
+// Load statistics (notebook section "Switch Transformer auxiliary loss"):
+// the sum over the block's valid tokens of every expert's softmax
+// probability, stored as prob_part[e * gridDim.x + blockIdx.x].  The
+// ranking already forms exp(l - max) and the denominator of every token, so
+// each lane has added its experts' probabilities over the tokens its group
+// ranked (pacc[i]: expert l16 + 16 i).  Here the four groups of a wave are
+// summed with two xor shuffles, then the four waves in LDS, in a fixed
+// order.  Block 0 also clears the ticket of the second pass.
+template <int NT>
+__device__ void block_prob_sums(const RouteArgs& a, float (&pacc)[NT], int wave, int lane, int tid) {
+  constexpr int NP = 16 * NT;
+  __shared__ float red[4][NP];
+  if (blockIdx.x == 0 && tid == 0) *a.stats_ticket = 0ull;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    float x = pacc[i];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    if (lane < 16) red[wave][lane + 16 * i] = x;
+  }
+  __syncthreads();
+  for (int e = tid; e < a.N; e += 256)
+    a.prob_part[(int64_t)e * gridDim.x + blockIdx.x] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+}
+
 // Ranks the rows r = it*16 + wave*4 + group of the block's logits (16-lane
 // groups, fp32); the tokens whose top-(k+1) fp32 logits are too close are
 // then ranked again, one after the other, by the whole wave.
@@ -409,12 +446,16 @@ __device__ void rank_rows(const RouteArgs& a, const float* lg, int ldl, int64_t 
                           int lane) {
   constexpr int NJ = (16 * NT + 63) / 64;
   const int grp = lane >> 4, l16 = lane & 15;
+  float pacc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) pacc[i] = 0.f;
+  const bool stats = a.prob_part != nullptr;
   uint32_t marked = 0;
 #pragma unroll 1
   for (int it = 0; it < ITERS; ++it) {
     const int r = it * 16 + wave * 4 + grp;
     const int64_t t = t0 + r;
-    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false);
+    const bool ok = group_rank<float, NT>(lg + r * ldl, a, t, l16, kRefineMargin, false, stats, pacc);
     if (a.logits && t < a.T)
       for (int e = l16; e < a.N; e += 16) a.logits[t * a.N + e] = lg[r * ldl + e];
     const uint64_t bad = __ballot(!ok && t < a.T);
@@ -422,6 +463,7 @@ __device__ void rank_rows(const RouteArgs& a, const float* lg, int ldl, int64_t 
     for (int g = 0; g < 4; ++g)
       if ((bad >> (16 * g)) & 1ull) marked |= 1u << (it * 4 + g);
   }
+  if (stats) block_prob_sums<NT>(a, pacc, wave, lane, threadIdx.x);
   marked = __builtin_amdgcn_readfirstlane(marked);
   while (marked) {
     const int m = __builtin_ctz(marked);
@@ -610,14 +652,11 @@ hipError_t launch_ring(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tokens per block: as many as keep >= ~2 blocks per CU busy, fewer for the
-// widest expert counts (their ring stages are large).
 template <int NT>
-hipError_t launch_ring_nt(const RouteArgs& a, hipStream_t st) {
-  const int64_t cus = device_cu_count();
+hipError_t launch_ring_nt(const RouteArgs& a, int rows, hipStream_t st) {
   if constexpr (NT < 16) {
-    if (a.T >= 64 * cus) return launch_ring<NT, 64>(a, st);
-    if (a.T >= 32 * cus) return launch_ring<NT, 32>(a, st);
+    if (rows == 64) return launch_ring<NT, 64>(a, st);
+    if (rows == 32) return launch_ring<NT, 32>(a, st);
   }
   return launch_ring<NT, 16>(a, st);
 }
@@ -630,14 +669,14 @@ hipError_t launch_nt(const RouteArgs& a, hipStream_t st) {
 }
 
 template <typename T>
-hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
+hipError_t launch_t(const RouteArgs& a, int rows, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     if (a.D % 128 == 0) {
-      if (a.N <= 16) return launch_ring_nt<1>(a, st);
-      if (a.N <= 32) return launch_ring_nt<2>(a, st);
-      if (a.N <= 64) return launch_ring_nt<4>(a, st);
-      if (a.N <= 128) return launch_ring_nt<8>(a, st);
-      return launch_ring_nt<16>(a, st);
+      if (a.N <= 16) return launch_ring_nt<1>(a, rows, st);
+      if (a.N <= 32) return launch_ring_nt<2>(a, rows, st);
+      if (a.N <= 64) return launch_ring_nt<4>(a, rows, st);
+      if (a.N <= 128) return launch_ring_nt<8>(a, rows, st);
+      return launch_ring_nt<16>(a, rows, st);
     }
   }
   if (a.N <= 16) return launch_nt<T, 1>(a, st);
@@ -647,10 +686,116 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t st) {
   return launch_nt<T, 16>(a, st);
 }
 
+// Statistics, second pass, one wave per expert e (grid N): lane l adds the
+// block partials b = l, l + 64, ... in increasing b in fp64 (loads issued 8
+// at a time), then a butterfly; P_e = sum / T and f_e = counts[e] / T.  The
+// order is fixed, so the result does not depend on timing.  Each wave then
+// takes a ticket; the wave that draws the last one of this call (N tickets
+// per call, the count cleared by the router) reads every P_e back and forms
+// the Switch auxiliary loss N * sum_e f_e * P_e, the imbalance
+// max_e count_e / (T*k/N) and the drop rate n_dropped / (T*k).
+__global__ __launch_bounds__(64) void router_stats_kernel(const float* part, int nblk, int N, int64_t T, int k,
+                                                          const int32_t* counts, const int32_t* n_dropped,
+                                                          double* prob_mean, double* frac, double* summary,
+                                                          unsigned long long* ticket) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const float* row = part + (int64_t)e * nblk;
+  double sum = 0.0;
+  for (int b0 = 0; b0 < nblk; b0 += 8 * kWave) {
+    // clamped, unconditional loads: all 8 are in flight before the first add
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = b0 + i * kWave + lane;
+      v[i] = row[b < nblk ? b : nblk - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (b0 + i * kWave + lane < nblk) sum += (double)v[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  int last = 0;
+  if (lane == 0) {
+    prob_mean[e] = sum / (double)T;
+    if (frac) frac[e] = (double)counts[e] / (double)T;
+    __threadfence();  // publish prob_mean[e] before the ticket
+    const unsigned long long old = atomicAdd(ticket, 1ull);
+    last = (old % (unsigned long long)N) == (unsigned long long)(N - 1);
+  }
+  last = __shfl(last, 0);
+  if (!last) return;
+  __threadfence();  // every other wave's prob_mean is visible past its ticket
+  // at most 4 experts per lane, loads clamped and all in flight
+  static_assert(kMaxExperts <= 4 * kWave, "experts per lane");
+  int c[4];
+  double p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane + j * kWave < N ? lane + j * kWave : N - 1;
+    c[j] = counts[i];
+    p[j] = prob_mean[i];
+  }
+  double acc = 0.0;
+  int mx = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (lane + j * kWave < N) {
+      acc += ((double)c[j] / (double)T) * p[j];
+      mx = c[j] > mx ? c[j] : mx;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    acc += __shfl_xor(acc, off);
+    const int o = __shfl_xor(mx, off);
+    mx = o > mx ? o : mx;
+  }
+  if (lane == 0) {
+    const double A = (double)T * (double)k;
+    summary[0] = (double)N * acc;
+    summary[1] = (double)mx / (A / (double)N);
+    summary[2] = (double)*n_dropped / A;
+  }
+}
+
 }  // namespace
 
+// Tokens per router block.  bf16 with D a multiple of 128 uses the DMA ring
+// kernel: as many tokens as keep >= ~2 blocks per CU busy, 16 for the widest
+// expert counts (their ring stages are large); otherwise 32.
+int route_rows_per_block(const moe_shape& s) {
+  if (s.dtype == MOE_DTYPE_BF16 && s.D % 128 == 0) {
+    if (s.N > 128) return 16;
+    const int64_t cus = device_cu_count();
+    if (s.T >= 64 * cus) return 64;
+    if (s.T >= 32 * cus) return 32;
+    return 16;
+  }
+  return 32;
+}
+
+int64_t route_blocks(const moe_shape& s) {
+  const int rows = route_rows_per_block(s);
+  return (s.T + rows - 1) / rows;
+}
+
+// The second pass's ticket sits after the partials, 256-byte aligned.
+unsigned long long* stats_ticket(const moe_shape& s, const float* part) {
+  const size_t off = ((size_t)route_blocks(s) * (size_t)s.N * sizeof(float) + 255) & ~(size_t)255;
+  return (unsigned long long*)((const unsigned char*)part + off);
+}
+
+hipError_t launch_router_stats(const moe_shape& s, const float* part, const int32_t* counts,
+                               const int32_t* n_dropped, double* prob_mean, double* frac, double* summary,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(router_stats_kernel, dim3(s.N), dim3(kWave), 0, st, part, (int)route_blocks(s), s.N, s.T,
+                     s.k, counts, n_dropped, prob_mean, frac, summary, stats_ticket(s, part));
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,
-                        int32_t* idx, float* gate, float* logits, hipStream_t st) {
+                        int32_t* idx, float* gate, float* logits, float* prob_part, hipStream_t st) {
   RouteArgs a;
   a.x = x;
   a.wr = wr;
@@ -664,8 +809,11 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const
   a.idx = idx;
   a.gate = gate;
   a.logits = logits;
-  if (s.dtype == MOE_DTYPE_BF16) return launch_t<bf16>(a, st);
-  return launch_t<float>(a, st);
+  a.prob_part = prob_part;
+  a.stats_ticket = prob_part ? stats_ticket(s, prob_part) : nullptr;
+  const int rows = route_rows_per_block(s);
+  if (s.dtype == MOE_DTYPE_BF16) return launch_t<bf16>(a, rows, st);
+  return launch_t<float>(a, rows, st);
 }
 
 }  // namespace moe

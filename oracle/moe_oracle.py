@@ -241,6 +241,21 @@ def imbalance(counts: np.ndarray, T: int, k: int, N: int) -> float:
     return float(np.max(counts) / (T * k / N))
 
 
+def router_stats(idx: np.ndarray, probs: np.ndarray, counts: np.ndarray, N: int, C: Optional[int]) -> dict:
+    """The router's load statistics for one batch: per expert the fraction
+    f_i of tokens with expert i among their choices and the mean softmax
+    probability P_i over all N experts (notebook section "Switch Transformer
+    auxiliary loss"), the auxiliary loss N * sum f_i P_i, the imbalance
+    max count / (T*k/N) and the drop rate at capacity C (section "Capacity
+    factor")."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    f = np.array([(idx == e).any(axis=1).mean() for e in range(N)])
+    P = np.asarray(probs).mean(axis=0)
+    return {"frac": f, "prob_mean": P, "aux_loss": float(N * (f * P).sum()),
+            "imbalance": imbalance(counts, T, k, N), "drop_rate": drop_rate(counts, C)}
+
+
 def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, N: int) -> float:
     """N * sum_i f_i * P_i with f_i the fraction of tokens having expert i
     among their choices and P_i the mean router probability of expert i

@@ -240,3 +240,41 @@ def test_padded_layout_layer_equals_compact():
         a = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C)
         b = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, layout="padded")
         assert np.allclose(a["y"], b["y"], rtol=1e-14, atol=1e-14)
+
+
+def test_router_stats_closed_forms_and_invariants():
+    """f sums to k and P to 1 on any batch; equal logits give P = 1/N and a
+    loss of exactly k; all tokens on one expert with all probability there
+    gives a loss of N; the hand case below is worked out on paper."""
+    rng = np.random.default_rng(5)
+    T, N, k = 50, 6, 2
+    logits = rng.standard_normal((T, N))
+    probs = oracle.softmax(logits)
+    idx = oracle.select_topk(logits, k)
+    counts = oracle.expert_counts(idx, N)
+    st = oracle.router_stats(idx, probs, counts, N, oracle.capacity(T, k, N, 1.0))
+    assert st["frac"].sum() == pytest.approx(k, abs=1e-12)
+    assert st["prob_mean"].sum() == pytest.approx(1.0, abs=1e-12)
+    assert np.array_equal(st["frac"], counts / T)  # distinct choices: any() == count
+    assert st["aux_loss"] == pytest.approx(oracle.switch_aux_loss(idx, probs, N), abs=0)
+    # equal logits: P = 1/N, loss = N * sum f / N = k
+    flat = np.zeros((T, N))
+    st = oracle.router_stats(oracle.select_topk(flat, k), oracle.softmax(flat),
+                             oracle.expert_counts(oracle.select_topk(flat, k), N), N, None)
+    assert np.allclose(st["prob_mean"], 1.0 / N, atol=1e-15)
+    assert st["aux_loss"] == pytest.approx(k, abs=1e-12)
+    # ties go to the lowest indices: every token on experts 0..k-1
+    assert st["imbalance"] == T / (T * k / N) and st["drop_rate"] == 0.0
+    # hand case: T=4, N=4, k=1, tokens on experts 0, 0, 0, 2; probabilities
+    # 0.7 on the chosen expert and 0.1 elsewhere; capacity 2
+    idx = np.array([[0], [0], [0], [2]])
+    probs = np.full((4, 4), 0.1)
+    probs[np.arange(4), idx[:, 0]] = 0.7
+    counts = oracle.expert_counts(idx, 4)
+    st = oracle.router_stats(idx, probs, counts, 4, 2)
+    assert np.allclose(st["frac"], [0.75, 0.0, 0.25, 0.0])
+    assert np.allclose(st["prob_mean"], [0.55, 0.1, 0.25, 0.1])
+    # 4 * (0.75*0.55 + 0.25*0.25) = 4 * 0.475 = 1.9
+    assert st["aux_loss"] == pytest.approx(1.9, abs=1e-12)
+    assert st["imbalance"] == 3.0      # 3 / (4*1/4)
+    assert st["drop_rate"] == 0.25     # one of four over capacity 2
