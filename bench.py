@@ -92,6 +92,9 @@ def parse():
                     help="capacity priority: token order, or (choice, token) (MOE_SLOT_MAJOR)")
     ap.add_argument("--router-stats", action="store_true",
                     help="also compute the router's load statistics (moe_route_stats + moe_router_stats)")
+    ap.add_argument("--expert-shard", type=int, default=1, metavar="G",
+                    help="time one GPU's share of an expert-sharded layer: every expert's hidden dim F/G "
+                         "(a column block of w1/w3 and the matching row block of w2), all tokens")
     ap.add_argument("--layout", choices=("compact", "padded"), default="compact",
                     help="grouped rows sized by the counts, or N*capacity rows (MOE_PADDED)")
     ap.add_argument("--copies", type=int, default=3,
@@ -207,10 +210,15 @@ def main():
     import torch
 
     from mixture_experts_layer_expert_amd import api
-    from workloads import generate, get_config
+    from workloads import generate, get_config, scaled_config
 
     cf = "keep" if args.cf is None else (None if args.cf < 0 else args.cf)
     cfg = get_config(args.workload, cf=cf)
+    if args.expert_shard > 1:
+        G = args.expert_shard
+        if cfg.F % G or (cfg.F // G) % 32:
+            raise SystemExit(f"--expert-shard {G}: F={cfg.F} must split into multiples of 32")
+        cfg = scaled_config(cfg, F=cfg.F // G, name=f"{cfg.name}_fshare{G}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -355,7 +363,7 @@ def main():
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
                    "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
                    "capacity_priority": args.priority, "layout": args.layout,
-                   "router_stats": args.router_stats, "input_copies": R},
+                   "router_stats": args.router_stats, "expert_shard": args.expert_shard, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stages,
@@ -373,7 +381,7 @@ def main():
             "frac": achieved / peak,
             "traffic": (measured_traffic(args.workload, launch)
                         if args.cf is None and args.priority == "token" and args.layout == "compact"
-                        else None),
+                        and args.expert_shard == 1 else None),
             "launch_ms": stages[launch],
             "algorithmic": {"flops": flops, "bytes": bytes_,
                             "rule": "used experts' weights once + activation rows in once + "

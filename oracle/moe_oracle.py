@@ -184,6 +184,73 @@ def dispatch(idx: np.ndarray, N: int, C: Optional[int], priority: str = "token")
             "n_dropped": int(n_dropped)}
 
 
+def fallback_choices(logits: np.ndarray, probs: np.ndarray, k: int, R: int, renorm: bool):
+    """The R next-best experts of every token after its k choices (ranks
+    k .. k+R-1 of ``expert_order``) and their gates: the softmax probability,
+    divided by the same sum over the k choices as the k gates when
+    ``renorm``."""
+    N = logits.shape[1]
+    if not 1 <= k + R <= N:
+        raise ValueError(f"k + R = {k + R} must lie in [1, N={N}]")
+    order = expert_order(logits)[:, :k + R].astype(np.int64)
+    p = np.take_along_axis(probs, order, axis=1)
+    fb = p[:, k:]
+    if renorm:
+        fb = fb / p[:, :k].sum(axis=1, keepdims=True)
+    return order[:, k:], fb
+
+
+def reroute(disp: dict, idx: np.ndarray, gate: np.ndarray, fb_idx: np.ndarray, fb_gate: np.ndarray,
+            N: int, C: Optional[int]) -> dict:
+    """Overflow fallback after the capacity cut: a dropped assignment is sent
+    to the token's next-best expert that still has room (the notebook's
+    "What" section names a fallback path for the overflow; rerouting rejected
+    tokens to less busy experts is the first page's tuning trick).
+
+    Level r = 0 .. R-1: every token with a dropped assignment left offers its
+    lowest-j one to its expert of rank k + r (``fb_idx[t, r]``); each expert
+    accepts the offers in increasing token order while its rows stay within
+    C.  An accepted assignment (t, j) takes that expert and the gate
+    ``fb_gate[t, r]``.  Expert e's rows are its kept assignments in priority
+    order (``disp``), then the accepted ones in (level, token) order.  Returns
+    ``disp`` updated (counts keep the routed counts before the cut, n_dropped
+    counts what stays dropped) plus the rewritten ``idx`` and ``gate`` and
+    ``n_rerouted``.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    R = fb_idx.shape[1]
+    idx2 = idx.copy()
+    gate2 = np.array(gate, dtype=np.float64, copy=True)
+    off = disp["offsets"]
+    rows = [list(disp["perm"][off[e]:off[e + 1]]) for e in range(N)]
+    if C is not None:
+        room = [C - len(rows[e]) for e in range(N)]
+        dropped = [[j for j in range(k) if disp["slot"][t * k + j] < 0] for t in range(T)]
+        for r in range(R):
+            for t in range(T):
+                if not dropped[t]:
+                    continue
+                e = int(fb_idx[t, r])
+                if room[e] > 0:
+                    j = dropped[t].pop(0)
+                    room[e] -= 1
+                    rows[e].append(t * k + j)
+                    idx2[t, j] = e
+                    gate2[t, j] = fb_gate[t, r]
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    slot = np.full(T * k, -1, dtype=np.int64)
+    for e in range(N):
+        offsets[e + 1] = offsets[e] + len(rows[e])
+        for i, a in enumerate(rows[e]):
+            slot[a] = offsets[e] + i
+    perm = np.array([a for e in range(N) for a in rows[e]], dtype=np.int64)
+    out = dict(disp)
+    out.update({"offsets": offsets, "perm": perm, "slot": slot, "n_dropped": int(T * k - perm.size),
+                "n_rerouted": int(perm.size - disp["perm"].size), "idx": idx2, "gate": gate2})
+    return out
+
+
 def padded(disp: dict, N: int, C: int) -> dict:
     """The static capacity layout: every expert owns exactly C rows, expert e
     rows e*C .. e*C + C - 1, its kept assignments first in rank order and
@@ -398,7 +465,7 @@ def combine_rows(y_perm, slot, gate, k: int, x=None, n_shared: int = 0) -> np.nd
 def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
                 capacity_slots: Optional[int] = None, residual: bool = False,
                 tokens: Optional[Sequence[int]] = None, priority: str = "token",
-                n_shared: int = 0, layout: str = "compact") -> dict:
+                n_shared: int = 0, layout: str = "compact", n_fallback: int = 0) -> dict:
     """Whole layer: route, dispatch with capacity, experts, combine.
 
     ``params`` holds w_router, b_router, w1, b1, w3, w2, b2 (numpy arrays or
@@ -406,11 +473,19 @@ def moe_forward(x, params: dict, *, k: int, act: str, renorm: bool = False,
     stacks hold n_shared shared experts first, then the routed ones.
     ``priority`` is the capacity order of ``dispatch``; ``layout`` is
     "compact" (rows sized by the counts) or "padded" (``padded``: C rows
-    per expert).
+    per expert); ``n_fallback`` = R > 0 reroutes dropped assignments over R
+    levels (``reroute``, compact layout).
     """
     r = route(x, params["w_router"], params.get("b_router"), k, renorm)
     N = r["logits"].shape[1]
     d = dispatch(r["idx"], N, capacity_slots, priority)
+    if n_fallback:
+        if layout != "compact":
+            raise ValueError("rerouting uses the compact layout")
+        fb_idx, fb_gate = fallback_choices(r["logits"], r["probs"], k, n_fallback, renorm)
+        d = reroute(d, r["idx"], r["gate"], fb_idx, fb_gate, N, capacity_slots)
+        r = dict(r)
+        r.update({"idx": d.pop("idx"), "gate": d.pop("gate"), "fb_idx": fb_idx, "fb_gate": fb_gate})
     if layout == "padded":
         d = padded(d, N, capacity_slots)
     elif layout != "compact":

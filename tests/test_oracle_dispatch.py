@@ -278,3 +278,100 @@ def test_router_stats_closed_forms_and_invariants():
     assert st["aux_loss"] == pytest.approx(1.9, abs=1e-12)
     assert st["imbalance"] == 3.0      # 3 / (4*1/4)
     assert st["drop_rate"] == 0.25     # one of four over capacity 2
+
+
+def _reroute_case(idx, fb, N, C):
+    idx = np.asarray(idx)
+    fb = np.asarray(fb)
+    T, k = idx.shape
+    gate = np.full((T, k), 0.5)
+    fb_gate = np.tile(np.arange(1, fb.shape[1] + 1) * 0.01, (T, 1))
+    d = oracle.dispatch(idx, N, C)
+    return oracle.reroute(d, idx, gate, fb, fb_gate, N, C)
+
+
+def test_reroute_hand_examples():
+    """Worked on paper.  (1) Switch-like k=1, C=1: tokens 1 and 2 overflow
+    expert 0; token 1's fallbacks (1, 2) find expert 1 full and, one level
+    later, expert 2 already taken at level 0 by token 2.  (2) Level order
+    beats token order: token 1 fails at level 0 and its level-1 expert went to
+    token 3 at level 0.  (3) k=2: both of token 1's choices overflow and come
+    back on two levels, lowest j first."""
+    r = _reroute_case([[0], [0], [0], [1]], [[1, 2], [1, 2], [2, 1], [0, 2]], N=3, C=1)
+    assert r["offsets"].tolist() == [0, 1, 2, 3]
+    assert r["perm"].tolist() == [0, 3, 2]
+    assert r["slot"].tolist() == [0, -1, 2, 1]
+    assert r["idx"].ravel().tolist() == [0, 0, 2, 1]
+    assert r["gate"].ravel().tolist() == [0.5, 0.5, 0.01, 0.5]
+    assert (r["n_dropped"], r["n_rerouted"]) == (1, 1)
+    assert r["counts"].tolist() == [3, 1, 0]  # routed counts before the cut
+    r = _reroute_case([[0], [0], [1], [0]], [[1, 2], [1, 2], [0, 2], [2, 1]], N=3, C=1)
+    assert r["perm"].tolist() == [0, 2, 3] and r["slot"].tolist() == [0, -1, 1, 2]
+    assert (r["n_dropped"], r["n_rerouted"]) == (1, 1)
+    r = _reroute_case([[0, 1], [0, 1]], [[2, 3], [2, 3]], N=4, C=1)
+    assert r["offsets"].tolist() == [0, 1, 2, 3, 4]
+    assert r["perm"].tolist() == [0, 1, 2, 3]
+    assert r["idx"].tolist() == [[0, 1], [2, 3]]
+    assert r["gate"].tolist() == [[0.5, 0.5], [0.01, 0.02]]
+    assert r["n_dropped"] == 0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_reroute_invariants(seed):
+    """No level or no capacity changes nothing; no expert exceeds C; a
+    rerouted choice is one of the token's fallbacks and never repeats one of
+    its experts; rows + drops = T*k; slot and perm agree; expert rows hold
+    their kept assignments first, in dispatch order."""
+    rng = np.random.default_rng(seed)
+    T, N, k, R = 300, 8, 2, 3
+    logits = rng.standard_normal((T, N)) + np.linspace(1.5, 0, N)  # skewed
+    probs = oracle.softmax(logits)
+    idx = oracle.select_topk(logits, k)
+    gate = oracle.gate_values(probs, idx, False)
+    fb_idx, fb_gate = oracle.fallback_choices(logits, probs, k, R, False)
+    C = oracle.capacity(T, k, N, 1.0)
+    d = oracle.dispatch(idx, N, C)
+    for none in (oracle.reroute(d, idx, gate, fb_idx[:, :0], fb_gate[:, :0], N, C),
+                 oracle.reroute(oracle.dispatch(idx, N, None), idx, gate, fb_idx, fb_gate, N, None)):
+        base = d if none["n_dropped"] else oracle.dispatch(idx, N, None)
+        for key in ("offsets", "perm", "slot"):
+            assert np.array_equal(none[key], base[key])
+        assert np.array_equal(none["idx"], idx) and none["n_rerouted"] == 0
+    r = oracle.reroute(d, idx, gate, fb_idx, fb_gate, N, C)
+    assert r["n_rerouted"] > 0 and r["n_dropped"] < d["n_dropped"]
+    assert r["n_dropped"] + r["perm"].size == T * k
+    assert (np.diff(r["offsets"]) <= C).all()
+    for t in range(T):
+        assert len(set(r["idx"][t])) == k
+        for j in range(k):
+            if r["idx"][t, j] != idx[t, j]:
+                rr = list(fb_idx[t]).index(r["idx"][t, j])
+                assert r["gate"][t, j] == fb_gate[t, rr]
+                assert d["slot"][t * k + j] < 0 <= r["slot"][t * k + j]
+    assert np.array_equal(r["slot"][r["perm"]], np.arange(r["perm"].size))
+    for e in range(N):
+        kept = d["perm"][d["offsets"][e]:d["offsets"][e + 1]]
+        assert np.array_equal(r["perm"][r["offsets"][e]:r["offsets"][e] + kept.size], kept)
+        rows = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]
+        assert (r["idx"].reshape(-1)[rows] == e).all()
+
+
+def test_reroute_layer_matches_dense_gates():
+    """The layer with rerouting equals the dense formulation of its final
+    routing: y[t] = sum over assignments that end in a row of
+    gate[t, j] * MLP_{idx[t, j]}(x[t]), every expert run on every token."""
+    from workloads import get_config, generate, scaled_config
+    cfg = scaled_config(get_config("c1"), T=96)
+    inp = generate(cfg)
+    C = oracle.capacity(cfg.T, cfg.k, cfg.N, 1.0)
+    out = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, capacity_slots=C, n_fallback=2)
+    assert out["n_rerouted"] > 0 and out["n_dropped"] > 0
+    X = oracle.f64(inp["x"])
+    Yall = np.stack([oracle.expert_mlp(X, cfg.act, w1=inp["w1"][e], b1=inp["b1"][e], w2=inp["w2"][e],
+                                       b2=inp["b2"][e]) for e in range(cfg.N)])
+    y = np.zeros_like(X)
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            if out["slot"][t * cfg.k + j] >= 0:
+                y[t] += out["gate"][t, j] * Yall[out["idx"][t, j], t]
+    assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-12)
