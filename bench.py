@@ -92,6 +92,9 @@ def parse():
                     help="capacity priority: token order, or (choice, token) (MOE_SLOT_MAJOR)")
     ap.add_argument("--router-stats", action="store_true",
                     help="also compute the router's load statistics (moe_route_stats + moe_router_stats)")
+    ap.add_argument("--reroute", type=int, default=0, metavar="R",
+                    help="send overflow to the next-best experts with room over R levels "
+                         "(moe_route_fallback + moe_dispatch_reroute)")
     ap.add_argument("--expert-shard", type=int, default=1, metavar="G",
                     help="time one GPU's share of an expert-sharded layer: every expert's hidden dim F/G "
                          "(a column block of w1/w3 and the matching row block of w2), all tokens")
@@ -238,6 +241,11 @@ def main():
     y_perm = torch.empty(shape.group_rows, cfg.D, dtype=shape.torch_dtype, device=dev)
     st = torch.cuda.current_stream()
     rstats = args.router_stats
+    if args.reroute and rstats:
+        raise SystemExit("--reroute and --router-stats are separate router variants")
+    if args.reroute:
+        fb_idx = torch.empty(cfg.T, args.reroute, dtype=torch.int32, device=dev)
+        fb_gate = torch.empty(cfg.T, args.reroute, dtype=torch.float32, device=dev)
     if rstats:
         stats_ws = torch.empty(api.stats_workspace_bytes(shape), dtype=torch.uint8, device=dev)
         prob_mean = torch.empty(cfg.N, dtype=torch.float64, device=dev)
@@ -250,9 +258,16 @@ def main():
         if rstats:
             api.route_stats(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate,
                             stats_ws, None, s)
+        elif args.reroute:
+            api.route_fallback(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate,
+                               args.reroute, fb_idx, fb_gate, None, s)
         else:
             api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s)
-        api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
+        if args.reroute:
+            api.dispatch_reroute(shape, args.reroute, fb_idx, fb_gate, buf.topk_idx, buf.topk_gate, buf.counts,
+                                 buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
+        else:
+            api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
         if rstats:
             api.router_stats(shape, stats_ws, buf.counts, buf.n_dropped, prob_mean, frac, summary, s)
         if ev is not None:
@@ -292,6 +307,9 @@ def main():
     counts = buf.counts.cpu()
     # useful rows and experts (the padded layout's padding rows are excluded)
     kept_r = counts.clamp(max=shape.capacity) if shape.capacity >= 0 else counts
+    if args.reroute:  # rows per expert: kept plus rerouted (compact layout)
+        off = buf.offsets.cpu()
+        kept_r = off[cfg.n_shared + 1:] - off[cfg.n_shared:-1]
     n_sh = cfg.n_shared if cfg.T > 0 else 0
     kept = cfg.n_shared * cfg.T + int(kept_r.sum())
     used = n_sh + int((kept_r > 0).sum())
@@ -363,7 +381,8 @@ def main():
                    "top_k": cfg.k, "act": cfg.act, "capacity_factor": cfg.cf,
                    "capacity": shape.capacity, "renorm": cfg.renorm, "residual": cfg.residual,
                    "capacity_priority": args.priority, "layout": args.layout,
-                   "router_stats": args.router_stats, "expert_shard": args.expert_shard, "input_copies": R},
+                   "router_stats": args.router_stats, "reroute_levels": args.reroute,
+                   "expert_shard": args.expert_shard, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "stages_ms": stages,
@@ -381,7 +400,7 @@ def main():
             "frac": achieved / peak,
             "traffic": (measured_traffic(args.workload, launch)
                         if args.cf is None and args.priority == "token" and args.layout == "compact"
-                        and args.expert_shard == 1 else None),
+                        and args.expert_shard == 1 and not args.reroute else None),
             "launch_ms": stages[launch],
             "algorithmic": {"flops": flops, "bytes": bytes_,
                             "rule": "used experts' weights once + activation rows in once + "

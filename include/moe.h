@@ -202,6 +202,49 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* count
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                  moe_stream_t stream);
 
+/* Overflow fallback. The notebook's "What" section sends capacity overflow
+ * to a fallback path. The first page's tuning tricks reroute rejected tokens
+ * to less busy experts. Two calls implement this with R = n_fallback levels.
+ * R must be >= 1 (MOE_ERR_INVALID_ARG otherwise). k + R must not exceed
+ * min(8, N), and the layout must be compact, not MOE_PADDED; otherwise the
+ * call returns MOE_ERR_UNSUPPORTED. T = 0 is a no-op.
+ *
+ * moe_route_fallback does what moe_route does, with identical idx. It also
+ * writes each token's experts of rank k .. k+R-1 in the same order. Its
+ * near-tie test covers the top k+R+1, so more tokens may be re-ranked from
+ * fp64 logits. Such a token's gates equal moe_route's only up to fp32
+ * rounding. The fallback outputs are:
+ *   fb_idx [T, R] int32 receives those experts.
+ *   fb_gate [T, R] fp32 receives their softmax probabilities. With
+ *     MOE_RENORM they are divided by the same sum over the k choices as the
+ *     gates.
+ *
+ * moe_dispatch_reroute does what moe_dispatch does, then runs R levels.
+ * At level r:
+ *   - every token with a dropped assignment left offers its lowest-j one to
+ *     expert fb_idx[t, r];
+ *   - each expert accepts offers in increasing token order while its rows
+ *     stay within the capacity;
+ *   - for an accepted assignment, topk_idx[t, j] and topk_gate[t, j]
+ *     (in/out) are rewritten to that expert and fb_gate[t, r].
+ * Results:
+ *   - Expert e's rows are its kept assignments in priority order, then the
+ *     rerouted ones in (level, token) order. offsets, perm and slot describe
+ *     the final rows.
+ *   - n_dropped counts what stays dropped. counts keeps the routed counts
+ *     before the capacity cut.
+ *   - Entries of perm past offsets[S+N] are unspecified: they serve as
+ *     scratch.
+ * The expert calls and moe_combine then take the rewritten topk_gate. */
+int moe_route_fallback(const moe_shape* shape, const void* x, const void* w_router,
+                       const float* b_router, int32_t* topk_idx, float* topk_gate,
+                       int32_t n_fallback, int32_t* fb_idx, float* fb_gate, float* logits_opt,
+                       moe_stream_t stream);
+int moe_dispatch_reroute(const moe_shape* shape, int32_t n_fallback, const int32_t* fb_idx,
+                         const float* fb_gate, int32_t* topk_idx, float* topk_gate,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot,
+                         int32_t* n_dropped, moe_stream_t stream);
+
 /* Expert MLPs on the grouped rows: for every expert e and every row r in
  * [offsets[e], offsets[e+1]), token t = perm[r] / k,
  *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [T*k, D];

@@ -31,7 +31,8 @@ MOE_PADDED = 64
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_stats_workspace_bytes",
-            "moe_route_stats", "moe_router_stats", "moe_status_string")
+            "moe_route_stats", "moe_router_stats", "moe_route_fallback", "moe_dispatch_reroute",
+            "moe_status_string")
 
 
 class MoeShapeC(ctypes.Structure):
@@ -59,6 +60,10 @@ _SIGS = {
     "moe_route_stats": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_router_stats": (ctypes.c_int, [_shape_p, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_dispatch": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_fallback": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
+                                          _vp]),
+    "moe_dispatch_reroute": (ctypes.c_int, [_shape_p, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp]),
     "moe_expert_ffn": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
     "moe_expert_up": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,

@@ -146,6 +146,28 @@ def router_stats(shape: MoeShape, stats_ws, counts, n_dropped, prob_mean, frac, 
         _ptr(summary, f64, "summary"), _stream(stream)))
 
 
+def route_fallback(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, n_fallback, fb_idx, fb_gate,
+                   logits=None, stream=None):
+    dt = shape.torch_dtype
+    sc = shape.c()
+    _check("moe_route_fallback", L.load().moe_route_fallback(
+        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_gate, torch.float32, "topk_gate"), int(n_fallback), _ptr(fb_idx, torch.int32, "fb_idx"),
+        _ptr(fb_gate, torch.float32, "fb_gate"), _ptr(logits, torch.float32, "logits"), _stream(stream)))
+
+
+def dispatch_reroute(shape: MoeShape, n_fallback, fb_idx, fb_gate, topk_idx, topk_gate, counts, offsets, perm,
+                     slot, n_dropped, stream=None):
+    i32 = torch.int32
+    sc = shape.c()
+    _check("moe_dispatch_reroute", L.load().moe_dispatch_reroute(
+        ctypes.byref(sc), int(n_fallback), _ptr(fb_idx, i32, "fb_idx"), _ptr(fb_gate, torch.float32, "fb_gate"),
+        _ptr(topk_idx, i32, "topk_idx"), _ptr(topk_gate, torch.float32, "topk_gate"),
+        _ptr(counts, i32, "counts"), _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"),
+        _ptr(slot, i32, "slot"), _ptr(n_dropped, i32, "n_dropped"), _stream(stream)))
+
+
 def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None):
     i32 = torch.int32
     sc = shape.c()

@@ -26,6 +26,18 @@
 // shifted by S*T.  In the padded layout expert e's rows start at S*T + e*C
 // and its C - kept padding rows get perm = 0 (a valid gather row whose
 // output nobody reads).
+//
+// Rerouting (R fallback levels, compact layout): C only records provisional
+// rows in slot.  Then, level r = 0 .. R-1: every token with a dropped
+// assignment left offers its lowest-j one to its expert of rank k + r
+// (fb_idx[t, r]); the offers are ranked per expert in token order with the
+// ballot scheme of A over 16 token segments (in-wave ranks parked in the
+// routed perm rows, not yet written), and the first `room` of each expert are
+// accepted: idx and gate of the assignment are rewritten and slot holds
+// -2 - (its place among the expert's rerouted rows).  Finally the offsets
+// are the scan of kept + rerouted, and one pass over the assignments writes
+// the final slot and perm (kept rows first, then rerouted ones in level and
+// token order).
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,14 +54,62 @@ __device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
   return (i - j * T) * k + j;
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __restrict__ idx,
-                                                            int64_t A, int64_t T, int k, int by_choice,
-                                                            int N, int C, int S, int pad,
+// Rank of each valid lane among the lanes of its wave holding the same
+// expert e (lanes below it), plus the wave's running count of e in cnt,
+// which the lowest such lane advances.  Every lane reads the count before
+// the leader writes it; all lanes of the wave take part.
+__device__ inline int wave_rank(bool valid, int e, int bits, uint64_t lt_mask, int* cnt) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    same &= bit ? bb : ~bb;
+  }
+  int rank = 0;
+  if (valid) {
+    const int below = __popcll(same & lt_mask);
+    const int base = cnt[e];
+    if (below == 0) cnt[e] = base + __popcll(same);
+    rank = base + below;
+  }
+  return rank;
+}
+
+// Exclusive scan over the waves of each expert's wave counts (in place:
+// wcnt[w][e] becomes wave w's base); tot[e] = the expert's total.
+__device__ inline void wave_bases(int (*wcnt)[kMaxExperts], int* tot, int N, int tid) {
+  if (tid < N) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = run;
+      run += c;
+    }
+    tot[tid] = run;
+  }
+}
+
+// Inclusive scan of v[0..N) in place (all threads call it).
+__device__ inline void block_scan(int* v, int N, int tid) {
+  for (int d = 1; d < kMaxExperts; d <<= 1) {
+    int x = 0;
+    if (tid < N && tid >= d) x = v[tid - d];
+    __syncthreads();
+    if (tid < N && tid >= d) v[tid] += x;
+    __syncthreads();
+  }
+}
+
+template <bool REROUTE>
+__global__ __launch_bounds__(kThreads) void dispatch_kernel(int32_t* idx, int64_t A, int64_t T, int k,
+                                                            int by_choice, int N, int C, int S, int pad,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ slot,
-                                                            int32_t* __restrict__ n_dropped) {
+                                                            int32_t* __restrict__ n_dropped, int R,
+                                                            const int32_t* __restrict__ fb_idx,
+                                                            const float* __restrict__ fb_gate, float* gate) {
   __shared__ int wcnt[kWaves][kMaxExperts];  // A: running counts; then wave bases
   __shared__ int scan[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
@@ -82,43 +142,25 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
       const int64_t a = flat_of(i, T, k, by_choice);
       const int e = ev[c];
       const bool valid = i < a_end && e >= 0 && e < N;
-      uint64_t same = __ballot(valid);
-      for (int b = 0; b < bits; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
-        const uint64_t bb = __ballot(bit);
-        same &= bit ? bb : ~bb;
-      }
-      if (valid) {
-        const int below = __popcll(same & lt_mask);
-        const int base = wcnt[wave][e];  // every lane reads before the leader writes
-        if (below == 0) wcnt[wave][e] = base + __popcll(same);
-        slot[a] = base + below;
-      }
+      const int rank = wave_rank(valid, e, bits, lt_mask, wcnt[wave]);
+      if (valid) slot[a] = rank;
     }
   }
   __syncthreads();
 
   // ---- B: wave bases per expert, totals, capacity cut, offsets
+  __shared__ int keep[kMaxExperts];
+  wave_bases(wcnt, scan, N, tid);
   int kept = 0;
   if (tid < N) {
-    int run = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = wcnt[w][tid];
-      wcnt[w][tid] = run;
-      run += c;
-    }
+    const int run = scan[tid];
     counts[tid] = run;
     kept = (C >= 0 && run > C) ? C : run;
     scan[tid] = kept;
+    keep[tid] = kept;
   }
   __syncthreads();
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
-    int v = 0;
-    if (tid < N && tid >= d) v = scan[tid - d];
-    __syncthreads();
-    if (tid < N && tid >= d) scan[tid] += v;
-    __syncthreads();
-  }
+  block_scan(scan, N, tid);
   const int ST = S * (int)T;  // rows of the shared experts, in front
   if (tid < N) {
     const int o = ST + (pad ? tid * C : scan[tid] - kept);
@@ -168,9 +210,138 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(const int32_t* __res
       if (C < 0 || rank < C) {
         const int s = off[e] + rank;
         slot[a] = s;
-        perm[s] = (int32_t)a;
+        if constexpr (!REROUTE) perm[s] = (int32_t)a;
       } else {
         slot[a] = -1;
+      }
+    }
+  }
+  if constexpr (REROUTE) {
+    __shared__ int room[kMaxExperts], rer[kMaxExperts], tot[kMaxExperts], offf[kMaxExperts + 1];
+    __syncthreads();  // every wave is done with C's wave bases (wcnt) and slot writes
+    if (tid < N) {
+      room[tid] = C >= 0 ? C - keep[tid] : 0;
+      rer[tid] = 0;
+    }
+    // token segments of the waves, in whole 64-wide chunks
+    const int64_t tchunks = (T + kWave - 1) / kWave;
+    const int64_t tper = (tchunks + kWaves - 1) / kWaves;
+    const int64_t t_begin = (int64_t)wave * tper * kWave;
+    const int64_t t_end = (t_begin + tper * kWave < T) ? t_begin + tper * kWave : T;
+    // scratch in the routed perm rows (T*k >= T entries, >= 2T when k >= 2),
+    // rewritten by the final pass: in-wave ranks of the offers, and with
+    // k >= 2 each token's mask of still-dropped choices (with k = 1 the slot
+    // itself says whether the one choice is dropped)
+    int32_t* parked = perm + (int64_t)S * T;
+    int32_t* dmask = parked + T;
+    if (k > 1) {
+      for (int64_t t = tid; t < T; t += kThreads) {
+        int m = 0;
+        for (int j = 0; j < k; ++j) m |= (slot[t * k + j] == -1) ? (1 << j) : 0;
+        dmask[t] = m;
+      }
+    }
+    // the offers of a chunk group: lowest still-dropped choice jd[c] of token
+    // t0 + c*64 + lane and its expert of rank k + r (-1: no offer); all loads
+    // are issued before any is used
+    auto offers = [&](int64_t t0, int r, int (&jd)[kPrefetch], int (&ev)[kPrefetch]) {
+      int dv[kPrefetch], fv[kPrefetch];
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t t = t0 + c * kWave + lane;
+        const int64_t tc = t < t_end ? t : t_begin;  // in range: t_begin < t_end here
+        dv[c] = k > 1 ? dmask[tc] : (slot[tc] == -1 ? 1 : 0);
+        fv[c] = fb_idx[tc * R + r];
+      }
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t t = t0 + c * kWave + lane;
+        const bool has = t < t_end && dv[c] != 0;
+        jd[c] = has ? __builtin_ctz((unsigned)dv[c]) : -1;
+        ev[c] = has ? fv[c] : -1;
+      }
+    };
+    for (int r = 0; r < (C >= 0 ? R : 0); ++r) {
+      for (int i = tid; i < kWaves * kMaxExperts; i += kThreads) (&wcnt[0][0])[i] = 0;
+      __syncthreads();  // also orders the previous level's writes before these reads
+      for (int64_t t0 = t_begin; t0 < t_end; t0 += kPrefetch * kWave) {
+        int jd[kPrefetch], ev[kPrefetch];
+        offers(t0, r, jd, ev);
+#pragma unroll
+        for (int c = 0; c < kPrefetch; ++c) {
+          const int e = ev[c];
+          const bool valid = e >= 0 && e < N;
+          const int rank = wave_rank(valid, e, bits, lt_mask, wcnt[wave]);
+          if (valid) parked[t0 + c * kWave + lane] = rank;
+        }
+      }
+      __syncthreads();
+      wave_bases(wcnt, tot, N, tid);
+      __syncthreads();
+      for (int64_t t0 = t_begin; t0 < t_end; t0 += kPrefetch * kWave) {
+        int jd[kPrefetch], ev[kPrefetch], pv[kPrefetch];
+        offers(t0, r, jd, ev);
+#pragma unroll
+        for (int c = 0; c < kPrefetch; ++c) {
+          const int64_t t = t0 + c * kWave + lane;
+          pv[c] = parked[t < t_end ? t : t_begin];
+        }
+#pragma unroll
+        for (int c = 0; c < kPrefetch; ++c) {
+          const int e = ev[c];
+          if (e < 0 || e >= N) continue;
+          const int64_t t = t0 + c * kWave + lane;
+          const int rank = wcnt[wave][e] + pv[c];
+          if (rank < room[e]) {
+            const int64_t a = t * k + jd[c];
+            slot[a] = -2 - (rer[e] + rank);
+            idx[a] = e;
+            gate[a] = fb_gate[t * R + r];
+            if (k > 1) dmask[t] &= ~(1 << jd[c]);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < N) {
+        const int acc = tot[tid] < room[tid] ? tot[tid] : room[tid];
+        rer[tid] += acc;
+        room[tid] -= acc;
+      }
+    }
+    __syncthreads();
+    // final offsets: scan of kept + rerouted rows
+    if (tid < N) scan[tid] = keep[tid] + rer[tid];
+    __syncthreads();
+    block_scan(scan, N, tid);
+    if (tid < N) {
+      const int o = ST + scan[tid] - (keep[tid] + rer[tid]);
+      offf[tid] = o;
+      offsets[S + tid] = o;
+    }
+    if (tid == 0) {
+      const int total = N > 0 ? scan[N - 1] : 0;
+      offsets[S + N] = ST + total;
+      *n_dropped = (int32_t)(A - total);
+    }
+    __syncthreads();
+    // final rows: kept ones keep their rank, rerouted ones follow
+    for (int64_t a0 = tid; a0 < A; a0 += kPrefetch * kThreads) {
+      int sv[kPrefetch], ev[kPrefetch];
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t a = a0 + c * kThreads;
+        const int64_t ac = a < A ? a : a0;
+        sv[c] = slot[ac];
+        ev[c] = idx[ac];
+      }
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t a = a0 + c * kThreads;
+        const int e = ev[c];
+        if (a >= A || sv[c] == -1 || e < 0 || e >= N) continue;
+        const int row = sv[c] >= 0 ? offf[e] + (sv[c] - off[e]) : offf[e] + keep[e] + (-2 - sv[c]);
+        slot[a] = row;
+        perm[row] = (int32_t)a;
       }
     }
   }
@@ -183,9 +354,20 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
                            hipStream_t st) {
   const int64_t A = s.T * (int64_t)s.k;
   const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
-                     s.capacity, s.n_shared, (s.flags & MOE_PADDED) ? 1 : 0, counts, offsets, perm, slot,
-                     n_dropped);
+  // the plain dispatch never writes idx
+  hipLaunchKernelGGL(dispatch_kernel<false>, dim3(1), dim3(kThreads), 0, st, const_cast<int32_t*>(idx), A, s.T,
+                     s.k, by_choice, s.N, s.capacity, s.n_shared, (s.flags & MOE_PADDED) ? 1 : 0, counts, offsets,
+                     perm, slot, n_dropped, 0, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_reroute(const moe_shape& s, int R, const int32_t* fb_idx, const float* fb_gate,
+                                   int32_t* idx, float* gate, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                   int32_t* slot, int32_t* n_dropped, hipStream_t st) {
+  const int64_t A = s.T * (int64_t)s.k;
+  const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
+  hipLaunchKernelGGL(dispatch_kernel<true>, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
+                     s.capacity, s.n_shared, 0, counts, offsets, perm, slot, n_dropped, R, fb_idx, fb_gate, gate);
   return hipGetLastError();
 }
 

@@ -196,8 +196,8 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router, const
   if (s.T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, nullptr,
-                                 (hipStream_t)stream));
+  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, nullptr, 0,
+                                 nullptr, nullptr, (hipStream_t)stream));
 }
 
 static size_t stats_ws_bytes(const moe_shape& s) {
@@ -225,7 +225,7 @@ int moe_route_stats(const moe_shape* shape, const void* x, const void* w_router,
   if (!stats_ws || stats_ws_bytes_ < stats_ws_bytes(s)) return MOE_ERR_WORKSPACE;
   if ((uintptr_t)stats_ws % kAlign) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt,
-                                 (float*)stats_ws, (hipStream_t)stream));
+                                 (float*)stats_ws, 0, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_ws_bytes_,
@@ -240,6 +240,43 @@ int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_
   if ((uintptr_t)stats_ws % kAlign) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_router_stats(s, (const float*)stats_ws, counts, n_dropped, prob_mean, frac,
                                         summary, (hipStream_t)stream));
+}
+
+// Fallback ranks: 1 <= R and k + R <= min(8, N); rerouting needs the
+// compact layout.
+static int check_fallback(const moe_shape& s, int32_t R) {
+  if (R < 1) return MOE_ERR_INVALID_ARG;
+  if (s.k + R > kMaxTopK || s.k + R > s.N) return MOE_ERR_UNSUPPORTED;
+  if (s.flags & MOE_PADDED) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_route_fallback(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                       int32_t* topk_idx, float* topk_gate, int32_t n_fallback, int32_t* fb_idx, float* fb_gate,
+                       float* logits_opt, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((v = check_fallback(s, n_fallback)) != MOE_OK) return v;
+  if (s.T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate || !fb_idx || !fb_gate) return MOE_ERR_INVALID_ARG;
+  if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, nullptr, n_fallback,
+                                 fb_idx, fb_gate, (hipStream_t)stream));
+}
+
+int moe_dispatch_reroute(const moe_shape* shape, int32_t n_fallback, const int32_t* fb_idx, const float* fb_gate,
+                         int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* slot, int32_t* n_dropped, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const moe_shape& s = *shape;
+  if ((v = check_fallback(s, n_fallback)) != MOE_OK) return v;
+  if (s.T == 0) return MOE_OK;
+  if (!fb_idx || !fb_gate || !topk_idx || !topk_gate || !counts || !offsets || !perm || !slot || !n_dropped)
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_dispatch_reroute(s, n_fallback, fb_idx, fb_gate, topk_idx, topk_gate, counts, offsets,
+                                            perm, slot, n_dropped, (hipStream_t)stream));
 }
 
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -338,7 +375,8 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   hipStream_t st = (hipStream_t)stream;
   void* y_perm = ws;
   void* ffn_ws = (unsigned char*)ws + align_up((size_t)group_rows(s) * s.D * elem_size(s));
-  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, st);
+  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, 0, nullptr,
+                              nullptr, st);
   if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool decode = use_decode(s);

@@ -30,7 +30,8 @@ int device_cu_count();
 
 // ---- launchers (stream-ordered, no synchronisation, return hipError_t) ----
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,
-                        int32_t* idx, float* gate, float* logits, float* prob_part, hipStream_t st);
+                        int32_t* idx, float* gate, float* logits, float* prob_part, int R, int32_t* fb_idx,
+                        float* fb_gate, hipStream_t st);
 
 // Router blocks of a launch (tokens per block depend on the shape and the
 // device's CU count); prob_part holds N * route_blocks(s) floats.
@@ -44,6 +45,11 @@ hipError_t launch_router_stats(const moe_shape& s, const float* prob_part, const
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                            hipStream_t st);
+// Dispatch with R levels of overflow rerouting (compact layout); rewrites
+// idx and gate of the rerouted assignments.
+hipError_t launch_dispatch_reroute(const moe_shape& s, int R, const int32_t* fb_idx, const float* fb_gate,
+                                   int32_t* idx, float* gate, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                   int32_t* slot, int32_t* n_dropped, hipStream_t st);
 
 // Grouped GEMM over experts:  C[r, n] = act(sum_k A[row(r), k] * B[e, n, k] + bias[e, n])
 // for r in [offsets[e], offsets[e+1]).  row(r) = perm[r] / topk when perm is

@@ -17,6 +17,9 @@
 //     are exact in fp64).  Near-ties are rare: a handful of tokens per batch.
 //  4. Gates are softmax probabilities of the chosen experts, optionally
 //     renormalised over the k choices.
+// With R fallback ranks the same steps select the top k + R (the near-tie
+// test then covers the top k + R + 1): ranks k .. k+R-1 go to fb_idx and
+// fb_gate, their gates scaled like the k gates.
 #include <float.h>
 #include <limits.h>
 
@@ -35,6 +38,9 @@ struct RouteArgs {
   int32_t* idx;
   float* gate;
   float* logits;
+  int R;            // fallback ranks after the k choices (0 = none)
+  int32_t* fb_idx;  // [T, R]: experts of ranks k .. k+R-1
+  float* fb_gate;   // [T, R]: their gates, scaled like the k gates
   float* prob_part;  // optional: [N][blocks] per-block probability sums
   unsigned long long* stats_ticket;  // with prob_part: cleared by block 0
 };
@@ -60,14 +66,14 @@ __device__ inline float vexp(float v) { return expf(v); }
 template <typename V, int NV>
 __device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, int64_t t, int l16, V margin,
                                            bool force, bool stats, V (&pacc)[NV]) {
-  const int N = a.N, k = a.k;
+  const int N = a.N, k = a.k, KS = a.k + a.R;  // ranks to select
   V v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     int e = l16 + 16 * i;
     v[i] = (e < N) ? vals[e] : neg_inf<V>();
   }
-  const int nsel = (k + 1 <= N) ? k + 1 : N;
+  const int nsel = (KS + 1 <= N) ? KS + 1 : N;
   V tv[kMaxTopK + 1];
   int ti[kMaxTopK + 1];
   uint32_t taken = 0;
@@ -99,7 +105,7 @@ __device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, in
     }
   }
   bool ok = true;
-  const int ngap = (k < N - 1) ? k : N - 1;
+  const int ngap = (KS < N - 1) ? KS : N - 1;
 #pragma unroll
   for (int r = 0; r < kMaxTopK; ++r)
     if (r < ngap) ok = ok && (tv[r] - tv[r + 1] >= margin);
@@ -127,14 +133,18 @@ __device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, in
     V ps = 0;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      p[j] = (j < k) ? vexp(tv[j] - vmax) / s : V(0);
-      ps += p[j];
+      p[j] = (j < KS) ? vexp(tv[j] - vmax) / s : V(0);
+      if (j < k) ps += p[j];
     }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
+      const float g = (float)(a.renorm ? p[j] / ps : p[j]);
       if (j < k) {
         a.idx[t * k + j] = ti[j];
-        a.gate[t * k + j] = (float)(a.renorm ? p[j] / ps : p[j]);
+        a.gate[t * k + j] = g;
+      } else if (j < KS) {
+        a.fb_idx[t * a.R + (j - k)] = ti[j];
+        a.fb_gate[t * a.R + (j - k)] = g;
       }
     }
   }
@@ -271,15 +281,15 @@ template <typename T, int NJ>
 __device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t t, int lane) {
   constexpr int W = Chunk<T>::W;
   typedef typename Chunk<T>::type V;
-  const int N = a.N, k = a.k, D = a.D;
+  const int N = a.N, k = a.k, D = a.D, KS = a.k + a.R;
   float v[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     v[j] = (e < N) ? lgrow[e] : -FLT_MAX;
   }
-  // the (k+1)-th largest fp32 logit (or the N-th when k = N)
-  const int nsel = (k + 1 <= N) ? k + 1 : N;
+  // the (KS+1)-th largest fp32 logit (or the N-th when KS = N)
+  const int nsel = (KS + 1 <= N) ? KS + 1 : N;
   uint32_t taken = 0;
   float vk = 0.f;
 #pragma unroll
@@ -357,11 +367,11 @@ __device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t 
       if (lane == l) ex[j] = sum;
     }
   }
-  // top k of the candidates by exact logit; lane r keeps round r's choice
+  // top KS of the candidates by exact logit; lane r keeps round r's choice
   int my_i = 0;
   double my_v = 0.0;
   uint32_t used = 0;
-  for (int r = 0; r < k; ++r) {
+  for (int r = 0; r < KS; ++r) {
     double bv = -DBL_MAX;
     int bi = INT_MAX;
 #pragma unroll
@@ -396,13 +406,17 @@ __device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t 
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  const double p = (lane < k) ? exp(my_v - vmax) / s : 0.0;
-  double ps = p;
+  const double p = (lane < KS) ? exp(my_v - vmax) / s : 0.0;
+  double ps = (lane < k) ? p : 0.0;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+  const float g = (float)(a.renorm ? p / ps : p);
   if (lane < k) {
     a.idx[t * k + lane] = my_i;
-    a.gate[t * k + lane] = (float)(a.renorm ? p / ps : p);
+    a.gate[t * k + lane] = g;
+  } else if (lane < KS) {
+    a.fb_idx[t * a.R + (lane - k)] = my_i;
+    a.fb_gate[t * a.R + (lane - k)] = g;
   }
   if (a.logits) {
 #pragma unroll
@@ -795,7 +809,8 @@ hipError_t launch_router_stats(const moe_shape& s, const float* part, const int3
 }
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,
-                        int32_t* idx, float* gate, float* logits, float* prob_part, hipStream_t st) {
+                        int32_t* idx, float* gate, float* logits, float* prob_part, int R, int32_t* fb_idx,
+                        float* fb_gate, hipStream_t st) {
   RouteArgs a;
   a.x = x;
   a.wr = wr;
@@ -809,6 +824,9 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const
   a.idx = idx;
   a.gate = gate;
   a.logits = logits;
+  a.R = R;
+  a.fb_idx = fb_idx;
+  a.fb_gate = fb_gate;
   a.prob_part = prob_part;
   a.stats_ticket = prob_part ? stats_ticket(s, prob_part) : nullptr;
   const int rows = route_rows_per_block(s);

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-              "moe_combine", "moe_forward", "moe_route_stats", "moe_router_stats",
+              "moe_combine", "moe_forward", "moe_route_stats", "moe_router_stats", "moe_route_fallback",
+              "moe_dispatch_reroute",
               "moe_capacity", "moe_workspace_bytes", "moe_stats_workspace_bytes", "moe_status_string"):
         assert n in names
 
@@ -157,6 +158,24 @@ def test_stats_workspace_bytes_and_validation(lib):
     z = ctypes.byref(_shape(T=0))
     assert lib.moe_route_stats(z, fake, fake, None, fake, fake, None, None, 0, None) == L.MOE_OK
     assert lib.moe_router_stats(z, None, 0, fake, fake, fake, None, fake, None) == L.MOE_OK
+
+
+def test_reroute_entry_points_validate(lib):
+    """Fallback depth R: >= 1, k + R <= min(8, N); compact layout only;
+    T = 0 is a no-op once the arguments are valid."""
+    from mixture_experts_layer_expert_amd import _lib as L
+    fake = ctypes.c_void_p(0x1000)
+    s = ctypes.byref(_shape(k=2, N=8, capacity=10))
+    route = lambda sh, R, fb=fake: lib.moe_route_fallback(sh, fake, fake, None, fake, fake, R, fb, fb, None, None)
+    disp = lambda sh, R, fb=fake: lib.moe_dispatch_reroute(sh, R, fb, fb, fake, fake, fake, fake, fake, fake, fake,
+                                                           None)
+    for f in (route, disp):
+        assert f(s, 0) == L.MOE_ERR_INVALID_ARG
+        assert f(s, 7) == L.MOE_ERR_UNSUPPORTED  # k + R = 9 > 8
+        assert f(ctypes.byref(_shape(k=2, N=3, capacity=10)), 2) == L.MOE_ERR_UNSUPPORTED  # k + R > N
+        assert f(ctypes.byref(_shape(k=2, N=8, capacity=10, flags=L.MOE_PADDED)), 1) == L.MOE_ERR_UNSUPPORTED
+        assert f(s, 2, None) == L.MOE_ERR_INVALID_ARG
+        assert f(ctypes.byref(_shape(T=0, k=2, N=8, capacity=10)), 2) == L.MOE_OK
 
 
 def test_entry_points_reject_null_pointers_before_launch(lib):

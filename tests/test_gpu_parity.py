@@ -234,7 +234,8 @@ def _rand_idx(rng, T, N, k, p=None):
 
 @pytest.mark.parametrize("T,N,k,C", [
     (1, 1, 1, None), (1, 4, 4, None), (777, 8, 2, None), (777, 8, 2, 150), (2000, 128, 1, 15),
-    (2000, 128, 1, 0), (3001, 16, 2, 1), (5000, 64, 6, None), (16384, 128, 1, 128), (40000, 256, 2, 300),
+    (2000, 128, 1, 0), (3001, 16, 2, 1), (5000, 64, 6, None), (5000, 64, 6, 50), (5000, 64, 6, 480),
+    (16384, 128, 1, 128), (40000, 256, 2, 300),
 ])
 def test_dispatch_random(gpu, T, N, k, C):
     rng = np.random.default_rng(T + N + k)
@@ -477,6 +478,132 @@ def test_forward_padded_layout(gpu, key, T, cf):
     compact = run_forward(cfg, g)
     y_c = compact.out.float().cpu().numpy().astype(np.float64)
     assert row_rel_err(y, y_c) <= TOL[cfg.dtype]
+
+
+# ------------------------------------------------ overflow rerouting
+FALLBACK_R = {"c1": 3, "c2": 2, "c3": 2, "c4": 2, "c5": 2, "c6": 2}
+
+
+@pytest.mark.parametrize("key", sorted(CONFIGS))
+def test_route_fallback_full_size(gpu, key):
+    """moe_route_fallback: the k choices equal moe_route's (gates up to the
+    rounding of tokens that the wider near-tie test re-ranks in fp64), the R
+    fallback experts equal the oracle's ranks k .. k+R-1 exactly, their gates
+    are within the gate tolerance (scaled like the gates with renorm)."""
+    cfg = CONFIGS[key]
+    R = FALLBACK_R[key]
+    _say(f"route fallback {cfg.name} R={R}")
+    inp = generate(cfg, parts=("x", "router"))
+    g = to_gpu(inp)
+    shape = api.MoeShape.from_config(cfg)
+    i32 = dict(dtype=torch.int32, device=gpu)
+    f32 = dict(dtype=torch.float32, device=gpu)
+    idx, gate = torch.empty(cfg.T, cfg.k, **i32), torch.empty(cfg.T, cfg.k, **f32)
+    idx2, gate2 = torch.empty_like(idx), torch.empty_like(gate)
+    fb_idx, fb_gate = torch.empty(cfg.T, R, **i32), torch.empty(cfg.T, R, **f32)
+    api.route_fallback(shape, g["x"], g["w_router"], g["b_router"], idx, gate, R, fb_idx, fb_gate)
+    api.route(shape, g["x"], g["w_router"], g["b_router"], idx2, gate2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert (gate - gate2).abs().max().item() <= GATE_ATOL[cfg.dtype]
+    r = oracle.route(inp["x"], inp["w_router"], inp["b_router"], cfg.k, cfg.renorm)
+    assert np.abs(gate.cpu().numpy() - r["gate"]).max() <= GATE_ATOL[cfg.dtype]
+    want_idx, want_gate = oracle.fallback_choices(r["logits"], r["probs"], cfg.k, R, cfg.renorm)
+    assert np.array_equal(fb_idx.cpu().numpy(), want_idx)
+    assert np.abs(fb_gate.cpu().numpy() - want_gate).max() <= GATE_ATOL[cfg.dtype]
+
+
+def _reroute_case(gpu, T, N, k, C, R, seed, priority="token", n_shared=0, skew=None):
+    rng = np.random.default_rng(seed)
+    order = np.stack([rng.choice(N, size=k + R, replace=False, p=skew) for _ in range(T)])
+    idx_np, fb_np = order[:, :k], order[:, k:]
+    gate_np = rng.random((T, k)).astype(np.float32)
+    fbg_np = rng.random((T, R)).astype(np.float32)
+    shape = api.MoeShape(T=T, D=64, F=64, N=N, k=k, capacity=C, act="relu",
+                         slot_major=(priority == "choice"), n_shared=n_shared)
+    i32 = dict(dtype=torch.int32, device=gpu)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).to(gpu)
+    gate = torch.from_numpy(gate_np).to(gpu)
+    fb_idx = torch.from_numpy(fb_np.astype(np.int32)).to(gpu)
+    fb_gate = torch.from_numpy(fbg_np).to(gpu)
+    counts = torch.full((N,), -7, **i32)
+    offsets = torch.full((n_shared + N + 1,), -7, **i32)
+    perm = torch.full((shape.group_rows,), -7, **i32)
+    slot = torch.full((T * k,), -7, **i32)
+    nd = torch.full((1,), -7, **i32)
+    api.dispatch_reroute(shape, R, fb_idx, fb_gate, idx, gate, counts, offsets, perm, slot, nd)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(idx_np, N, C, priority)
+    ref = oracle.reroute(d, idx_np, gate_np.astype(np.float64), fb_np, fbg_np.astype(np.float64), N, C)
+    idx_ref, gate_ref = ref.pop("idx"), ref.pop("gate")
+    ref = oracle.with_shared(ref, T, k, n_shared)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    K = int(ref["offsets"][-1])
+    p = perm.cpu().numpy()[:K]
+    bad = np.nonzero(p != ref["perm"])[0]
+    if bad.size:
+        _say(f"{bad.size} perm rows differ, first {bad[:8].tolist()}: gpu {p[bad[:8]].tolist()} "
+             f"oracle {ref['perm'][bad[:8]].tolist()}; rerouted {ref['n_rerouted']}")
+    assert bad.size == 0
+    assert np.array_equal(slot.cpu().numpy(), ref["slot"])
+    assert int(nd.item()) == ref["n_dropped"]
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.array_equal(gate.cpu().numpy(), gate_ref.astype(np.float32))
+    return ref
+
+
+@pytest.mark.parametrize("T,N,k,C,R", [
+    (777, 8, 2, 150, 2), (2000, 128, 1, 15, 3), (3001, 16, 2, 1, 4), (5000, 64, 6, 50, 2),
+    (16384, 128, 1, 128, 2), (40000, 256, 2, 300, 2), (2000, 32, 2, 0, 2), (1, 4, 1, 0, 3), (300, 8, 1, 1000, 2),
+])
+def test_dispatch_reroute(gpu, T, N, k, C, R):
+    _reroute_case(gpu, T, N, k, C, R, seed=T + N + k + R)
+
+
+def test_dispatch_reroute_skewed_choice_and_shared(gpu):
+    """Skewed loads (many drops, few experts with room), (choice, token)
+    priority for the cut, and shared experts in front of the routed rows."""
+    N = 16
+    zipf = np.array([1.0 / (e + 1) ** 1.2 for e in range(N)])
+    zipf /= zipf.sum()
+    ref = _reroute_case(gpu, 4000, N, 2, 300, 3, seed=11, skew=zipf)
+    assert ref["n_rerouted"] > 0 and ref["n_dropped"] > 0
+    _reroute_case(gpu, 4000, N, 2, 300, 3, seed=12, priority="choice", skew=zipf)
+    _reroute_case(gpu, 3000, N, 2, 250, 2, seed=13, n_shared=2, skew=zipf)
+
+
+@pytest.mark.parametrize("key,T,cf,R", [("c2", 2048, 1.0, 2), ("c3", 1500, 1.0, 2), ("c1", None, 1.0, 3),
+                                        ("c6", 1024, 1.0, 2)])
+def test_forward_reroute(gpu, key, T, cf, R):
+    """Whole layer with rerouting through the stage entry points: routing
+    (rewritten idx and gates, rows) exact against the oracle's rerouted
+    layer, outputs within tolerance."""
+    base = get_config(key, cf=cf)
+    cfg = base if T is None else scaled_config(base, T=T)
+    _say(f"forward reroute {cfg.name}: T={cfg.T} k={cfg.k} cf={cfg.cf} R={R}")
+    inp = generate(cfg)
+    C = capacity_of(cfg)
+    ref = oracle.moe_forward(inp["x"], inp, k=cfg.k, act=cfg.act, renorm=cfg.renorm, capacity_slots=C,
+                             residual=cfg.residual, n_shared=cfg.n_shared, n_fallback=R)
+    assert ref["n_rerouted"] > 0
+    g = to_gpu(inp)
+    shape = api.MoeShape.from_config(cfg)
+    buf = api.MoeBuffers(shape)
+    i32 = dict(dtype=torch.int32, device=gpu)
+    fb_idx = torch.empty(cfg.T, R, **i32)
+    fb_gate = torch.empty(cfg.T, R, dtype=torch.float32, device=gpu)
+    h = torch.empty(shape.group_rows, cfg.F, dtype=shape.torch_dtype, device=gpu)
+    y_perm = torch.empty(shape.group_rows, cfg.D, dtype=shape.torch_dtype, device=gpu)
+    api.route_fallback(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, R, fb_idx, fb_gate)
+    api.dispatch_reroute(shape, R, fb_idx, fb_gate, buf.topk_idx, buf.topk_gate, buf.counts, buf.offsets,
+                         buf.perm, buf.slot, buf.n_dropped)
+    api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g.get("b1"), g.get("w3"), h, buf.ws)
+    api.expert_down(shape, h, buf.offsets, g["w2"], g.get("b2"), y_perm, buf.ws)
+    api.combine(shape, y_perm, buf.slot, buf.topk_gate, g["x"], buf.out)
+    torch.cuda.synchronize()
+    check_routing(buf, ref, cfg)
+    check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
 
 
 # ------------------------------------------ full-size layers, sampled rows
