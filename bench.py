@@ -51,7 +51,7 @@ CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, 
 # (--copy-calibration).  A figure is used only while the kernel sources hash
 # to the value it was measured with; otherwise traffic is null.
 PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
-                      "mixture_experts_layer_expert_amd/csrc/moe_internal.h")
+                      "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h")
 PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
     "c2": {"sources": "71a869a347bd3511",
            "fc1": {"fetch_kib": 309436.7, "write_kib": 91818.5},

@@ -51,36 +51,6 @@ hipError_t launch_dispatch_reroute(const moe_shape& s, int R, const int32_t* fb_
                                    int32_t* idx, float* gate, int32_t* counts, int32_t* offsets, int32_t* perm,
                                    int32_t* slot, int32_t* n_dropped, hipStream_t st);
 
-// Grouped GEMM over experts:  C[r, n] = act(sum_k A[row(r), k] * B[e, n, k] + bias[e, n])
-// for r in [offsets[e], offsets[e+1]).  row(r) = perm[r] / topk when perm is
-// non-null (gather of x), else r.  For SwiGLU, B = w1 and B2 = w3 and
-// C[r, n] = silu(A.w1[e,n]) * (A.w3[e,n]).
-struct GroupedGemm {
-  const void* A;
-  const int32_t* perm;
-  int topk;
-  const int32_t* offsets;
-  int n_experts;
-  int64_t a_rows;  // rows addressable in A (for clamping of tail loads)
-  const void* B;
-  const void* B2;
-  const void* bias;
-  void* C;
-  int K;
-  int n_out;
-  int act;      // GemmAct
-  float* part;  // bf16 path: workspace for split-K partial tiles, or nullptr
-};
-
-// Picks the bf16 MFMA tile configuration from the expected rows per expert.
-// With g.part, a partial last round of tiles is split along K into that
-// workspace and finished by a second launch.
-hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows_per_expert,
-                                    hipStream_t st);
-// Bytes of g.part the bf16 grouped GEMM may use (both projections).
-size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows_per_expert);
-hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st);
-
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t* slot,
                           const float* gate, const void* x_res, void* out, hipStream_t st);
 
@@ -101,3 +71,5 @@ hipError_t launch_combine_shards(const moe_shape& s, const float* part, int n_sh
                                  hipStream_t st);
 
 }  // namespace moe
+
+#include "grouped_gemm.h"
