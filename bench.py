@@ -53,29 +53,35 @@ CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, 
 PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
                       "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h")
 PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
-    "c2": {"sources": "71a869a347bd3511",
-           "fc1": {"fetch_kib": 309436.7, "write_kib": 91818.5},
+    "c2": {"sources": "e32a9db052f7d51f",
+           "fc1": {"fetch_kib": 309450.9, "write_kib": 91805.1},
            # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 0, 3>
-           "fc2": {"fetch_kib": 389921.7, "write_kib": 55726.7},
+           "fc2": {"fetch_kib": 390074.8, "write_kib": 55726.4},
            # grouped_gemm_kernel<128, 256, 2, 4, 64, 0, 0, 3> + splitk_finish_kernel<128, 256, 2, 4, 64, 0, 0>
            },
-    "c4": {"sources": "71a869a347bd3511",
-           "fc1": {"fetch_kib": 3149833.8, "write_kib": 458910.8},
+    "c4": {"sources": "e32a9db052f7d51f",
+           "fc1": {"fetch_kib": 3363246.8, "write_kib": 458904.3},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2>
-           "fc2": {"fetch_kib": 1646148.6, "write_kib": 199651.2},
+           "fc2": {"fetch_kib": 1749746.5, "write_kib": 208137.5},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
-    "c5": {"sources": "71a869a347bd3511",
-           "fc1": {"fetch_kib": 363845.5, "write_kib": 2116.0},
+    "c5": {"sources": "e32a9db052f7d51f",
+           "fc1": {"fetch_kib": 363817.2, "write_kib": 2115.6},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 0, 4>
-           "fc2": {"fetch_kib": 181437.6, "write_kib": 3072.1},
+           "fc2": {"fetch_kib": 181432.5, "write_kib": 3072.1},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 0, 4>
            },
-    "c3": {"sources": "71a869a347bd3511",
-           "fc1": {"fetch_kib": 251129.0, "write_kib": 143179.3},
+    "c3": {"sources": "e32a9db052f7d51f",
+           "fc1": {"fetch_kib": 148387.5, "write_kib": 140566.6},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 1, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 1, 1>
-           "fc2": {"fetch_kib": 299485.6, "write_kib": 89850.4},
+           "fc2": {"fetch_kib": 212384.9, "write_kib": 89744.9},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 1>
+           },
+    "c6": {"sources": "e32a9db052f7d51f",
+           "fc1": {"fetch_kib": 584152.3, "write_kib": 90134.4},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 3, 0>
+           "fc2": {"fetch_kib": 265225.8, "write_kib": 133060.7},
+           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
