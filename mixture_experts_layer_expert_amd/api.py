@@ -75,7 +75,10 @@ class MoeShape:
                         fused_decode=fused_decode, n_shared=getattr(cfg, "n_shared", 0))
 
 
-def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "") -> Optional[int]:
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: str = "",
+         n: Optional[int] = None) -> Optional[int]:
+    """Device address of t after checking device, layout, dtype and, when n is
+    given, that t holds at least n elements (the library trusts its sizes)."""
     if t is None:
         return None
     if not t.is_cuda:
@@ -84,7 +87,13 @@ def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None, name: s
         raise ValueError(f"{name}: expected a contiguous tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if n is not None and t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, the shape needs {n}")
     return t.data_ptr()
+
+
+def _slots(shape: "MoeShape") -> int:
+    return shape.n_shared + shape.N  # expert slots of the weight stacks
 
 
 def _stream(stream) -> int:
@@ -113,9 +122,9 @@ def route(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, logits=No
     dt = shape.torch_dtype
     sc = shape.c()
     _check("moe_route", L.load().moe_route(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
-        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
+        _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(topk_idx, torch.int32, "topk_idx", shape.T * shape.k),
+        _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k), _ptr(logits, torch.float32, "logits", shape.T * shape.N),
         _stream(stream)))
 
 
@@ -131,9 +140,9 @@ def route_stats(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, sta
     dt = shape.torch_dtype
     sc = shape.c()
     _check("moe_route_stats", L.load().moe_route_stats(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
-        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(logits, torch.float32, "logits"),
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
+        _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(topk_idx, torch.int32, "topk_idx", shape.T * shape.k),
+        _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k), _ptr(logits, torch.float32, "logits", shape.T * shape.N),
         *_ws_arg(stats_ws), _stream(stream)))
 
 
@@ -141,9 +150,9 @@ def router_stats(shape: MoeShape, stats_ws, counts, n_dropped, prob_mean, frac, 
     i32, f64 = torch.int32, torch.float64
     sc = shape.c()
     _check("moe_router_stats", L.load().moe_router_stats(
-        ctypes.byref(sc), *_ws_arg(stats_ws), _ptr(counts, i32, "counts"),
-        _ptr(n_dropped, i32, "n_dropped"), _ptr(prob_mean, f64, "prob_mean"), _ptr(frac, f64, "frac"),
-        _ptr(summary, f64, "summary"), _stream(stream)))
+        ctypes.byref(sc), *_ws_arg(stats_ws), _ptr(counts, i32, "counts", shape.N),
+        _ptr(n_dropped, i32, "n_dropped", 1), _ptr(prob_mean, f64, "prob_mean", shape.N), _ptr(frac, f64, "frac", shape.N),
+        _ptr(summary, f64, "summary", 3), _stream(stream)))
 
 
 def route_fallback(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, n_fallback, fb_idx, fb_gate,
@@ -151,10 +160,10 @@ def route_fallback(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, 
     dt = shape.torch_dtype
     sc = shape.c()
     _check("moe_route_fallback", L.load().moe_route_fallback(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
-        _ptr(b_router, torch.float32, "b_router"), _ptr(topk_idx, torch.int32, "topk_idx"),
-        _ptr(topk_gate, torch.float32, "topk_gate"), int(n_fallback), _ptr(fb_idx, torch.int32, "fb_idx"),
-        _ptr(fb_gate, torch.float32, "fb_gate"), _ptr(logits, torch.float32, "logits"), _stream(stream)))
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
+        _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(topk_idx, torch.int32, "topk_idx", shape.T * shape.k),
+        _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k), int(n_fallback), _ptr(fb_idx, torch.int32, "fb_idx", shape.T * int(n_fallback)),
+        _ptr(fb_gate, torch.float32, "fb_gate", shape.T * int(n_fallback)), _ptr(logits, torch.float32, "logits", shape.T * shape.N), _stream(stream)))
 
 
 def dispatch_reroute(shape: MoeShape, n_fallback, fb_idx, fb_gate, topk_idx, topk_gate, counts, offsets, perm,
@@ -162,19 +171,19 @@ def dispatch_reroute(shape: MoeShape, n_fallback, fb_idx, fb_gate, topk_idx, top
     i32 = torch.int32
     sc = shape.c()
     _check("moe_dispatch_reroute", L.load().moe_dispatch_reroute(
-        ctypes.byref(sc), int(n_fallback), _ptr(fb_idx, i32, "fb_idx"), _ptr(fb_gate, torch.float32, "fb_gate"),
-        _ptr(topk_idx, i32, "topk_idx"), _ptr(topk_gate, torch.float32, "topk_gate"),
-        _ptr(counts, i32, "counts"), _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"),
-        _ptr(slot, i32, "slot"), _ptr(n_dropped, i32, "n_dropped"), _stream(stream)))
+        ctypes.byref(sc), int(n_fallback), _ptr(fb_idx, i32, "fb_idx", shape.T * int(n_fallback)), _ptr(fb_gate, torch.float32, "fb_gate", shape.T * int(n_fallback)),
+        _ptr(topk_idx, i32, "topk_idx", shape.T * shape.k), _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k),
+        _ptr(counts, i32, "counts", shape.N), _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows),
+        _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
 
 
 def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None):
     i32 = torch.int32
     sc = shape.c()
     _check("moe_dispatch", L.load().moe_dispatch(
-        ctypes.byref(sc), _ptr(topk_idx, i32, "topk_idx"), _ptr(counts, i32, "counts"),
-        _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"), _ptr(slot, i32, "slot"),
-        _ptr(n_dropped, i32, "n_dropped"), _stream(stream)))
+        ctypes.byref(sc), _ptr(topk_idx, i32, "topk_idx", shape.T * shape.k), _ptr(counts, i32, "counts", shape.N),
+        _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows), _ptr(slot, i32, "slot", shape.T * shape.k),
+        _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
 
 
 def expert_ffn(shape: MoeShape, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, stream=None):
@@ -182,9 +191,9 @@ def expert_ffn(shape: MoeShape, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws
     i32 = torch.int32
     sc = shape.c()
     _check("moe_expert_ffn", L.load().moe_expert_ffn(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(perm, i32, "perm"), _ptr(offsets, i32, "offsets"),
-        _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"), _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"),
-        _ptr(b2, dt, "b2"), _ptr(y_perm, dt, "y_perm"), _ptr(ws, None, "ws"),
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(perm, i32, "perm", shape.group_rows), _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1),
+        _ptr(w1, dt, "w1", _slots(shape) * shape.F * shape.D), _ptr(b1, dt, "b1", _slots(shape) * shape.F), _ptr(w3, dt, "w3", _slots(shape) * shape.F * shape.D), _ptr(w2, dt, "w2", _slots(shape) * shape.D * shape.F),
+        _ptr(b2, dt, "b2", _slots(shape) * shape.D), _ptr(y_perm, dt, "y_perm", shape.group_rows * shape.D), _ptr(ws, None, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -202,8 +211,8 @@ def expert_up(shape: MoeShape, x, perm, offsets, w1, b1, w3, h, ws=None, stream=
     sc = shape.c()
     wp, wn = _ws_arg(ws)
     _check("moe_expert_up", L.load().moe_expert_up(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(perm, i32, "perm"), _ptr(offsets, i32, "offsets"),
-        _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"), _ptr(w3, dt, "w3"), _ptr(h, dt, "h"), wp, wn,
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(perm, i32, "perm", shape.group_rows), _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1),
+        _ptr(w1, dt, "w1", _slots(shape) * shape.F * shape.D), _ptr(b1, dt, "b1", _slots(shape) * shape.F), _ptr(w3, dt, "w3", _slots(shape) * shape.F * shape.D), _ptr(h, dt, "h", shape.group_rows * shape.F), wp, wn,
         _stream(stream)))
 
 
@@ -213,17 +222,17 @@ def expert_down(shape: MoeShape, h, offsets, w2, b2, y_perm, ws=None, stream=Non
     sc = shape.c()
     wp, wn = _ws_arg(ws)
     _check("moe_expert_down", L.load().moe_expert_down(
-        ctypes.byref(sc), _ptr(h, dt, "h"), _ptr(offsets, torch.int32, "offsets"),
-        _ptr(w2, dt, "w2"), _ptr(b2, dt, "b2"), _ptr(y_perm, dt, "y_perm"), wp, wn, _stream(stream)))
+        ctypes.byref(sc), _ptr(h, dt, "h", shape.group_rows * shape.F), _ptr(offsets, torch.int32, "offsets", shape.n_shared + shape.N + 1),
+        _ptr(w2, dt, "w2", _slots(shape) * shape.D * shape.F), _ptr(b2, dt, "b2", _slots(shape) * shape.D), _ptr(y_perm, dt, "y_perm", shape.group_rows * shape.D), wp, wn, _stream(stream)))
 
 
 def combine(shape: MoeShape, y_perm, slot, topk_gate, x_residual, out, stream=None):
     dt = shape.torch_dtype
     sc = shape.c()
     _check("moe_combine", L.load().moe_combine(
-        ctypes.byref(sc), _ptr(y_perm, dt, "y_perm"), _ptr(slot, torch.int32, "slot"),
-        _ptr(topk_gate, torch.float32, "topk_gate"), _ptr(x_residual, dt, "x_residual"),
-        _ptr(out, dt, "out"), _stream(stream)))
+        ctypes.byref(sc), _ptr(y_perm, dt, "y_perm", shape.group_rows * shape.D), _ptr(slot, torch.int32, "slot", shape.T * shape.k),
+        _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k), _ptr(x_residual, dt, "x_residual", shape.T * shape.D),
+        _ptr(out, dt, "out", shape.T * shape.D), _stream(stream)))
 
 
 def forward(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, topk_idx, topk_gate,
@@ -232,12 +241,12 @@ def forward(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, top
     i32 = torch.int32
     sc = shape.c()
     _check("moe_forward", L.load().moe_forward(
-        ctypes.byref(sc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
-        _ptr(b_router, torch.float32, "b_router"), _ptr(w1, dt, "w1"), _ptr(b1, dt, "b1"),
-        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), _ptr(b2, dt, "b2"), _ptr(out, dt, "out"),
-        _ptr(topk_idx, i32, "topk_idx"), _ptr(topk_gate, torch.float32, "topk_gate"),
-        _ptr(counts, i32, "counts"), _ptr(offsets, i32, "offsets"), _ptr(perm, i32, "perm"),
-        _ptr(slot, i32, "slot"), _ptr(n_dropped, i32, "n_dropped"), _ptr(ws, None, "ws"),
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
+        _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(w1, dt, "w1", _slots(shape) * shape.F * shape.D), _ptr(b1, dt, "b1", _slots(shape) * shape.F),
+        _ptr(w3, dt, "w3", _slots(shape) * shape.F * shape.D), _ptr(w2, dt, "w2", _slots(shape) * shape.D * shape.F), _ptr(b2, dt, "b2", _slots(shape) * shape.D), _ptr(out, dt, "out", shape.T * shape.D),
+        _ptr(topk_idx, i32, "topk_idx", shape.T * shape.k), _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k),
+        _ptr(counts, i32, "counts", shape.N), _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows),
+        _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), _ptr(ws, None, "ws"),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 

@@ -241,3 +241,35 @@ def test_library_has_no_undefined_internal_symbols():
                          check=True).stdout
     bad = [l for l in out.splitlines() if "3moe" in l]
     assert not bad, bad[:5]
+
+
+def test_binding_rejects_undersized_buffers():
+    """The Python binding checks every buffer against the shape before the
+    library sees a pointer (the library itself trusts its sizes)."""
+    import torch
+    from mixture_experts_layer_expert_amd import api
+
+    class FakeGpuTensor:  # stands in for a device tensor on a host without a GPU
+        is_cuda = True
+
+        def __init__(self, n, dtype=torch.bfloat16):
+            self.n, self.dtype = n, dtype
+
+        def is_contiguous(self):
+            return True
+
+        def numel(self):
+            return self.n
+
+        def data_ptr(self):
+            return 0x1000
+
+    assert api._ptr(FakeGpuTensor(64 * 128), torch.bfloat16, "x", 64 * 128) == 0x1000
+    with pytest.raises(ValueError, match="the shape needs"):
+        api._ptr(FakeGpuTensor(64 * 128 - 1), torch.bfloat16, "x", 64 * 128)
+    with pytest.raises(ValueError, match="expected torch.float32"):
+        api._ptr(FakeGpuTensor(10), torch.float32, "topk_gate", 10)
+    shape = api.MoeShape(T=64, D=128, F=256, N=8, k=2, capacity=-1, act="relu")
+    with pytest.raises(ValueError, match="x: 4096 elements"):
+        api.route(shape, FakeGpuTensor(4096), FakeGpuTensor(8 * 128), None,
+                  FakeGpuTensor(128, torch.int32), FakeGpuTensor(128, torch.float32))
