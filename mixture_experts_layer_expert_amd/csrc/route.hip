@@ -777,10 +777,12 @@ __global__ __launch_bounds__(64) void router_stats_kernel(const float* part, int
 
 // Tokens per router block.  bf16 with D a multiple of 128 uses the DMA ring
 // kernel: as many tokens as keep >= ~2 blocks per CU busy, 16 for the widest
-// expert counts (their ring stages are large); otherwise 32.
+// expert counts (their ring stages are large) and for at most 16 experts
+// (8 KiB stages: an 8-deep ring and two blocks per CU beat fewer, larger
+// blocks); otherwise 32.
 int route_rows_per_block(const moe_shape& s) {
   if (s.dtype == MOE_DTYPE_BF16 && s.D % 128 == 0) {
-    if (s.N > 128) return 16;
+    if (s.N > 128 || s.N <= 16) return 16;
     const int64_t cus = device_cu_count();
     if (s.T >= 64 * cus) return 64;
     if (s.T >= 32 * cus) return 32;

@@ -131,13 +131,17 @@ def test_stats_workspace_bytes_and_validation(lib):
     """One fp32 partial per (router block, expert), rounded up to 256 bytes,
     then 256 bytes for the ticket of the second pass: bf16 with D % 128 == 0
     uses 16 tokens per block below 32 tokens per CU (256 CUs without a
-    device), fp32 32 tokens per block."""
+    device) and for at most 16 experts, fp32 32 tokens per block."""
     from mixture_experts_layer_expert_amd import _lib as L
     n = ctypes.c_size_t(0)
     assert lib.moe_stats_workspace_bytes(ctypes.byref(_shape(T=4096)), ctypes.byref(n)) == L.MOE_OK
     assert n.value == (4096 // 16) * 8 * 4 + 256
+    # 64 tokens per block from 64 per CU on, for more than 16 experts
+    assert lib.moe_stats_workspace_bytes(ctypes.byref(_shape(T=4096 * 4, N=32)), ctypes.byref(n)) == L.MOE_OK
+    assert n.value == (4096 * 4 // 64) * 32 * 4 + 256
+    # at most 16 experts: always 16 tokens per block
     assert lib.moe_stats_workspace_bytes(ctypes.byref(_shape(T=4096 * 4)), ctypes.byref(n)) == L.MOE_OK
-    assert n.value == (4096 * 4 // 64) * 8 * 4 + 256
+    assert n.value == (4096 * 4 // 16) * 8 * 4 + 256
     s32 = _shape(T=1000, dtype=L.MOE_DTYPE_F32, act=L.MOE_ACT_GELU)
     assert lib.moe_stats_workspace_bytes(ctypes.byref(s32), ctypes.byref(n)) == L.MOE_OK
     assert n.value == 1024 + 256  # 32 blocks * 8 experts * 4 bytes, rounded up to 256 bytes
