@@ -633,6 +633,26 @@ def test_forward_full_size(gpu, key):
     _say(f"  row-rel err {err:.3e} over {sample.size} sampled tokens, dropped {ref['n_dropped']}")
 
 
+@pytest.mark.slow
+def test_forward_large_batch(gpu):
+    """The Switch-shaped layer at 8x its batch (131072 tokens, 128 experts,
+    capacity 1024): routing, counts, offsets, perm, slot and drops exact over
+    all tokens; outputs on sampled tokens."""
+    cfg = scaled_config(get_config("c2"), T=131072)
+    _say(f"forward large {cfg.name}: T={cfg.T} cf={cfg.cf}")
+    inp = generate(cfg)
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g)
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([np.arange(4), np.arange(cfg.T - 4, cfg.T),
+                                       rng.choice(cfg.T, size=60, replace=False)]))
+    ref = oracle_layer(cfg, inp, tokens=sample)
+    check_routing(buf, ref, cfg)
+    y = buf.out.float().cpu().numpy().astype(np.float64)[sample]
+    err = check_outputs(y, ref, cfg, inp["x"].double().numpy()[sample], tokens=sample)
+    _say(f"  row-rel err {err:.3e}, dropped {ref['n_dropped']} of {cfg.T}")
+
+
 # ------------------------------------------ HIP-graph capture of the layer
 @pytest.mark.parametrize("key", ["c2", "c5"])
 def test_graph_replay_matches_eager(gpu, key, scaled_cases):
