@@ -55,7 +55,47 @@ __device__ inline V neg_inf();
 template <>
 __device__ inline float neg_inf<float>() { return -FLT_MAX; }
 
-__device__ inline float vexp(float v) { return expf(v); }
+// exp of a non-positive argument (logit minus the row maximum) with the
+// hardware exponential: a few ulp, far below the gate tolerance
+__device__ inline float vexp(float v) { return __expf(v); }
+
+// Exchanges within a 16-lane group through DPP (no LDS round trip): after
+// xor 1, xor 2, the mirror within 8 lanes and the mirror within 16 lanes,
+// every lane of the group has combined all 16 values.  All lanes of the wave
+// take part.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+template <int CTRL>
+__device__ inline void argmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  const bool take = (ov > bv) | ((ov == bv) & (oi < bi));  // better(), branch-free
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
+// (value, lower index) arg-max of the group, in every lane; a total order,
+// so the result does not depend on the exchange pattern
+__device__ inline void group16_argmax(float& bv, int& bi) {
+  argmax_step<kDppXor1>(bv, bi);
+  argmax_step<kDppXor2>(bv, bi);
+  argmax_step<kDppHalfMirror>(bv, bi);
+  argmax_step<kDppMirror>(bv, bi);
+}
+// sum of the group in every lane (fixed pairing, so deterministic)
+__device__ inline float group16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
 
 // Ranks one token within a 16-lane group.  vals: LDS row of N logits.
 // Returns true when the top-(k+1) are separated by at least `margin`
@@ -76,32 +116,29 @@ __device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, in
   const int nsel = (KS + 1 <= N) ? KS + 1 : N;
   V tv[kMaxTopK + 1];
   int ti[kMaxTopK + 1];
-  uint32_t taken = 0;
+  // experts of this lane still to rank (bit i: expert l16 + 16 i); the
+  // selection is written with bitwise conditions and selects so that it
+  // compiles without branches
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) avail |= (l16 + 16 * i < N) ? (1u << i) : 0u;
 #pragma unroll
   for (int r = 0; r < kMaxTopK + 1; ++r) {
-    if (r < nsel) {
-    V bv = neg_inf<V>();
-    int bi = INT_MAX;
+    if (r < nsel) {  // wave-uniform
+      V bv = neg_inf<V>();
+      int bi = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int e = l16 + 16 * i;
-      if (e < N && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
+      for (int i = 0; i < NV; ++i) {
+        const int e = l16 + 16 * i;
+        const bool take = ((avail >> i) & 1u) & ((v[i] > bv) | ((v[i] == bv) & (e < bi)));
+        bv = take ? v[i] : bv;
+        bi = take ? e : bi;
       }
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      V ov = __shfl_xor(bv, off, 16);
-      int oi = __shfl_xor(bi, off, 16);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    tv[r] = bv;
-    ti[r] = bi;
-    if ((bi & 15) == l16) taken |= 1u << (bi >> 4);
+      group16_argmax(bv, bi);
+      tv[r] = bv;
+      ti[r] = bi;
+      const bool mine = (bi < N) & ((bi & 15) == l16);
+      avail &= mine ? ~(1u << ((bi >> 4) & 31)) : ~0u;
     }
   }
   bool ok = true;
@@ -120,32 +157,33 @@ __device__ __forceinline__ bool group_rank(const V* vals, const RouteArgs& a, in
     ex[i] = (e < N) ? vexp(v[i] - vmax) : V(0);
     s += ex[i];
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  s = group16_sum(s);
   if (stats && t < a.T) {
     const V inv = V(1) / s;
 #pragma unroll
     for (int i = 0; i < NV; ++i) pacc[i] += ex[i] * inv;
   }
   if (!ok && !force) return false;
-  if (l16 == 0 && t < a.T) {
-    V p[kMaxTopK];
-    V ps = 0;
+  // lane j of the group finishes rank j (j < KS): one exponential and one
+  // division per lane instead of KS of each in one lane
+  V myv = tv[0];
+  int myi = ti[0];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      p[j] = (j < KS) ? vexp(tv[j] - vmax) / s : V(0);
-      if (j < k) ps += p[j];
+  for (int r = 1; r < kMaxTopK; ++r)
+    if (l16 == r && r < nsel) {
+      myv = tv[r];
+      myi = ti[r];
     }
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      const float g = (float)(a.renorm ? p[j] / ps : p[j]);
-      if (j < k) {
-        a.idx[t * k + j] = ti[j];
-        a.gate[t * k + j] = g;
-      } else if (j < KS) {
-        a.fb_idx[t * a.R + (j - k)] = ti[j];
-        a.fb_gate[t * a.R + (j - k)] = g;
-      }
+  const V p = (l16 < KS) ? vexp(myv - vmax) / s : V(0);
+  const V ps = group16_sum(l16 < k ? p : V(0));
+  if (t < a.T) {
+    const float g = (float)(a.renorm ? p / ps : p);
+    if (l16 < k) {
+      a.idx[t * k + l16] = myi;
+      a.gate[t * k + l16] = g;
+    } else if (l16 < KS) {
+      a.fb_idx[t * a.R + (l16 - k)] = myi;
+      a.fb_gate[t * a.R + (l16 - k)] = g;
     }
   }
   return true;
