@@ -273,7 +273,8 @@ def main():
             api.dispatch_reroute(shape, args.reroute, fb_idx, fb_gate, buf.topk_idx, buf.topk_gate, buf.counts,
                                  buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
         else:
-            api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
+            api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped, s,
+                         ws=buf.ws)
         if rstats:
             api.router_stats(shape, stats_ws, buf.counts, buf.n_dropped, prob_mean, frac, summary, s)
         if ev is not None:

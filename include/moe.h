@@ -196,11 +196,20 @@ int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_
  * past offsets[N] are left untouched.  With n_shared = S the S shared groups
  * come first (offsets[S+N+1], perm of S*T + T*k entries, routed rows and
  * slots shifted by S*T; see moe_shape).  With MOE_PADDED expert e's rows
- * start at S*T + e*C and perm holds S*T + N*C entries, padding included.  Expert ids outside [0, N) are
- * treated as dropped and not counted.  Bit-exact, deterministic. */
+ * start at S*T + e*C and perm holds S*T + N*C entries, padding included.
+ * Expert ids outside [0, N) are treated as dropped and not counted.
+ * Bit-exact and deterministic.
+ *
+ * ws is optional device scratch. With ws = NULL, one workgroup does the whole
+ * dispatch in one launch. Otherwise ws needs at least
+ * moe_workspace_bytes(shape) bytes with 256-byte alignment (MOE_ERR_WORKSPACE
+ * or MOE_ERR_INVALID_ARG otherwise). Large batches with many experts then take
+ * two launches over many workgroups: segments of the priority order are
+ * ranked apart and placed from their fixed-order counts. "Large" means T*k
+ * times (bits of N + 2) above 120000. The results are identical. */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
-                 moe_stream_t stream);
+                 void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Overflow fallback. The notebook's "What" section sends capacity overflow
  * to a fallback path. The first page's tuning tricks reroute rejected tokens

@@ -59,7 +59,7 @@ _SIGS = {
     "moe_stats_workspace_bytes": (ctypes.c_int, [_shape_p, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route_stats": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_router_stats": (ctypes.c_int, [_shape_p, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_dispatch": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_dispatch": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_route_fallback": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp,
                                           _vp]),
     "moe_dispatch_reroute": (ctypes.c_int, [_shape_p, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,

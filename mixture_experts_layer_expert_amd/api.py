@@ -177,13 +177,16 @@ def dispatch_reroute(shape: MoeShape, n_fallback, fb_idx, fb_gate, topk_idx, top
         _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
 
 
-def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None):
+def dispatch(shape: MoeShape, topk_idx, counts, offsets, perm, slot, n_dropped, stream=None, ws=None):
+    """ws (optional, >= workspace_bytes) lets large batches use the
+    multi-workgroup dispatch; the results are the same."""
     i32 = torch.int32
     sc = shape.c()
+    wp, wn = _ws_arg(ws)
     _check("moe_dispatch", L.load().moe_dispatch(
         ctypes.byref(sc), _ptr(topk_idx, i32, "topk_idx", shape.T * shape.k), _ptr(counts, i32, "counts", shape.N),
-        _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows), _ptr(slot, i32, "slot", shape.T * shape.k),
-        _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
+        _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows),
+        _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), wp, wn, _stream(stream)))
 
 
 def expert_ffn(shape: MoeShape, x, perm, offsets, w1, b1, w3, w2, b2, y_perm, ws, stream=None):

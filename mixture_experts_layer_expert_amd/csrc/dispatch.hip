@@ -46,6 +46,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPrefetch = 8;  // chunks whose ids are loaded ahead
+constexpr int kRegChunks = 24;  // register mode: up to 24 chunks per wave (24576 assignments)
 
 // Flat index a = t*k + j of the i-th assignment in priority order.
 __device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
@@ -61,6 +62,27 @@ __device__ inline int64_t flat_of(int64_t i, int64_t T, int k, bool by_choice) {
 __device__ inline int wave_rank(bool valid, int e, int bits, uint64_t lt_mask, int* cnt) {
   uint64_t same = __ballot(valid);
   for (int b = 0; b < bits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    same &= bit ? bb : ~bb;
+  }
+  int rank = 0;
+  if (valid) {
+    const int below = __popcll(same & lt_mask);
+    const int base = cnt[e];
+    if (below == 0) cnt[e] = base + __popcll(same);
+    rank = base + below;
+  }
+  return rank;
+}
+
+// wave_rank with the number of expert-id bits fixed at compile time: the
+// ballot loop unrolls, so the ballots of independent chunks can interleave.
+template <int BITS>
+__device__ inline int wave_rank_c(bool valid, int e, uint64_t lt_mask, int* cnt) {
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
     const bool bit = valid && ((e >> b) & 1);
     const uint64_t bb = __ballot(bit);
     same &= bit ? bb : ~bb;
@@ -100,7 +122,10 @@ __device__ inline void block_scan(int* v, int N, int tid) {
   }
 }
 
-template <bool REROUTE>
+// BITS >= 0: the expert-id bit count, fixed; -1: computed.  CH > 0: each
+// wave keeps its at most CH chunks (ids and in-wave ranks) in registers from
+// A to C instead of parking the ranks in slot and loading both again.
+template <bool REROUTE, int BITS, int CH>
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(int32_t* idx, int64_t A, int64_t T, int k,
                                                             int by_choice, int N, int C, int S, int pad,
                                                             int32_t* __restrict__ counts,
@@ -128,22 +153,47 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(int32_t* idx, int64_
   const int64_t a_begin = (int64_t)wave * per * kWave;
   const int64_t a_end = (a_begin + per * kWave < A) ? a_begin + per * kWave : A;
 
+  auto rank_of = [&](bool valid, int e) {
+    if constexpr (BITS >= 0)
+      return wave_rank_c<BITS>(valid, e, lt_mask, wcnt[wave]);
+    else
+      return wave_rank(valid, e, bits, lt_mask, wcnt[wave]);
+  };
+  int rev[CH > 0 ? CH : 1], rrk[CH > 0 ? CH : 1];  // register mode: ids, in-wave ranks
+
   // ---- A: in-wave ranks
-  for (int64_t b0 = a_begin; b0 < a_end; b0 += kPrefetch * kWave) {
-    int ev[kPrefetch];
+  if constexpr (CH > 0) {
 #pragma unroll
-    for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t i = b0 + c * kWave + lane;
-      ev[c] = (i < a_end) ? idx[flat_of(i, T, k, by_choice)] : -1;
+    for (int c = 0; c < CH; ++c) {  // every load in flight at once
+      const int64_t i = a_begin + c * kWave + lane;
+      rev[c] = (i < a_end) ? idx[flat_of(i, T, k, by_choice)] : -1;
     }
 #pragma unroll
-    for (int c = 0; c < kPrefetch; ++c) {
-      const int64_t i = b0 + c * kWave + lane;
-      const int64_t a = flat_of(i, T, k, by_choice);
-      const int e = ev[c];
-      const bool valid = i < a_end && e >= 0 && e < N;
-      const int rank = wave_rank(valid, e, bits, lt_mask, wcnt[wave]);
-      if (valid) slot[a] = rank;
+    for (int c = 0; c < CH; ++c) {
+      rrk[c] = 0;
+      if (a_begin + c * kWave < a_end) {  // wave-uniform
+        const int64_t i = a_begin + c * kWave + lane;
+        const int e = rev[c];
+        rrk[c] = rank_of(i < a_end && e >= 0 && e < N, e);
+      }
+    }
+  } else {
+    for (int64_t b0 = a_begin; b0 < a_end; b0 += kPrefetch * kWave) {
+      int ev[kPrefetch];
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t i = b0 + c * kWave + lane;
+        ev[c] = (i < a_end) ? idx[flat_of(i, T, k, by_choice)] : -1;
+      }
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int64_t i = b0 + c * kWave + lane;
+        const int64_t a = flat_of(i, T, k, by_choice);
+        const int e = ev[c];
+        const bool valid = i < a_end && e >= 0 && e < N;
+        const int rank = rank_of(valid, e);
+        if (valid) slot[a] = rank;
+      }
     }
   }
   __syncthreads();
@@ -187,7 +237,28 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(int32_t* idx, int64_
   __syncthreads();
 
   // ---- C: final ranks -> slot and perm
-  for (int64_t b0 = a_begin; b0 < a_end; b0 += kPrefetch * kWave) {
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t i = a_begin + c * kWave + lane;
+      if (i >= a_end) continue;
+      const int64_t a = flat_of(i, T, k, by_choice);
+      const int e = rev[c];
+      if (e < 0 || e >= N) {
+        slot[a] = -1;
+        continue;
+      }
+      const int rank = wcnt[wave][e] + rrk[c];
+      if (C < 0 || rank < C) {
+        const int sr = off[e] + rank;
+        slot[a] = sr;
+        perm[sr] = (int32_t)a;
+      } else {
+        slot[a] = -1;
+      }
+    }
+  }
+  for (int64_t b0 = a_begin; b0 < (CH > 0 ? a_begin : a_end); b0 += kPrefetch * kWave) {
     int ev[kPrefetch], rv[kPrefetch];
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
@@ -347,6 +418,160 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(int32_t* idx, int64_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dispatch over many workgroups (the same result as dispatch_kernel).  The
+// priority order is cut into segments of kSeg assignments, one per
+// workgroup of kSegWaves waves (each wave kSegChunks 64-wide chunks):
+//  count: in-segment stable ranks with the ballot scheme (waves in order),
+//         parked in slot; the segment's per-expert counts go to
+//         bc[seg * N + e] (workspace).
+//  place: every workgroup sums bc over the segments in increasing order:
+//         its own per-expert base, the totals, the capacity cut and the
+//         offsets; segment 0 writes counts, offsets and n_dropped, and the
+//         shared rows and padding rows are filled grid-stride; then each
+//         workgroup turns its parked ranks into slot and perm.
+constexpr int kSegWaves = 4;
+constexpr int kSegChunks = 4;
+constexpr int kSeg = kSegWaves * kSegChunks * kWave;  // 1024
+
+template <int BITS>
+__global__ __launch_bounds__(kSegWaves * kWave) void dispatch_count_kernel(const int32_t* __restrict__ idx, int64_t A,
+                                                                           int64_t T, int k, int by_choice, int N,
+                                                                           int32_t* __restrict__ slot,
+                                                                           int32_t* __restrict__ bc) {
+  __shared__ int wcnt[kSegWaves][kMaxExperts];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  for (int i = tid; i < kSegWaves * kMaxExperts; i += kSegWaves * kWave) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t w0 = (int64_t)blockIdx.x * kSeg + (int64_t)wave * kSegChunks * kWave;
+  int ev[kSegChunks], rk[kSegChunks];
+#pragma unroll
+  for (int c = 0; c < kSegChunks; ++c) {
+    const int64_t i = w0 + c * kWave + lane;
+    ev[c] = (i < A) ? idx[flat_of(i, T, k, by_choice)] : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < kSegChunks; ++c) {
+    const int64_t i = w0 + c * kWave + lane;
+    const int e = ev[c];
+    rk[c] = wave_rank_c<BITS>(i < A && e >= 0 && e < N, e, lt_mask, wcnt[wave]);
+  }
+  __syncthreads();
+  // wave bases inside the segment, and the segment's counts
+  if (tid < N) {
+    int run = 0;
+    for (int w = 0; w < kSegWaves; ++w) {
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = run;
+      run += c;
+    }
+    bc[(int64_t)blockIdx.x * N + tid] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kSegChunks; ++c) {
+    const int64_t i = w0 + c * kWave + lane;
+    const int e = ev[c];
+    if (i < A && e >= 0 && e < N) slot[flat_of(i, T, k, by_choice)] = wcnt[wave][e] + rk[c];
+  }
+}
+
+__global__ __launch_bounds__(kSegWaves * kWave) void dispatch_place_kernel(
+    const int32_t* __restrict__ idx, int64_t A, int64_t T, int k, int by_choice, int N, int C, int S, int pad,
+    const int32_t* __restrict__ bc, int nseg, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ slot, int32_t* __restrict__ n_dropped) {
+  constexpr int kThr = kSegWaves * kWave;
+  __shared__ int base[kMaxExperts], scan[kMaxExperts], off[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int seg = blockIdx.x;
+  // per expert: this segment's base and the total, summed in segment order
+  for (int e = tid; e < N; e += kThr) {
+    int run = 0, mine = 0;
+    for (int g0 = 0; g0 < nseg; g0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = bc[(int64_t)(g0 + u < nseg ? g0 + u : 0) * N + e];  // all in flight
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (g0 + u < nseg) {
+          if (g0 + u == seg) mine = run;
+          run += v[u];
+        }
+      }
+    }
+    base[e] = mine;
+    scan[e] = (C >= 0 && run > C) ? C : run;  // kept
+    if (seg == 0) counts[e] = run;
+  }
+  __syncthreads();
+  // offsets: exclusive scan of the kept counts (compact) or e*C (padded)
+  for (int d = 1; d < kMaxExperts; d <<= 1) {
+    int v[kMaxExperts / kThr > 0 ? kMaxExperts / kThr : 1];
+#pragma unroll
+    for (int u = 0; u < (kMaxExperts + kThr - 1) / kThr; ++u) {
+      const int e = tid + u * kThr;
+      v[u] = (e < N && e >= d) ? scan[e - d] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < (kMaxExperts + kThr - 1) / kThr; ++u) {
+      const int e = tid + u * kThr;
+      if (e < N && e >= d) scan[e] += v[u];
+    }
+    __syncthreads();
+  }
+  const int ST = S * (int)T;
+  for (int e = tid; e < N; e += kThr) {
+    const int kept = scan[e] - (e > 0 ? scan[e - 1] : 0);
+    const int o = ST + (pad ? e * C : scan[e] - kept);
+    off[e] = o;
+    if (seg == 0) offsets[S + e] = o;
+  }
+  if (seg == 0) {
+    if (tid < S) offsets[tid] = tid * (int)T;
+    if (tid == 0) {
+      const int total = N > 0 ? scan[N - 1] : 0;
+      offsets[S + N] = ST + (pad ? N * C : total);
+      *n_dropped = (int32_t)(A - total);
+    }
+  }
+  // shared rows and padding rows, grid-stride over all workgroups
+  const int64_t gthreads = (int64_t)gridDim.x * kThr;
+  for (int64_t r = (int64_t)seg * kThr + tid; r < (int64_t)ST; r += gthreads) perm[r] = (int32_t)((r % T) * k);
+  if (pad) {
+    for (int64_t i = (int64_t)seg * kThr + tid; i < (int64_t)N * C; i += gthreads) {
+      const int e = (int)(i / C), r = (int)(i - (int64_t)e * C);
+      const int kept_e = scan[e] - (e > 0 ? scan[e - 1] : 0);
+      if (r >= kept_e) perm[ST + i] = 0;
+    }
+  }
+  __syncthreads();
+  // place this segment
+  const int64_t s0 = (int64_t)seg * kSeg;
+#pragma unroll 4
+  for (int c = 0; c < kSeg / kThr; ++c) {
+    const int64_t i = s0 + c * kThr + tid;
+    if (i >= A) continue;
+    const int64_t a = flat_of(i, T, k, by_choice);
+    const int e = idx[a];
+    if (e < 0 || e >= N) {
+      slot[a] = -1;
+      continue;
+    }
+    const int rank = base[e] + slot[a];
+    if (C < 0 || rank < C) {
+      const int sr = off[e] + rank;
+      slot[a] = sr;
+      perm[sr] = (int32_t)a;
+    } else {
+      slot[a] = -1;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* counts,
@@ -355,9 +580,66 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
   const int64_t A = s.T * (int64_t)s.k;
   const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
   // the plain dispatch never writes idx
-  hipLaunchKernelGGL(dispatch_kernel<false>, dim3(1), dim3(kThreads), 0, st, const_cast<int32_t*>(idx), A, s.T,
-                     s.k, by_choice, s.N, s.capacity, s.n_shared, (s.flags & MOE_PADDED) ? 1 : 0, counts, offsets,
-                     perm, slot, n_dropped, 0, nullptr, nullptr, nullptr);
+  int32_t* idx_rw = const_cast<int32_t*>(idx);
+  const int pad = (s.flags & MOE_PADDED) ? 1 : 0;
+  int bits = 0;
+  while ((1 << bits) < s.N) ++bits;
+  const int64_t per = ((A + kWave - 1) / kWave + kWaves - 1) / kWaves;  // chunks per wave
+#define MOE_DISPATCH(BITS, CH)                                                                                    \
+  hipLaunchKernelGGL((dispatch_kernel<false, BITS, CH>), dim3(1), dim3(kThreads), 0, st, idx_rw, A, s.T, s.k,     \
+                     by_choice, s.N, s.capacity, s.n_shared, pad, counts, offsets, perm, slot, n_dropped, 0, nullptr, \
+                     nullptr, nullptr)
+  if (per <= kRegChunks) {
+    switch (bits) {
+      case 0: MOE_DISPATCH(0, kRegChunks); break;
+      case 1: MOE_DISPATCH(1, kRegChunks); break;
+      case 2: MOE_DISPATCH(2, kRegChunks); break;
+      case 3: MOE_DISPATCH(3, kRegChunks); break;
+      case 4: MOE_DISPATCH(4, kRegChunks); break;
+      case 5: MOE_DISPATCH(5, kRegChunks); break;
+      case 6: MOE_DISPATCH(6, kRegChunks); break;
+      case 7: MOE_DISPATCH(7, kRegChunks); break;
+      default: MOE_DISPATCH(8, kRegChunks); break;
+    }
+  } else {
+    MOE_DISPATCH(-1, 0);
+  }
+#undef MOE_DISPATCH
+  return hipGetLastError();
+}
+
+size_t dispatch_ws_bytes(const moe_shape& s) {
+  const int64_t A = s.T * (int64_t)s.k;
+  return (size_t)((A + kSeg - 1) / kSeg) * (size_t)s.N * sizeof(int32_t);
+}
+
+hipError_t launch_dispatch_multi(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* slot, int32_t* n_dropped, int32_t* bc, hipStream_t st) {
+  const int64_t A = s.T * (int64_t)s.k;
+  const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
+  const int pad = (s.flags & MOE_PADDED) ? 1 : 0;
+  const int nseg = (int)((A + kSeg - 1) / kSeg);
+  int bits = 0;
+  while ((1 << bits) < s.N) ++bits;
+#define MOE_COUNT(BITS)                                                                                      \
+  hipLaunchKernelGGL((dispatch_count_kernel<BITS>), dim3(nseg), dim3(kSegWaves * kWave), 0, st, idx, A, s.T, \
+                     s.k, by_choice, s.N, slot, bc)
+  switch (bits) {
+    case 0: MOE_COUNT(0); break;
+    case 1: MOE_COUNT(1); break;
+    case 2: MOE_COUNT(2); break;
+    case 3: MOE_COUNT(3); break;
+    case 4: MOE_COUNT(4); break;
+    case 5: MOE_COUNT(5); break;
+    case 6: MOE_COUNT(6); break;
+    case 7: MOE_COUNT(7); break;
+    default: MOE_COUNT(8); break;
+  }
+#undef MOE_COUNT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_place_kernel, dim3(nseg), dim3(kSegWaves * kWave), 0, st, idx, A, s.T, s.k, by_choice,
+                     s.N, s.capacity, s.n_shared, pad, bc, nseg, counts, offsets, perm, slot, n_dropped);
   return hipGetLastError();
 }
 
@@ -366,7 +648,7 @@ hipError_t launch_dispatch_reroute(const moe_shape& s, int R, const int32_t* fb_
                                    int32_t* slot, int32_t* n_dropped, hipStream_t st) {
   const int64_t A = s.T * (int64_t)s.k;
   const int by_choice = (s.flags & MOE_SLOT_MAJOR) && s.k > 1;
-  hipLaunchKernelGGL(dispatch_kernel<true>, dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
+  hipLaunchKernelGGL((dispatch_kernel<true, -1, 0>), dim3(1), dim3(kThreads), 0, st, idx, A, s.T, s.k, by_choice, s.N,
                      s.capacity, s.n_shared, 0, counts, offsets, perm, slot, n_dropped, R, fb_idx, fb_gate, gate);
   return hipGetLastError();
 }

@@ -279,15 +279,34 @@ int moe_dispatch_reroute(const moe_shape* shape, int32_t n_fallback, const int32
                                             perm, slot, n_dropped, (hipStream_t)stream));
 }
 
+// Dispatch over many workgroups when scratch is at hand and the single
+// workgroup's work, about A * (expert-id bits + 2) ballot steps, exceeds what
+// the second launch costs (measured: worth it for 16384 assignments over 128
+// experts and 24576 over 64, not for 16384 over 8 or 16); one workgroup
+// otherwise.  The results are identical.
+constexpr int64_t kMultiDispatchWork = 120000;
+static hipError_t dispatch_any(const moe_shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, int32_t* slot, int32_t* n_dropped, void* ws, hipStream_t st) {
+  int bits = 0;
+  while ((1 << bits) < s.N) ++bits;
+  if (ws && s.T * (int64_t)s.k * (bits + 2) > kMultiDispatchWork)
+    return launch_dispatch_multi(s, topk_idx, counts, offsets, perm, slot, n_dropped, (int32_t*)ws, st);
+  return launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
+}
+
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
-                 int32_t* perm, int32_t* slot, int32_t* n_dropped, moe_stream_t stream) {
+                 int32_t* perm, int32_t* slot, int32_t* n_dropped, void* ws, size_t ws_bytes,
+                 moe_stream_t stream) {
   int v = validate(shape);
   if (v != MOE_OK) return v;
   const moe_shape& s = *shape;
   if (s.T == 0) return MOE_OK;
   if (!topk_idx || !counts || !offsets || !perm || !slot || !n_dropped) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped,
-                                    (hipStream_t)stream));
+  if (ws) {
+    if (ws_bytes < forward_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(dispatch_any(s, topk_idx, counts, offsets, perm, slot, n_dropped, ws, (hipStream_t)stream));
 }
 
 int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm, const int32_t* offsets,
@@ -377,7 +396,8 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   void* ffn_ws = (unsigned char*)ws + align_up((size_t)group_rows(s) * s.D * elem_size(s));
   hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, 0, nullptr,
                               nullptr, st);
-  if (e == hipSuccess) e = launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
+  // the dispatch scratch lives where the expert stage's workspace will be
+  if (e == hipSuccess) e = dispatch_any(s, topk_idx, counts, offsets, perm, slot, n_dropped, ffn_ws, st);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool decode = use_decode(s);
   int r = expert_ffn_impl(s, x, perm, offsets, w1, b1, w3, w2, b2, decode ? nullptr : y_perm, ffn_ws, st);

@@ -45,6 +45,11 @@ hipError_t launch_router_stats(const moe_shape& s, const float* prob_part, const
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                            hipStream_t st);
+// The same dispatch over many workgroups (two launches): bc is device
+// scratch of dispatch_ws_bytes(s) bytes for the per-segment counts.
+size_t dispatch_ws_bytes(const moe_shape& s);
+hipError_t launch_dispatch_multi(const moe_shape& s, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                 int32_t* perm, int32_t* slot, int32_t* n_dropped, int32_t* bc, hipStream_t st);
 // Dispatch with R levels of overflow rerouting (compact layout); rewrites
 // idx and gate of the rerouted assignments.
 hipError_t launch_dispatch_reroute(const moe_shape& s, int R, const int32_t* fb_idx, const float* fb_gate,

@@ -189,7 +189,11 @@ def test_entry_points_reject_null_pointers_before_launch(lib):
     assert lib.moe_route(s, None, fake, None, fake, fake, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(_shape(flags=L.MOE_ROUTER_BIAS)), fake, fake, None, fake, fake,
                          None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_dispatch(s, fake, None, fake, fake, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(s, fake, None, fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # optional scratch: too small, misaligned
+    assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, fake, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, ctypes.c_void_p(0x1001), 1 << 40,
+                            None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, None, fake, None, fake, fake, 1 << 30,
                               None) == L.MOE_ERR_INVALID_ARG  # SwiGLU without w3
     assert lib.moe_expert_ffn(s, fake, fake, fake, fake, None, fake, fake, None, fake, fake, 16,
@@ -225,7 +229,7 @@ def test_zero_tokens_is_a_no_op(lib):
     s = ctypes.byref(_shape(T=0))
     fake = ctypes.c_void_p(0x1000)
     assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
-    assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None) == L.MOE_OK
+    assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None, 0, None) == L.MOE_OK
     assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK
     assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, None, 0, None) == L.MOE_OK
     assert lib.moe_expert_down(s, fake, fake, fake, None, fake, None, 0, None) == L.MOE_OK

@@ -200,6 +200,14 @@ def test_route_shapes(gpu, N, k):
 
 # ------------------------------------------------------------- dispatch
 def _dispatch_case(gpu, idx_np, N, C, priority="token", padded=False):
+    """Both dispatch paths against the oracle: one workgroup (no scratch) and,
+    given the workspace, many workgroups for large batches over many experts
+    (T*k*(bits of N + 2) > 120000)."""
+    for multi in (False, True):
+        _dispatch_once(gpu, idx_np, N, C, priority, padded, multi)
+
+
+def _dispatch_once(gpu, idx_np, N, C, priority, padded, multi):
     T, k = idx_np.shape
     shape = api.MoeShape(T=T, D=64, F=64, N=N, k=k, capacity=-1 if C is None else C, act="relu",
                          slot_major=(priority == "choice"), padded=padded)
@@ -210,7 +218,8 @@ def _dispatch_case(gpu, idx_np, N, C, priority="token", padded=False):
     perm = torch.full((max(shape.group_rows, 1) + 5,), -7, **i32)
     slot = torch.full((T * k,), -7, **i32)
     nd = torch.full((1,), -7, **i32)
-    api.dispatch(shape, idx, counts, offsets, perm, slot, nd)
+    ws = torch.empty(api.workspace_bytes(shape), dtype=torch.uint8, device=gpu) if multi else None
+    api.dispatch(shape, idx, counts, offsets, perm, slot, nd, ws=ws)
     torch.cuda.synchronize()
     ref = oracle.dispatch(idx_np, N, C, priority)
     if padded:
