@@ -14,10 +14,15 @@ Consecutive steps cycle over --copies separate copies of x and the weights,
 so that no step finds its weights in the 256 MB last-level cache from the
 step before.
 
+The timed steps are the same chain captured once per input copy into HIP
+graphs and replayed (W warm-up replays, then K timed ones between
+synchronisations); the eager run before it supplies the per-launch HIP-event
+timings and its own step time ("eager").  --no-graph times the eager steps.
+
 Prints one JSON line: tokens/s of the layer, the roofline of the dominant
 launch (HBM-bound for weight-streaming workloads, MFMA-bound for large
-prefill), the same steps replayed from HIP graphs, and the CPU oracle timed on
-the host on a bounded sample of the same workload.
+prefill), and the CPU oracle timed on the host on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -370,6 +375,11 @@ def main():
         g_ms = g_start.elapsed_time(g_end) / args.steps
         graph = {"ms_per_step": g_ms, "tokens_per_s": cfg.T / (g_ms / 1e3)}
 
+    # the timed steps: the graph replays (the same launches without the host's
+    # per-launch cost, how a serving loop runs the layer), else the eager run
+    eager = {"ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step / 1e3)}
+    if graph is not None:
+        ms_step = graph["ms_per_step"]
     tokens_per_s = cfg.T / (ms_step / 1e3)
     res = {
         "metric": METRIC,
@@ -392,7 +402,9 @@ def main():
                    "expert_shard": args.expert_shard, "input_copies": R},
         "layer_tflops": lflops / (ms_step / 1e3) / 1e12,
         "layer_tflops_frac_bf16_peak": lflops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-        "stages_ms": stages,
+        "timed": "hip_graph_replay" if graph is not None else "eager",
+        "eager": eager,
+        "stages_ms": stages,  # from the eager run, HIP events between the launches
         "graph": graph,
         "routing": {"kept_assignments": kept, "dropped": n_dropped, "experts_used": used,
                     "max_count": int(counts.max()), "imbalance": float(counts.max()) / (A / cfg.N)},
