@@ -679,15 +679,18 @@ __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
     for (int r = 0; r < 4; ++r)
       lg[(kp * TB + mt * 16 + 4 * (lane >> 4) + r) * ldl + nt * 16 + (lane & 15)] = acc[nt][r];
   __syncthreads();
-  // sum the KSPLIT partial tiles in fixed order, add the router bias
-  for (int i = tid; i < TB * R::NP; i += 256) {
-    const int r = i / R::NP, e = i % R::NP;
-    float v = (a.has_bias && e < a.N) ? a.br[e] : 0.f;
+  // sum the KSPLIT partial tiles in fixed order, add the router bias (with a
+  // single partial tile and no bias the tile is already final)
+  if (R::KSPLIT > 1 || a.has_bias) {
+    for (int i = tid; i < TB * R::NP; i += 256) {
+      const int r = i / R::NP, e = i % R::NP;
+      float v = (a.has_bias && e < a.N) ? a.br[e] : 0.f;
 #pragma unroll
-    for (int p = 0; p < R::KSPLIT; ++p) v += lg[(p * TB + r) * ldl + e];
-    lg[r * ldl + e] = v;  // p = 0 tile is overwritten by its own final value only
+      for (int p = 0; p < R::KSPLIT; ++p) v += lg[(p * TB + r) * ldl + e];
+      lg[r * ldl + e] = v;  // p = 0 tile is overwritten by its own final value only
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   rank_rows<bf16, NT, TB / 16>(a, lg, ldl, t0, wave, lane);
 }
