@@ -14,7 +14,8 @@
 //     rank inside its wave is the wave's running count of that expert plus
 //     the same-expert lanes below it; the lowest such lane advances the
 //     running count (wave-private LDS counters, no atomics, no barriers).
-//     The in-wave rank is parked in slot[a].
+//     The in-wave rank is parked in slot[a], or, for up to 24 chunks per
+//     wave, kept in registers together with the expert id until C.
 //  B. per expert, an exclusive scan of the 16 wave counts gives each wave's
 //     base and the expert's total; a scan of min(total, capacity) over the
 //     experts gives offsets.
@@ -38,6 +39,10 @@
 // are the scan of kept + rerouted, and one pass over the assignments writes
 // the final slot and perm (kept rows first, then rerouted ones in level and
 // token order).
+//
+// Large batches over many experts can instead take the two launches of
+// dispatch_count_kernel and dispatch_place_kernel (below), which spread the
+// same ranking over one workgroup per 1024-assignment segment.
 #include "moe_internal.h"
 
 namespace moe {

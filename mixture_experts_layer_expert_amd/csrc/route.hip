@@ -1,14 +1,17 @@
 // Router: logits, softmax and top-k of every token ("Top-k router" section of
 // the notebook "Mixture-of-experts and expert parallelism").
 //
-// One block = 4 waves = 32 tokens.
-//  1. bf16: the block's 32x(16*NT) logit tile is computed with
-//     v_mfma_f32_16x16x32_bf16, D split 4 ways over the waves (partial tiles
-//     summed in LDS), operands read straight from global memory (x rows are
-//     used once; the router matrix is L2-resident).  fp32: VALU dot products.
+// One block = 4 waves.  bf16 with D a multiple of 128: route_ring_kernel,
+// TB = 16/32/64 tokens per block, x rows and the router matrix streamed
+// through an LDS ring by DMA.  Otherwise route_kernel, 32 tokens per block.
+//  1. bf16: the block's token x (16*NT) logit tile is computed with
+//     v_mfma_f32_16x16x32_bf16 (D split over the waves when a wave has no
+//     tile of its own; partial tiles summed in LDS).  fp32: VALU dot
+//     products.
 //  2. A 16-lane group ranks one token: every lane owns experts l, l+16, ...;
-//     k+1 rounds of (value, index) arg-max over the group with xor shuffles.
-//     Larger value wins, equal values go to the lower expert index.
+//     k+1 rounds of (value, index) arg-max over the group, exchanged with DPP
+//     moves inside the 16 lanes.  Larger value wins, equal values go to the
+//     lower expert index.
 //  3. If two of the top-(k+1) fp32 logits are closer than kRefineMargin, the
 //     token is ranked again by its wave from exact logits: only the experts
 //     whose fp32 logit lies within the margin of the (k+1)-th value can change
