@@ -29,13 +29,14 @@ struct GroupedGemm {
   float* part;  // bf16 path: workspace for split-K partial tiles, or nullptr
 };
 
-// Picks the bf16 MFMA tile configuration from the expected rows per expert.
-// With g.part, a partial last round of tiles is split along K into that
-// workspace and finished by a second launch.
+// Picks the bf16 MFMA tile configuration from the expected rows per expert
+// and the most rows any expert can have (max_rows_per_expert).  With g.part,
+// a partial last round of tiles is split along K into that workspace and
+// finished by a second launch.
 hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows_per_expert,
-                                    hipStream_t st);
+                                    int64_t max_rows_per_expert, hipStream_t st);
 // Bytes of g.part the bf16 grouped GEMM may use (both projections).
-size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows_per_expert);
+size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows_per_expert, int64_t max_rows_per_expert);
 hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st);
 
 }  // namespace moe

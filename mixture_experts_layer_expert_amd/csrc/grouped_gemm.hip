@@ -178,6 +178,8 @@ struct TileInfo {
   int e, row0, row_end, n0;
 };
 
+constexpr int kMaxSplit = 8;  // K chunks per left-over tile at most
+
 template <int BM, int BN_OUT>
 struct WorkList {
   int total, rounds, R, S;
@@ -236,6 +238,9 @@ struct WorkList {
     if (can_split && R > 0) {
       s = G / R;
       if (s > KT) s = KT;
+      // more chunks shorten the last round less and less, while the partial
+      // traffic and the finishing work keep growing
+      if (s > kMaxSplit) s = kMaxSplit;
       if (s < 1) s = 1;
     }
     // block-uniform: keep them in scalar registers
@@ -307,69 +312,75 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-// Epilogue of one output tile: acc (this wave's 32x32 sub-tiles, weight rows
-// x tokens) -> bias, activation, bf16 stores.  A lane owns token column
-// (lane & 31) of each 32x32 tile and output rows (r/4)*8 + (lane/32)*4 + r%4;
-// rows of one token are gathered into 16-byte stores by store_block32.
+// Epilogue of one unit of a wave's share of an output tile: the 32 tokens of
+// MFMA block j and 32 output columns, from accumulator a0 (the w1 product
+// and a1 the w3 product under SwiGLU; unit u then pairs 32-row groups 2u and
+// 2u + 1 of the weight tile, otherwise unit u is group u).  A lane owns token
+// column (lane & 31) and output rows (r/4)*8 + (lane/32)*4 + r%4 of the 32x32
+// block; rows of one token are gathered into 16-byte stores by store_block32.
 // LDS_BIAS: bias_lds holds this wave's TN bias values of the tile (the
 // pipelined kernel); otherwise they are read from global memory.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, bool LDS_BIAS>
+__device__ inline void store_unit(const Params& p, const TileInfo& tc, const f32x16& a0, const f32x16& a1,
+                                  int wm, int wn, int j, int u, int lane, const bf16* bias_lds) {
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  const int h4 = (lane >> 5) * 4;
+  const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
+  const bool live = r_out < tc.row_end;
+  bf16* crow = p.C + (size_t)r_out * p.n_out;
+  uint32_t d[4][2];
+  int fbase;
+  if constexpr (ACT == kActSwiGLU) {
+    fbase = tc.n0 + (wn * TL::TN / 64 + u) * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = fast_silu(a0[q * 4 + t]) * a1[q * 4 + t];
+      d[q][0] = pack_bf16x2(v[0], v[1]);
+      d[q][1] = pack_bf16x2(v[2], v[3]);
+    }
+  } else {
+    fbase = tc.n0 + wn * TL::TN + u * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = fbase + q * 8 + h4;
+      bf16x4 bv = {};
+      // (no global load in the pipelined kernel: the compiler's wait for
+      // one would also drain the DMA already in flight)
+      if constexpr (BIAS && LDS_BIAS) bv = *(const bf16x4*)(bias_lds + u * 32 + q * 8 + h4);
+      if constexpr (BIAS && !LDS_BIAS)
+        if (f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float z = a0[q * 4 + t] + (float)bv[t];
+        if constexpr (ACT == kActGelu) z = gelu_erf(z);
+        if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
+        v[t] = z;
+      }
+      d[q][0] = pack_bf16x2(v[0], v[1]);
+      d[q][1] = pack_bf16x2(v[2], v[3]);
+    }
+  }
+  store_block32(crow, fbase, live && fbase < p.n_out, d, lane);
+}
+
+// Epilogue of a wave's whole share of an output tile (acc: its 32x32
+// sub-tiles, weight rows x tokens), unit by unit.
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, bool LDS_BIAS>
 __device__ inline void store_tile(const Params& p, const TileInfo& tc,
                                   f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][Tile<BM, BNB, WM, WN, BK>::FM],
                                   int wm, int wn, int lane, const bf16* bias_lds) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
-  constexpr bool kSwiGLU = (ACT == kActSwiGLU);
-  const int h4 = (lane >> 5) * 4;
+  constexpr int PAIR = (ACT == kActSwiGLU) ? 2 : 1;
 #pragma unroll
   for (int j = 0; j < TL::FM; ++j) {
-    const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
-    const bool live = r_out < tc.row_end;
-    bf16* crow = p.C + (size_t)r_out * p.n_out;
-    if constexpr (kSwiGLU) {
 #pragma unroll
-      for (int ip = 0; ip < TL::FN / 2; ++ip) {
-        const int fbase = tc.n0 + (wn * TL::TN / 64 + ip) * 32;
-        uint32_t d[4][2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            v[u] = fast_silu(acc[2 * ip][j][q * 4 + u]) * acc[2 * ip + 1][j][q * 4 + u];
-          d[q][0] = pack_bf16x2(v[0], v[1]);
-          d[q][1] = pack_bf16x2(v[2], v[3]);
-        }
-        store_block32(crow, fbase, live && fbase < p.n_out, d, lane);
-        __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < TL::FN; ++i) {
-        const int fbase = tc.n0 + wn * TL::TN + i * 32;
-        uint32_t d[4][2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = fbase + q * 8 + h4;
-          bf16x4 bv = {};
-          // (no global load in the pipelined kernel: the compiler's wait for
-          // one would also drain the DMA already in flight)
-          if constexpr (BIAS && LDS_BIAS) bv = *(const bf16x4*)(bias_lds + i * 32 + q * 8 + h4);
-          if constexpr (BIAS && !LDS_BIAS)
-            if (f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
-          float v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float z = acc[i][j][q * 4 + u] + (float)bv[u];
-            if constexpr (ACT == kActGelu) z = gelu_erf(z);
-            if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
-            v[u] = z;
-          }
-          d[q][0] = pack_bf16x2(v[0], v[1]);
-          d[q][1] = pack_bf16x2(v[2], v[3]);
-        }
-        store_block32(crow, fbase, live && fbase < p.n_out, d, lane);
-        __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
-      }
+    for (int u = 0; u < TL::FN / PAIR; ++u) {
+      store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, LDS_BIAS>(p, tc, acc[u * PAIR][j], acc[u * PAIR + PAIR - 1][j], wm,
+                                                          wn, j, u, lane, bias_lds);
+      __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
     }
   }
 }
@@ -381,6 +392,17 @@ template <int FN, int FM>
 __device__ inline float* part_ptr(const Params& p, int q, int nw, int wave, int lane) {
   return p.part + ((size_t)q * nw + wave) * (FN * FM * 16 * 64) + lane;
 }
+
+// Header of the split-K workspace, after the room for G partial tiles:
+// [0] = R (left-over tiles), [1] = S (chunks per tile; 1: nothing split),
+// then from int 4 on, (expert, first row, end row, first column) of each
+// left-over tile.  Written by workgroup 0 of the GEMM, read by the
+// finishing kernel, which then needs no work list of its own.
+template <int BM, int BNB>
+__device__ inline int* split_header(const Params& p, int G) {
+  return (int*)(p.part + (size_t)G * BM * BNB);
+}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
@@ -420,6 +442,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   wl.build(p, s_tile_start, s_scan, s_off, tid, TL::THREADS);
   const int G = gridDim.x;  // multiple of 8
   wl.split(G, KT, p.part != nullptr);
+  if (p.part && blockIdx.x == 0) {
+    // for the finishing kernel (issued before any DMA: an older store only
+    // makes the ring's waits stricter)
+    int* hdr = split_header<BM, BNB>(p, G);
+    if (tid == 0) {
+      hdr[0] = wl.R;
+      hdr[1] = wl.S;
+    }
+    if (wl.S > 1)
+      for (int r = tid; r < wl.R; r += TL::THREADS) {
+        const TileInfo t = wl.info(p, s_tile_start, s_off, wl.rounds * G + r);
+        *(i32x4*)(hdr + 4 + 4 * r) = i32x4{t.e, t.row0, t.row_end, t.n0};
+      }
+  }
 
   // ---- this workgroup's tiles: `rounds` full ones, then at most one more
   // (a whole left-over tile, or one K chunk of one)
@@ -477,12 +513,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     fetch_perm(i + 1);
     jobs_since_fetch = 0;
     if constexpr (BIAS) {
-      // lane l fetches dword min(l, TN/2 - 1) of the slice; a wave past the
-      // last column keeps a valid address (its values are never used)
-      int c0 = t.n0 + wn * TL::TN;
-      if (c0 > p.n_out - TL::TN) c0 = 0;
-      const uint32_t* src =
-          (const uint32_t*)(p.bias + (size_t)t.e * p.n_out + c0) + (lane < TL::TN / 2 ? lane : TL::TN / 2 - 1);
+      // lane l fetches dword min(l, TN/2 - 1) of the wave's slice (two
+      // columns); a column past n_out (a ragged last tile) is clamped to the
+      // last valid dword, so the address stays valid and is never stored
+      int col = t.n0 + wn * TL::TN + 2 * (lane < TL::TN / 2 ? lane : TL::TN / 2 - 1);
+      if (col > p.n_out - 2) col = p.n_out - 2;
+      const uint32_t* src = (const uint32_t*)(p.bias + (size_t)t.e * p.n_out + col);
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&s_bias[wave][i % kBiasSlots][0], 4, 0, 0);
     }
 #pragma unroll
@@ -643,53 +679,53 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
 
 // Second half of the split last round: tile r of the R left-over tiles is
 // the sum of its S partial tiles, in chunk order (deterministic), followed by
-// the epilogue.  One wave per block, block (r, w) finishes wave w's share of
-// tile r with the lane layout of the GEMM, so a lane reads back exactly the
-// accumulator elements it would have held; each chunk's 16*FN*FM values are
-// loaded together.  G: the GEMM's grid.
+// the epilogue.  One wave per block; block (x, w, unit) finishes one epilogue
+// unit (32 tokens x 32 columns, two accumulator blocks under SwiGLU) of wave
+// w's share of tiles x, x + gridDim.x, ..., with the lane layout of the GEMM,
+// so a lane reads back exactly the accumulator elements it would have held.
+// The chunks' loads go out in batches of kBatch.  R, S and the tiles come
+// from the header the GEMM wrote.  G: the GEMM's grid.
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
 __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
-  constexpr int BN_OUT = (ACT == kActSwiGLU) ? BNB / 2 : BNB;
-  __shared__ int s_tile_start[kMaxExperts + 1];
-  __shared__ int s_scan[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
+  constexpr int PAIR = (ACT == kActSwiGLU) ? 2 : 1;
+  constexpr int UPJ = TL::FN / PAIR;  // epilogue units per 32-token block
+  constexpr int kBatch = 4;
+  const int* hdr = split_header<BM, BNB>(p, G);
+  const int R = hdr[0], S = hdr[1];
+  if (S <= 1) return;
   const int lane = threadIdx.x;
   const int wave = blockIdx.y;
   const int wm = wave / WN, wn = wave % WN;
-  WorkList<BM, BN_OUT> wl;
-  wl.build(p, s_tile_start, s_scan, s_off, lane, 64);
-  wl.split(G, p.K / BK, true);
-  if (wl.S == 1) return;
-  for (int r = blockIdx.x; r < wl.R; r += gridDim.x) {
-    const TileInfo tc = wl.info(p, s_tile_start, s_off, wl.rounds * G + r);
-    f32x16 acc[TL::FN][TL::FM];
+  const int j = blockIdx.z / UPJ, u = blockIdx.z % UPJ;
+  for (int r = blockIdx.x; r < R; r += gridDim.x) {
+    const i32x4 ti = *(const i32x4*)(hdr + 4 + 4 * r);
+    const TileInfo tc{ti[0], ti[1], ti[2], ti[3]};
+    f32x16 acc[PAIR];
 #pragma unroll
-    for (int i = 0; i < TL::FN; ++i)
+    for (int pr = 0; pr < PAIR; ++pr)
 #pragma unroll
-      for (int j = 0; j < TL::FM; ++j)
+      for (int e = 0; e < 16; ++e) acc[pr][e] = 0.f;
+    for (int c0 = 0; c0 < S; c0 += kBatch) {
+      f32x16 v[kBatch][PAIR];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    for (int c = 0; c < wl.S; ++c) {
-      const float* src = part_ptr<TL::FN, TL::FM>(p, r * wl.S + c, TL::NW, wave, lane);
-      f32x16 v[TL::FN][TL::FM];
+      for (int b = 0; b < kBatch; ++b)
+        if (c0 + b < S)
 #pragma unroll
-      for (int i = 0; i < TL::FN; ++i)
+          for (int pr = 0; pr < PAIR; ++pr) {
+            const float* src = part_ptr<TL::FN, TL::FM>(p, r * S + c0 + b, TL::NW, wave, lane) +
+                               ((u * PAIR + pr) * TL::FM + j) * 1024;
 #pragma unroll
-        for (int j = 0; j < TL::FM; ++j) {
-          const float* d = src + (i * TL::FM + j) * 1024;
+            for (int e = 0; e < 16; ++e) v[b][pr][e] = src[e * 64];
+          }
+      __builtin_amdgcn_sched_barrier(0);  // the batch's loads in flight together
 #pragma unroll
-          for (int e = 0; e < 16; ++e) v[i][j][e] = d[e * 64];
-        }
-      __builtin_amdgcn_sched_barrier(0);  // all of the chunk's loads in flight together
+      for (int b = 0; b < kBatch; ++b)
+        if (c0 + b < S)
 #pragma unroll
-      for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::FM; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] += v[i][j][e];
+          for (int pr = 0; pr < PAIR; ++pr) acc[pr] += v[b][pr];
     }
-    store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, false>(p, tc, acc, wm, wn, lane, nullptr);
+    store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, false>(p, tc, acc[0], acc[PAIR - 1], wm, wn, j, u, lane, nullptr);
   }
 }
 
@@ -706,9 +742,11 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TL::THREADS), TL::kLdsBytes, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
-  // at most grid/2 left-over tiles are ever split (S >= 2); one wave per block
-  hipLaunchKernelGGL((splitk_finish_kernel<BM, BNB, WM, WN, BK, ACT, BIAS>), dim3(grid / 2, TL::NW), dim3(64),
-                     0, st, p, grid);
+  // at most grid/2 left-over tiles are ever split (S >= 2), two per block
+  // along x; one wave per block
+  constexpr int kUnits = TL::FM * (TL::FN / ((ACT == kActSwiGLU) ? 2 : 1));
+  hipLaunchKernelGGL((splitk_finish_kernel<BM, BNB, WM, WN, BK, ACT, BIAS>), dim3(grid / 4, TL::NW, kUnits),
+                     dim3(64), 0, st, p, grid);
   return hipGetLastError();
 }
 
@@ -722,7 +760,10 @@ hipError_t launch_act(const Params& p, hipStream_t st) {
     case kActRelu:
       return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true>(p, st)
                   : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false>(p, st);
-    case kActSwiGLU: return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false>(p, st);
+    case kActSwiGLU:
+      // the SwiGLU epilogue pairs each wave's w1 and w3 32-row groups
+      if constexpr ((BNB / WN / 32) % 2 == 0) return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false>(p, st);
+      else return hipErrorInvalidValue;
     default:
       return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true>(p, st)
                   : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false>(p, st);
@@ -734,17 +775,28 @@ hipError_t launch_act(const Params& p, hipStream_t st) {
 namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
-enum TileCfg { k256x256w8k64, k128x256w8k64, k32x256w4k64, kNumCfg };
-const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "32x256w4k64"};
-const int kCfgBM[kNumCfg] = {256, 128, 32};
-const int kCfgBN[kNumCfg] = {256, 256, 256};
+enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, kNumCfg };
+const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64"};
+const int kCfgBM[kNumCfg] = {256, 128, 128, 32};
+const int kCfgBN[kNumCfg] = {256, 256, 384, 256};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
-// tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64),
-// small ones 32x256 (4 waves of 32x64).  Output columns per tile: 256 (128
-// for SwiGLU).  MOE_GEMM_TILE (tuning) forces one of the instantiated
-// shapes for both projections, MOE_GEMM_TILE_UP / MOE_GEMM_TILE_DOWN for one.
-TileCfg choose_cfg(int64_t expected_rows, bool up) {
+// tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --
+// or 128x384 (8 waves of 64x96) for the down projection when no group can
+// exceed 128 rows (max_rows, from the capacity) -- and small ones 32x256 (4
+// waves of 32x64).  Output columns per tile: BN (BN/2
+// for SwiGLU, which needs an even number of 32-row groups per wave, so never
+// 128x384).  The wider down tile reads each row of the hidden activations
+// for 384 output columns instead of 256: the A operand (L2 hits, for the
+// most part) is a quarter of the bytes each stage brings in instead of a
+// third.  Those hits share each CU's load path with the weight stream: a
+// weight stage alone streams at about 6.2 TB/s, with a third of its bytes
+// from L2 at about 4.9.  A group of more than 128 rows would need a second,
+// mostly empty row tile that reads the wider weight panels again, which
+// costs more than the narrower tile (measured).  MOE_GEMM_TILE (tuning) forces one of the
+// instantiated shapes for both projections, MOE_GEMM_TILE_UP /
+// MOE_GEMM_TILE_DOWN for one.
+TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up) {
   static const char* forced_all = getenv("MOE_GEMM_TILE");
   static const char* forced_up = getenv("MOE_GEMM_TILE_UP");
   static const char* forced_down = getenv("MOE_GEMM_TILE_DOWN");
@@ -753,7 +805,7 @@ TileCfg choose_cfg(int64_t expected_rows, bool up) {
     for (int c = 0; c < kNumCfg; ++c)
       if (!strcmp(forced, kCfgName[c])) return (TileCfg)c;
   if (expected_rows >= 192) return k256x256w8k64;
-  if (expected_rows >= 48) return k128x256w8k64;
+  if (expected_rows >= 48) return (up || max_rows > 128) ? k128x256w8k64 : k128x384w8k64;
   return k32x256w4k64;
 }
 
@@ -772,13 +824,15 @@ bool allow_split(TileCfg c, const GroupedGemm& g, int64_t expected_rows) {
 
 }  // namespace
 
-size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows) {
-  const TileCfg u = choose_cfg(expected_rows, true), d = choose_cfg(expected_rows, false);
+size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows, int64_t max_rows) {
+  const TileCfg u = choose_cfg(expected_rows, max_rows, true), d = choose_cfg(expected_rows, max_rows, false);
   const int a = kCfgBM[u] * kCfgBN[u], b = kCfgBM[d] * kCfgBN[d];
-  return (size_t)gemm_grid() * (size_t)(a > b ? a : b) * sizeof(float);
+  const size_t G = (size_t)gemm_grid();
+  return G * (size_t)(a > b ? a : b) * sizeof(float) + 16 * (G + 1);  // partial tiles + header
 }
 
-hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows, hipStream_t st) {
+hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows, int64_t max_rows,
+                                    hipStream_t st) {
   Params p;
   p.A = (const bf16*)g.A;
   p.perm = g.perm;
@@ -792,11 +846,12 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.K = g.K;
   p.n_out = g.n_out;
   p.act = g.act;
-  const TileCfg cfg = choose_cfg(expected_rows, g.perm != nullptr);
+  const TileCfg cfg = choose_cfg(expected_rows, max_rows, g.perm != nullptr);
   p.part = (g.part && allow_split(cfg, g, expected_rows)) ? g.part : nullptr;
   switch (cfg) {
     case k256x256w8k64: return launch_act<256, 256, 2, 4, 64>(p, st);
     case k128x256w8k64: return launch_act<128, 256, 2, 4, 64>(p, st);
+    case k128x384w8k64: return launch_act<128, 384, 2, 4, 64>(p, st);
     default: return launch_act<32, 256, 1, 4, 64>(p, st);
   }
 }

@@ -75,6 +75,13 @@ int64_t expected_rows(const moe_shape& s) {
   return expect;
 }
 
+// The most rows any group can hold: the capacity (at most T) for routed
+// experts, T for a shared one.
+int64_t max_rows(const moe_shape& s) {
+  if (s.n_shared > 0 || s.capacity < 0) return s.T;
+  return s.capacity < s.T ? s.capacity : s.T;
+}
+
 bool use_decode(const moe_shape& s) {
   return (s.flags & MOE_FUSED_DECODE) && s.n_shared == 0 && !(s.flags & MOE_PADDED) &&
          decode_applicable(s, expected_rows(s));
@@ -84,7 +91,7 @@ bool use_decode(const moe_shape& s) {
 // of tiles is cut along K when this much workspace is given.
 size_t part_bytes(const moe_shape& s) {
   if (s.dtype != MOE_DTYPE_BF16) return 0;
-  return align_up(grouped_gemm_bf16_part_bytes(expected_rows(s)));
+  return align_up(grouped_gemm_bf16_part_bytes(expected_rows(s), max_rows(s)));
 }
 
 // Workspace of the expert stage: hidden activations H[T*k, F] and the
@@ -125,7 +132,7 @@ hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, con
   g.n_out = s.F;
   g.act = up_act(s);
   g.part = part;
-  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
+  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), max_rows(s), st)
                                    : launch_grouped_gemm_f32(g, st);
 }
 
@@ -147,7 +154,7 @@ hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets
   g.n_out = s.D;
   g.act = kActNone;
   g.part = part;
-  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), st)
+  return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), max_rows(s), st)
                                    : launch_grouped_gemm_f32(g, st);
 }
 

@@ -77,24 +77,35 @@ def test_workspace_bytes_and_validation(lib):
     from mixture_experts_layer_expert_amd import _lib as L
     # prefill-shaped (many rows per expert): y_perm[T*k, D] + H[T*k, F], bf16,
     # + fp32 split-K partial tiles, one 256x256 tile per workgroup of the
-    # persistent grid (one per CU; 256 without a device)
+    # persistent grid (one per CU; 256 without a device), + the split header
+    # (16 bytes per workgroup and 16 more, rounded up to 256)
     grid = 256
+    hdr = (16 * (grid + 1) + 255) // 256 * 256
     rc, n = _ws(lib, _shape(T=4096))
     assert rc == L.MOE_OK
-    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2 + grid * 256 * 256 * 4
+    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2 + grid * 256 * 256 * 4 + hdr
     # decode-shaped (<= 16 rows per expert): grouped GEMM by default (32x256
     # tiles) ...
     rc, n = _ws(lib, _shape(T=64))
     assert rc == L.MOE_OK
-    assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2 + grid * 32 * 256 * 4
+    assert n == 64 * 2 * 128 * 2 + 64 * 2 * 256 * 2 + grid * 32 * 256 * 4 + hdr
     # two shared experts: the grouped rows grow by 2*T
     rc, n = _ws(lib, _shape(T=4096, n_shared=2))
     assert rc == L.MOE_OK
-    assert n == 4096 * 4 * 128 * 2 + 4096 * 4 * 256 * 2 + grid * 256 * 256 * 4
+    assert n == 4096 * 4 * 128 * 2 + 4096 * 4 * 256 * 2 + grid * 256 * 256 * 4 + hdr
     # padded layout, capacity 1536: N*C = 12288 grouped rows instead of T*k
     rc, n = _ws(lib, _shape(T=4096, capacity=1536, flags=L.MOE_PADDED))
     assert rc == L.MOE_OK
-    assert n == 12288 * 128 * 2 + 12288 * 256 * 2 + grid * 256 * 256 * 4
+    assert n == 12288 * 128 * 2 + 12288 * 256 * 2 + grid * 256 * 256 * 4 + hdr
+    # mid-size groups bounded by a capacity of at most 128 rows: 128x256 tiles
+    # up, 128x384 down (the larger partial tile)
+    rc, n = _ws(lib, _shape(T=4096, N=64, capacity=128, act=L.MOE_ACT_RELU))
+    assert rc == L.MOE_OK
+    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2 + grid * 128 * 384 * 4 + hdr
+    # ... not bounded (capacity 192): 128x256 both ways
+    rc, n = _ws(lib, _shape(T=4096, N=64, capacity=192, act=L.MOE_ACT_RELU))
+    assert rc == L.MOE_OK
+    assert n == 4096 * 2 * 128 * 2 + 4096 * 2 * 256 * 2 + grid * 128 * 256 * 4 + hdr
     assert _ws(lib, _shape(n_shared=-1))[0] == L.MOE_ERR_INVALID_ARG
     assert _ws(lib, _shape(N=250, n_shared=7))[0] == L.MOE_ERR_UNSUPPORTED
     # fp32 layers never split

@@ -443,6 +443,95 @@ def test_expert_up_down(gpu, key, scaled_cases):
     assert row_rel_err(y2[:K].float().cpu().numpy().astype(np.float64), y2_ref) <= TOL[cfg.dtype]
 
 
+def _split_plan(cfg, rows, G, up):
+    """Tiles and K chunks per left-over tile of one grouped-GEMM launch, by the
+    library's tile rules (for reporting which split a case exercises)."""
+    T, k, N = cfg.T, cfg.k, cfg.N
+    cap = capacity_of(cfg)
+    cap = -1 if cap is None else cap
+    expect = -(-T * k // N)
+    if cap >= 0:
+        expect = min(expect, cap)
+    max_rows = T if (cfg.n_shared or cap < 0) else min(cap, T)
+    if expect >= 192:
+        bm, bn = 256, 256
+    elif expect >= 48:
+        bm, bn = (128, 256) if (up or max_rows > 128) else (128, 384)
+    else:
+        bm, bn = 32, 256
+    n_out, K = (cfg.F, cfg.D) if up else (cfg.D, cfg.F)
+    bn_out = bn // 2 if (up and cfg.act == "swiglu") else bn
+    ncol = -(-n_out // bn_out)
+    est = (N + cfg.n_shared) * -(-expect // bm) * ncol
+    total = sum(-(-int(r) // bm) * ncol for r in rows)
+    R = total % G
+    S = 1
+    if bm >= 64 and est < 6 * G and R > 0:
+        S = max(1, min(G // R, K // 64, 8))
+    return {"tile": f"{bm}x{bn}", "tiles": total, "R": R, "S": S}
+
+
+SPLIT_CASES = {
+    # mid-size groups capped at 128 rows: 128x256 up, 128x384 down (ragged
+    # 512 = 384 + 128 output columns, with biases)
+    "gelu_bias_S2": scaled_config(get_config("c2", cf=1.0), T=4096, D=512, F=1024, N=64, k=2, act="gelu",
+                                  expert_bias=True, residual=False, name="split_gelu_bias_s2"),
+    "gelu_bias_S8": scaled_config(get_config("c2", cf=1.0), T=1024, D=512, F=1024, N=16, k=2, act="gelu",
+                                  expert_bias=True, residual=False, name="split_gelu_bias_s8"),
+    "swiglu_S8": scaled_config(get_config("c2", cf=1.0), T=1024, D=512, F=1024, N=16, k=2, act="swiglu",
+                               residual=False, name="split_swiglu_s8"),
+    # large groups: 256x256 tiles, few of them
+    "relu_256": scaled_config(get_config("c2", cf=None), T=1024, D=512, F=1024, N=8, k=2, act="relu",
+                              expert_bias=True, residual=False, name="split_relu_256"),
+}
+
+
+@pytest.mark.parametrize("key", sorted(SPLIT_CASES))
+def test_split_last_round(gpu, key):
+    """Layers whose last round of tiles is cut along K into 2..8 chunks (a
+    few tiles on a full grid): the expert stage with the workspace (split,
+    finished by the second launch) and without (never split) both match the
+    oracle; the whole layer twice gives the same bits."""
+    cfg = SPLIT_CASES[key]
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp)
+    off = ref["offsets"]
+    rows = off[1:] - off[:-1]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    G = (cus + 7) // 8 * 8
+    plans = [_split_plan(cfg, rows, G, up) for up in (True, False)]
+    _say(f"split {key}: T={cfg.T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k} {cfg.act} G={G} up={plans[0]} "
+         f"down={plans[1]}")
+    if G == 256:  # the cases are sized for a 256-CU part
+        assert max(p["S"] for p in plans) >= 2
+    g = to_gpu(inp)
+    shape = api.MoeShape.from_config(cfg)
+    buf = api.MoeBuffers(shape)
+    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
+    api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
+    A = shape.group_rows
+    K = int(off[-1])
+    ys = {}
+    for mode, ws in (("split", buf.ws), ("plain", None)):
+        h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=gpu)
+        y = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
+        api.expert_up(shape, g["x"], buf.perm, buf.offsets, g["w1"], g["b1"], g["w3"], h, ws)
+        api.expert_down(shape, h, buf.offsets, g["w2"], g["b2"], y, ws)
+        torch.cuda.synchronize()
+        ys[mode] = y[:K].float().cpu().numpy().astype(np.float64)
+        err = row_rel_err(ys[mode], ref["y_perm"])
+        _say(f"  {mode}: y_perm row-rel err {err:.3e}")
+        assert err <= TOL[cfg.dtype]
+    check_routing(buf, ref, cfg)
+    buf.forward(g["x"], g)
+    torch.cuda.synchronize()
+    out1 = buf.out.clone()
+    check_outputs(out1.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
+    buf.forward(g["x"], g)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, buf.out)
+
+
 @pytest.mark.parametrize("key,T", [("c3", 1500), ("c5", None), ("c1", None)])
 def test_forward_choice_priority(gpu, key, T):
     """Whole layer with MOE_SLOT_MAJOR and a capacity that drops: routing
