@@ -813,13 +813,18 @@ TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up) {
 // launch): only when the expected work is a few rounds of large tiles, where
 // a partial last round idles a sizeable share of the GPU.  The estimate uses
 // the mean rows per expert; a wrong guess costs time, never correctness
-// (without p.part the kernel never splits).
-bool allow_split(TileCfg c, const GroupedGemm& g, int64_t expected_rows) {
+// (without p.part the kernel never splits).  When no group can exceed one
+// row tile, the estimate is the most tiles there can be: a whole number of
+// rounds then leaves nothing over when every expert is used, and the second
+// launch would only find nothing to do.
+bool allow_split(TileCfg c, const GroupedGemm& g, int64_t expected_rows, int64_t max_rows) {
   if (kCfgBM[c] < 64) return false;
   const int bn_out = g.act == kActSwiGLU ? kCfgBN[c] / 2 : kCfgBN[c];
   const int64_t est = (int64_t)g.n_experts * ((expected_rows + kCfgBM[c] - 1) / kCfgBM[c]) *
                       ((g.n_out + bn_out - 1) / bn_out);
-  return est < 6 * (int64_t)gemm_grid();
+  const int64_t G = gemm_grid();
+  if (max_rows <= kCfgBM[c] && est % G == 0) return false;
+  return est < 6 * G;
 }
 
 }  // namespace
@@ -847,7 +852,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.n_out = g.n_out;
   p.act = g.act;
   const TileCfg cfg = choose_cfg(expected_rows, max_rows, g.perm != nullptr);
-  p.part = (g.part && allow_split(cfg, g, expected_rows)) ? g.part : nullptr;
+  p.part = (g.part && allow_split(cfg, g, expected_rows, max_rows)) ? g.part : nullptr;
   switch (cfg) {
     case k256x256w8k64: return launch_act<256, 256, 2, 4, 64>(p, st);
     case k128x256w8k64: return launch_act<128, 256, 2, 4, 64>(p, st);

@@ -466,7 +466,8 @@ def _split_plan(cfg, rows, G, up):
     total = sum(-(-int(r) // bm) * ncol for r in rows)
     R = total % G
     S = 1
-    if bm >= 64 and est < 6 * G and R > 0:
+    allow = bm >= 64 and est < 6 * G and not (max_rows <= bm and est % G == 0)
+    if allow and R > 0:
         S = max(1, min(G // R, K // 64, 8))
     return {"tile": f"{bm}x{bn}", "tiles": total, "R": R, "S": S}
 
