@@ -203,10 +203,10 @@ int moe_router_stats(const moe_shape* shape, const void* stats_ws, size_t stats_
  * ws is optional device scratch. With ws = NULL, one workgroup does the whole
  * dispatch in one launch. Otherwise ws needs at least
  * moe_workspace_bytes(shape) bytes with 256-byte alignment (MOE_ERR_WORKSPACE
- * or MOE_ERR_INVALID_ARG otherwise). Large batches with many experts then take
- * two launches over many workgroups: segments of the priority order are
- * ranked apart and placed from their fixed-order counts. "Large" means T*k
- * times (bits of N + 2) above 120000. The results are identical. */
+ * or MOE_ERR_INVALID_ARG otherwise). Batches of more than 4096 assignments
+ * (T*k) then take two launches over many workgroups: segments of the
+ * priority order are ranked apart and placed from their fixed-order counts.
+ * The results are identical. */
 int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                  void* ws, size_t ws_bytes, moe_stream_t stream);

@@ -594,21 +594,33 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* idx, int32_t* coun
   hipLaunchKernelGGL((dispatch_kernel<false, BITS, CH>), dim3(1), dim3(kThreads), 0, st, idx_rw, A, s.T, s.k,     \
                      by_choice, s.N, s.capacity, s.n_shared, pad, counts, offsets, perm, slot, n_dropped, 0, nullptr, \
                      nullptr, nullptr)
-  if (per <= kRegChunks) {
-    switch (bits) {
-      case 0: MOE_DISPATCH(0, kRegChunks); break;
-      case 1: MOE_DISPATCH(1, kRegChunks); break;
-      case 2: MOE_DISPATCH(2, kRegChunks); break;
-      case 3: MOE_DISPATCH(3, kRegChunks); break;
-      case 4: MOE_DISPATCH(4, kRegChunks); break;
-      case 5: MOE_DISPATCH(5, kRegChunks); break;
-      case 6: MOE_DISPATCH(6, kRegChunks); break;
-      case 7: MOE_DISPATCH(7, kRegChunks); break;
-      default: MOE_DISPATCH(8, kRegChunks); break;
-    }
+#define MOE_DISPATCH_BITS(CH)        \
+  switch (bits) {                     \
+    case 0: MOE_DISPATCH(0, CH); break; \
+    case 1: MOE_DISPATCH(1, CH); break; \
+    case 2: MOE_DISPATCH(2, CH); break; \
+    case 3: MOE_DISPATCH(3, CH); break; \
+    case 4: MOE_DISPATCH(4, CH); break; \
+    case 5: MOE_DISPATCH(5, CH); break; \
+    case 6: MOE_DISPATCH(6, CH); break; \
+    case 7: MOE_DISPATCH(7, CH); break; \
+    default: MOE_DISPATCH(8, CH); break; \
+  }
+  // The register mode's chunk loops are unrolled, so the code grows with CH
+  // (about 65 KB at 24 chunks).  A launch that follows the expert GEMMs finds
+  // its code evicted from every cache, and fetching it took most of a small
+  // batch's dispatch (20 us of 6 for 768 assignments): small batches take the
+  // smallest register mode that holds them.
+  if (per <= 1) {
+    MOE_DISPATCH_BITS(1)
+  } else if (per <= 4) {
+    MOE_DISPATCH_BITS(4)
+  } else if (per <= kRegChunks) {
+    MOE_DISPATCH_BITS(kRegChunks)
   } else {
     MOE_DISPATCH(-1, 0);
   }
+#undef MOE_DISPATCH_BITS
 #undef MOE_DISPATCH
   return hipGetLastError();
 }

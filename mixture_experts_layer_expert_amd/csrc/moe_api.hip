@@ -286,17 +286,18 @@ int moe_dispatch_reroute(const moe_shape* shape, int32_t n_fallback, const int32
                                             perm, slot, n_dropped, (hipStream_t)stream));
 }
 
-// Dispatch over many workgroups when scratch is at hand and the single
-// workgroup's work, about A * (expert-id bits + 2) ballot steps, exceeds what
-// the second launch costs (measured: worth it for 16384 assignments over 128
-// experts and 24576 over 64, not for 16384 over 8 or 16); one workgroup
-// otherwise.  The results are identical.
-constexpr int64_t kMultiDispatchWork = 120000;
+// Dispatch over many workgroups when scratch is at hand and the batch has
+// more than kSmallDispatch assignments; one workgroup otherwise.  The results
+// are identical.  Timed inside the whole layer (graph replays): with 768
+// assignments one workgroup (its smallest register mode) beats two launches,
+// 0.233 against 0.237 ms per step; with 16384 over 16 experts two launches
+// win, 0.427 against 0.436 ms, and over 8 experts they tie.  (Timed alone, one
+// workgroup looked better for 16384 assignments over 8 or 16 experts: there
+// its 65 KB of unrolled code stays cached, which it does not in the layer.)
+constexpr int64_t kSmallDispatch = 4096;
 static hipError_t dispatch_any(const moe_shape& s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                                int32_t* perm, int32_t* slot, int32_t* n_dropped, void* ws, hipStream_t st) {
-  int bits = 0;
-  while ((1 << bits) < s.N) ++bits;
-  if (ws && s.T * (int64_t)s.k * (bits + 2) > kMultiDispatchWork)
+  if (ws && s.T * (int64_t)s.k > kSmallDispatch)
     return launch_dispatch_multi(s, topk_idx, counts, offsets, perm, slot, n_dropped, (int32_t*)ws, st);
   return launch_dispatch(s, topk_idx, counts, offsets, perm, slot, n_dropped, st);
 }

@@ -200,9 +200,10 @@ def test_route_shapes(gpu, N, k):
 
 # ------------------------------------------------------------- dispatch
 def _dispatch_case(gpu, idx_np, N, C, priority="token", padded=False):
-    """Both dispatch paths against the oracle: one workgroup (no scratch) and,
-    given the workspace, many workgroups for large batches over many experts
-    (T*k*(bits of N + 2) > 120000)."""
+    """Both dispatch paths against the oracle: one workgroup (no scratch; its
+    register mode of 1, 4 or 24 chunks per wave, or none, by batch size) and,
+    given the workspace, many workgroups for batches of more than 4096
+    assignments."""
     for multi in (False, True):
         _dispatch_once(gpu, idx_np, N, C, priority, padded, multi)
 
@@ -242,7 +243,8 @@ def _rand_idx(rng, T, N, k, p=None):
 
 
 @pytest.mark.parametrize("T,N,k,C", [
-    (1, 1, 1, None), (1, 4, 4, None), (777, 8, 2, None), (777, 8, 2, 150), (2000, 128, 1, 15),
+    (1, 1, 1, None), (1, 4, 4, None), (128, 64, 6, None), (500, 64, 2, 40), (1024, 8, 1, None),
+    (777, 8, 2, None), (777, 8, 2, 150), (2000, 128, 1, 15),
     (2000, 128, 1, 0), (3001, 16, 2, 1), (5000, 64, 6, None), (5000, 64, 6, 50), (5000, 64, 6, 480),
     (16384, 128, 1, 128), (40000, 256, 2, 300),
 ])
