@@ -15,7 +15,9 @@
 //     the same-expert lanes below it; the lowest such lane advances the
 //     running count (wave-private LDS counters, no atomics, no barriers).
 //     The in-wave rank is parked in slot[a], or, for up to 24 chunks per
-//     wave, kept in registers together with the expert id until C.
+//     wave, kept in registers together with the expert id until C (register
+//     modes of 1, 4 and 24 chunks: the smallest that holds the batch, since
+//     the unrolled code grows with the count).
 //  B. per expert, an exclusive scan of the 16 wave counts gives each wave's
 //     base and the expert's total; a scan of min(total, capacity) over the
 //     experts gives offsets.
@@ -40,9 +42,9 @@
 // the final slot and perm (kept rows first, then rerouted ones in level and
 // token order).
 //
-// Large batches over many experts can instead take the two launches of
-// dispatch_count_kernel and dispatch_place_kernel (below), which spread the
-// same ranking over one workgroup per 1024-assignment segment.
+// Batches of more than 4096 assignments can instead take the two launches
+// of dispatch_count_kernel and dispatch_place_kernel (below), which spread
+// the same ranking over one workgroup per 1024-assignment segment.
 #include "moe_internal.h"
 
 namespace moe {
