@@ -277,8 +277,9 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
  * ws: NULL, or scratch of at least moe_workspace_bytes(shape) bytes (256-byte
  * aligned) that lets a bf16 projection split its last, partial round of
  * tiles along K (fp32 partial sums, added in a fixed order by a second
- * launch); results then equal those of moe_expert_ffn and moe_forward, which
- * always split.  A too-small ws returns MOE_ERR_WORKSPACE.
+ * launch, only where the tile count leaves such a round); results then equal
+ * those of moe_expert_ffn and moe_forward, which always hand the kernels
+ * their workspace.  A too-small ws returns MOE_ERR_WORKSPACE.
  *
  * moe_expert_up: the expert's first projection and activation (the
  * notebook's Expert: fc1 then GELU or ReLU, biases with MOE_HAS_BIAS; for
