@@ -37,6 +37,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows_
                                     int64_t max_rows_per_expert, hipStream_t st);
 // Bytes of g.part the bf16 grouped GEMM may use (both projections).
 size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows_per_expert, int64_t max_rows_per_expert);
-hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, hipStream_t st);
+// fp32 (VALU) grouped GEMM; the expected rows per expert pick the tile height.
+hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, int64_t expected_rows_per_expert, hipStream_t st);
 
 }  // namespace moe

@@ -133,7 +133,7 @@ hipError_t launch_up(const moe_shape& s, const void* x, const int32_t* perm, con
   g.act = up_act(s);
   g.part = part;
   return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), max_rows(s), st)
-                                   : launch_grouped_gemm_f32(g, st);
+                                   : launch_grouped_gemm_f32(g, expected_rows(s), st);
 }
 
 // fc2: y_perm[r] = H[r] . w2[e]^T (+ b2[e]).
@@ -155,7 +155,7 @@ hipError_t launch_down(const moe_shape& s, const void* h, const int32_t* offsets
   g.act = kActNone;
   g.part = part;
   return s.dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(g, expected_rows(s), max_rows(s), st)
-                                   : launch_grouped_gemm_f32(g, st);
+                                   : launch_grouped_gemm_f32(g, expected_rows(s), st);
 }
 
 int expert_ffn_impl(const moe_shape& s, const void* x, const int32_t* perm, const int32_t* offsets,
