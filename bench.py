@@ -58,34 +58,34 @@ CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, 
 PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
                       "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h")
 PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
-    "c2": {"sources": "91e5a741340fd26e",
-           "fc1": {"fetch_kib": 309513.1, "write_kib": 91794.7},
+    "c2": {"sources": "c6189f206312eb9b",
+           "fc1": {"fetch_kib": 309457.2, "write_kib": 91794.2},
            # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 0, 3>
-           "fc2": {"fetch_kib": 340983.3, "write_kib": 22962.3},
+           "fc2": {"fetch_kib": 341009.7, "write_kib": 22970.5},
            # grouped_gemm_kernel<128, 384, 2, 4, 64, 0, 0, 2>
            },
-    "c4": {"sources": "91e5a741340fd26e",
-           "fc1": {"fetch_kib": 3362363.0, "write_kib": 458947.9},
+    "c4": {"sources": "c6189f206312eb9b",
+           "fc1": {"fetch_kib": 3361892.7, "write_kib": 458916.3},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2>
-           "fc2": {"fetch_kib": 1749097.5, "write_kib": 206439.5},
+           "fc2": {"fetch_kib": 1751301.1, "write_kib": 207205.8},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
-    "c5": {"sources": "91e5a741340fd26e",
-           "fc1": {"fetch_kib": 363842.6, "write_kib": 2117.4},
+    "c5": {"sources": "c6189f206312eb9b",
+           "fc1": {"fetch_kib": 363830.1, "write_kib": 2117.5},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 0, 4>
-           "fc2": {"fetch_kib": 181447.0, "write_kib": 3072.1},
+           "fc2": {"fetch_kib": 181424.5, "write_kib": 3072.1},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 0, 4>
            },
-    "c3": {"sources": "91e5a741340fd26e",
-           "fc1": {"fetch_kib": 148376.7, "write_kib": 140434.0},
+    "c3": {"sources": "c6189f206312eb9b",
+           "fc1": {"fetch_kib": 148374.3, "write_kib": 141576.7},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 1, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 1, 1>
-           "fc2": {"fetch_kib": 212318.9, "write_kib": 89672.3},
+           "fc2": {"fetch_kib": 212318.8, "write_kib": 89725.9},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 1>
            },
-    "c6": {"sources": "91e5a741340fd26e",
-           "fc1": {"fetch_kib": 584180.0, "write_kib": 90131.7},
+    "c6": {"sources": "c6189f206312eb9b",
+           "fc1": {"fetch_kib": 584125.9, "write_kib": 90145.4},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 3, 0>
-           "fc2": {"fetch_kib": 261815.9, "write_kib": 133229.1},
+           "fc2": {"fetch_kib": 266221.2, "write_kib": 133114.6},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
 }
