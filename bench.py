@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import hashlib
+import re
 import json
 import os
 import sys
@@ -58,31 +59,31 @@ CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, 
 PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
                       "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h")
 PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
-    "c2": {"sources": "c6189f206312eb9b",
+    "c2": {"sources": "4649bdfacb8eed23",
            "fc1": {"fetch_kib": 309457.2, "write_kib": 91794.2},
            # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 0, 3>
            "fc2": {"fetch_kib": 341009.7, "write_kib": 22970.5},
            # grouped_gemm_kernel<128, 384, 2, 4, 64, 0, 0, 2>
            },
-    "c4": {"sources": "c6189f206312eb9b",
+    "c4": {"sources": "4649bdfacb8eed23",
            "fc1": {"fetch_kib": 3361892.7, "write_kib": 458916.3},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2>
            "fc2": {"fetch_kib": 1751301.1, "write_kib": 207205.8},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
            },
-    "c5": {"sources": "c6189f206312eb9b",
+    "c5": {"sources": "4649bdfacb8eed23",
            "fc1": {"fetch_kib": 363830.1, "write_kib": 2117.5},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 0, 4>
            "fc2": {"fetch_kib": 181424.5, "write_kib": 3072.1},
            # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 0, 4>
            },
-    "c3": {"sources": "c6189f206312eb9b",
+    "c3": {"sources": "4649bdfacb8eed23",
            "fc1": {"fetch_kib": 148374.3, "write_kib": 141576.7},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 1, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 1, 1>
            "fc2": {"fetch_kib": 212318.8, "write_kib": 89725.9},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 1>
            },
-    "c6": {"sources": "c6189f206312eb9b",
+    "c6": {"sources": "4649bdfacb8eed23",
            "fc1": {"fetch_kib": 584125.9, "write_kib": 90145.4},
            # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 3, 0>
            "fc2": {"fetch_kib": 266221.2, "write_kib": 133114.6},
@@ -148,11 +149,19 @@ def layer_flops(cfg, counts_kept):
     return 2.0 * cfg.T * cfg.D * cfg.N + 2.0 * counts_kept * cfg.D * cfg.F * nproj
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks and empty lines: edits to
+    comments alone leave the kernel, and so its counters, unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def sources_sha():
     h = hashlib.sha256()
     for rel in PMC_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -18,23 +18,28 @@
 // routing skew.  One persistent launch covers the whole list (the pieces of
 // all experts fused into one kernel, same abstract).
 //
-// Scheduling.  Grid = a multiple of 8 persistent workgroups.  Workgroups are
-// dealt to the 8 XCDs round-robin by id, so XCD x = id % 8 is given the
-// contiguous eighth [x*P, (x+1)*P) of the list; its workgroups stride through
-// it.  Tiles that are adjacent in the list share a weight panel (row tile
-// varies fastest), so they meet in the same XCD's L2.
+// Scheduling.  Grid = one persistent workgroup per CU, a multiple of 8.
+// Workgroups are dealt to the 8 XCDs round-robin by id, so XCD x = id % 8 is
+// given a contiguous block of the full rounds' tiles; its workgroups stride
+// through it.  Tiles that are adjacent in the list share a weight or row
+// panel (row tiles in groups of 8 within an expert), so they meet in the same
+// XCD's L2.  A partial last round is dealt round-robin over the XCDs and,
+// given a workspace, cut along K (the split, finished by a second launch).
 //
-// Tile pipeline.  4 waves.  K is consumed 64 at a time (a "job" is one k
-// step of one tile).  Both operand tiles go global -> LDS with
-// global_load_lds_dwordx4 (no register staging) into a 2- or 3-stage ring
-// fed as one continuous stream of jobs, so the next tile's first k steps load
-// while the current tile finishes; a wave-instruction fills 1 KiB = 8 rows x
-// 128 B.  Fragments are read from LDS one k sub-step ahead of the MFMAs.  Inside a
-// row the eight 16-byte chunks are XOR-swizzled by the row index so that the
-// MFMA fragment reads (ds_read_b128, one row per lane) are conflict-free.
-// MFMA v_mfma_f32_32x32x16_bf16 with the weight tile as the first operand:
-// each lane then owns 4 consecutive output columns of one row, which the
-// epilogue stores as 8-byte chunks.
+// Tile shapes (rows x weight rows, waves): 256x256 (8 waves), 128x256 (8),
+// 128x384 (8, down projection only) and 32x256 (4), picked from the rows per
+// expert.  Tile pipeline: K is consumed 64 at a time (a "job" is one k step of
+// one tile).  Both operand tiles go global -> LDS with
+// global_load_lds_dwordx4 (no register staging) into a ring of as many
+// stages as fit (2 to 4), fed as one continuous stream of jobs, so the next
+// tile's first k steps load while the current tile finishes; a
+// wave-instruction fills 1 KiB = 8 rows x 128 B.  Fragments are read from
+// LDS one k sub-step ahead of the MFMAs.  Inside a row the eight 16-byte
+// chunks are XOR-swizzled by the row index so that the MFMA fragment reads
+// (ds_read_b128, one row per lane) are conflict-free.  MFMA
+// v_mfma_f32_32x32x16_bf16 with the weight tile as the first operand: each
+// lane then owns 4 consecutive output columns of one row; lanes l and l+32
+// swap halves so that the epilogue stores 16 bytes per lane.
 #include <stdlib.h>
 #include <string.h>
 
