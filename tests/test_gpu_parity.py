@@ -535,6 +535,21 @@ def test_split_last_round(gpu, key):
     assert torch.equal(out1, buf.out)
 
 
+@pytest.mark.parametrize("T", [256, 512, 1024])
+def test_forward_fp32_tile_heights(gpu, T):
+    """The tiny fp32 layer at sizes whose up projection takes 16-, 32- and
+    64-row tiles (on a 256-CU part: the tallest tile whose expected count
+    fills half of the 4-per-CU grid), against the oracle."""
+    cfg = get_config("c1") if T == 1024 else scaled_config(get_config("c1"), T=T, name=f"c1_T{T}")
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp)
+    _say(f"fp32 tiles T={T}")
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g)
+    check_routing(buf, ref, cfg)
+    check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
+
+
 @pytest.mark.parametrize("key,T", [("c3", 1500), ("c5", None), ("c1", None)])
 def test_forward_choice_priority(gpu, key, T):
     """Whole layer with MOE_SLOT_MAJOR and a capacity that drops: routing
