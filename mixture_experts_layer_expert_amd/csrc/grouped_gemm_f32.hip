@@ -1,15 +1,19 @@
-// Grouped GEMM of the expert MLPs in fp32 (VALU), for fp32 layers such as
-// the notebook's own 1024-token example ("Dispatch and gather" section of
+// Grouped GEMM of the expert MLPs in fp32, for fp32 layers such as the
+// notebook's own 1024-token example ("Dispatch and gather" section of
 // "Mixture-of-experts and expert parallelism").  Same contract and work list
-// as the bf16 MFMA kernel: (expert, 64-row tile, 64-column tile) items for
-// all experts in one persistent launch; rows of x gathered through perm for
-// fc1; bias + GELU/ReLU or SwiGLU fused into the store.
+// as the bf16 kernel: (expert, row tile, 64-column tile) items for all
+// experts in one persistent launch; rows of x gathered through perm for fc1;
+// bias + GELU/ReLU or SwiGLU fused into the store.
 //
 // Tile: TBM x 64 outputs (TBM = 64, 32 or 16 rows: the tallest whose
-// expected tile count still fills half the grid), 256 threads, TBM/16 x 4 outputs
-// per thread, k step 16, operands staged k-major in LDS so that each thread
-// reads its rows and 4 columns as vectors; the next k step's operands are
-// loaded into registers while the current one is computed.
+// expected tile count still fills half the grid), 4 waves.  Wave w owns
+// output columns 16w .. 16w+15 and computes them for every row of the tile
+// with v_mfma_f32_16x16x4f32 (fp32 products, fp32 accumulation): lane l
+// feeds row (l % 16) of the 16-row block and column (l % 16) of the wave's
+// columns at k offset l / 16, and holds outputs (rows 4*(l/16) + v, column
+// l % 16).  Operands are staged k-major in LDS, 16 k per step, and the next
+// step's operands are loaded into registers while the current one is
+// computed.
 #include "moe_internal.h"
 
 namespace moe {
@@ -37,11 +41,14 @@ __device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
 template <bool SWIGLU, int TBM>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(ParamsF p) {
-  constexpr int RPT = TBM / 16;  // output rows per thread
-  static_assert(RPT == 1 || RPT == 2 || RPT == 4, "16, 32 or 64 rows");
-  __shared__ float sA[TBK][TBM + 4];
-  __shared__ float sB[TBK][TBN + 4];
-  __shared__ float sB2[SWIGLU ? TBK : 1][TBN + 4];
+  constexpr int MT = TBM / 16;  // 16-row MFMA blocks per wave
+  static_assert(MT == 1 || MT == 2 || MT == 4, "16, 32 or 64 rows");
+  // row stride of the k-major tiles: the four 16-lane groups of an operand
+  // read (one k each) start 80 floats apart, on different banks
+  constexpr int LDW = 80;
+  __shared__ float sA[TBK][LDW];
+  __shared__ float sB[TBK][LDW];
+  __shared__ float sB2[SWIGLU ? TBK : 1][LDW];
   __shared__ int s_tile_start[kMaxExperts + 1];
   __shared__ int s_scan[kMaxExperts];
   const int tid = threadIdx.x;
@@ -67,7 +74,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(ParamsF p) {
   __syncthreads();
   const int total = s_tile_start[N];
 
-  const int tr = tid / 16, tc = tid % 16;  // 16x16 threads, RPT x 4 outputs each
+  const int wave = tid / 64, lane = tid % 64;
+  const int lr = lane % 16, lk = lane / 16;  // MFMA operand row/column, k offset
   // loader mapping: 64 rows x 16 k = 1024 floats = 256 float4s for B; the
   // first TBM * 4 threads load the TBM rows of A the same way
   const int ld_row = tid / 4, ld_k4 = (tid % 4) * 4;
@@ -97,8 +105,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(ParamsF p) {
     const float* b_src = p.B + ((size_t)e * p.n_out + fb) * p.K + ld_k4;
     const float* b2_src = SWIGLU ? p.B2 + ((size_t)e * p.n_out + fb) * p.K + ld_k4 : nullptr;
 
-    float acc[RPT][4] = {};
-    float acc3[SWIGLU ? RPT : 1][SWIGLU ? 4 : 1] = {};
+    f32x4 acc[MT], acc3[SWIGLU ? MT : 1];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < (SWIGLU ? MT : 1); ++i) acc3[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the operands of k step k0 + TBK are loaded into registers while step
     // k0 is computed from LDS, so each step's global latency is hidden
     float4 av = ld_a ? *(const float4*)a_src : float4{};
@@ -128,52 +139,35 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(ParamsF p) {
         if constexpr (SWIGLU) b3 = *(const float4*)(b2_src + k0 + TBK);
       }
 #pragma unroll
-      for (int kk = 0; kk < TBK; ++kk) {
-        float a_[RPT];
-        if constexpr (RPT == 4) {
-          const float4 a4 = *(const float4*)&sA[kk][tr * 4];
-          a_[0] = a4.x; a_[1] = a4.y; a_[2] = a4.z; a_[3] = a4.w;
-        } else if constexpr (RPT == 2) {
-          const float2 a2 = *(const float2*)&sA[kk][tr * 2];
-          a_[0] = a2.x; a_[1] = a2.y;
-        } else {
-          a_[0] = sA[kk][tr];
-        }
-        float4 b4 = *(const float4*)&sB[kk][tc * 4];
-        const float b_[4] = {b4.x, b4.y, b4.z, b4.w};
+      for (int ks = 0; ks < TBK / 4; ++ks) {
+        const float bv_ = sB[4 * ks + lk][16 * wave + lr];
+        float b3_ = 0.f;
+        if constexpr (SWIGLU) b3_ = sB2[4 * ks + lk][16 * wave + lr];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a_[i], b_[j], acc[i][j]);
-        if constexpr (SWIGLU) {
-          float4 c4 = *(const float4*)&sB2[kk][tc * 4];
-          const float c_[4] = {c4.x, c4.y, c4.z, c4.w};
-#pragma unroll
-          for (int i = 0; i < RPT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc3[i][j] = fmaf(a_[i], c_[j], acc3[i][j]);
+        for (int i = 0; i < MT; ++i) {
+          const float av_ = sA[4 * ks + lk][16 * i + lr];
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av_, bv_, acc[i], 0, 0, 0);
+          if constexpr (SWIGLU) acc3[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av_, b3_, acc3[i], 0, 0, 0);
         }
       }
       __syncthreads();
     }
+    const int f = n0 + 16 * wave + lr;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int ro = row0 + tr * RPT + i;
-      if (ro >= row_end) continue;
-      float* crow = p.C + (size_t)ro * p.n_out;
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = n0 + tc * 4 + j;
-        if (f >= p.n_out) continue;
-        float z = acc[i][j];
+      for (int v = 0; v < 4; ++v) {
+        const int ro = row0 + 16 * i + 4 * lk + v;
+        if (ro >= row_end || f >= p.n_out) continue;
+        float z = acc[i][v];
         if constexpr (SWIGLU) {
-          z = silu(z) * acc3[i][j];
+          z = silu(z) * acc3[i][v];
         } else {
           if (p.bias) z += p.bias[(size_t)e * p.n_out + f];
           if (p.act == kActGelu) z = gelu_erf(z);
           else if (p.act == kActRelu) z = fmaxf(z, 0.f);
         }
-        crow[f] = z;
+        p.C[(size_t)ro * p.n_out + f] = z;
       }
     }
   }
