@@ -191,11 +191,11 @@ hipError_t launch_grouped_gemm_f32(const GroupedGemm& g, int64_t expected_rows, 
   p.act = g.act;
   const int grid = device_cu_count() * 4;
   // tile height: the tallest whose expected tile count fills half the grid
-  // (two blocks per CU), else 16 rows.  Shorter tiles do less register
-  // blocking per LDS read, so they pay only where the launch would
-  // otherwise leave most CUs idle (measured on the 1024-token layer: the up
-  // projection, 512 tiles of 64 rows, 35 us, 39 us at 32 rows; the down
-  // projection, 128 tiles of 64 rows, 60 us, 55 us at 16 rows).
+  // (two blocks per CU), else 16 rows.  Shorter tiles give each wave fewer
+  // MFMA blocks per B operand read, so they pay only where the launch would
+  // otherwise leave most CUs idle (measured on the 1024-token layer, 64 / 32
+  // / 16 rows: the up projection, 512 tiles at 64 rows, 30.6 / 29.8 / 32.8
+  // us; the down projection, 128 tiles at 64 rows, 43.1 / 37.5 / 35.6 us).
   const int64_t ncol = (g.n_out + TBN - 1) / TBN;
   const int64_t er = expected_rows > 0 ? expected_rows : 1;
   auto tiles = [&](int tbm) { return (int64_t)g.n_experts * ((er + tbm - 1) / tbm) * ncol; };
