@@ -41,7 +41,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
-PEAK_FP32_TFLOPS = 157.3       # fp32 vector
+PEAK_FP32_TFLOPS = 157.3       # fp32 dense MFMA (the fp32 grouped GEMM runs on v_mfma_f32_16x16x4f32)
 METRIC = "MoE layer fwd tokens/s + TFLOP/s (% bf16 MFMA peak) or GB/s (% HBM peak), 1 GPU"
 
 # CPU-baseline sample (tokens) per workload: the oracle in fp64 on the host's
@@ -342,17 +342,14 @@ def main():
     launch = "fc1" if stages["fc1"] >= stages["fc2"] else "fc2"
     flops, bytes_ = work[launch]["flops"], work[launch]["bytes"]
     t_s = stages[launch] / 1e3
-    if cfg.dtype == "bf16":
-        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        bound = "hbm" if flops / bytes_ < ridge else "mfma"
-    else:
-        bound = "alu"
+    # both paths contract on MFMA: bf16 (2.5 PFLOP/s dense) or fp32 (157.3)
+    mfma_peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if flops / bytes_ < ridge else "mfma"
     if bound == "hbm":
         achieved, peak, unit = bytes_ / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    elif bound == "mfma":
-        achieved, peak, unit = flops / t_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = flops / t_s / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = flops / t_s / 1e12, mfma_peak, "TFLOP/s"
     act_name = {"gelu": "GELU", "relu": "ReLU", "swiglu": "SwiGLU"}[cfg.act]
 
     graph = None
