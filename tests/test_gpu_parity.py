@@ -576,7 +576,9 @@ def test_dispatch_padded(gpu, T, N, k, C):
 
 
 @pytest.mark.parametrize("key,T,cf", [("c2", 2048, 1.5), ("c3", 1500, 1.0), ("c6", 1024, 1.0),
-                                      ("c1", None, 2.0)])
+                                      ("c1", None, 2.0),
+                                      # capacity 64: 128x384 down tiles over padded groups
+                                      ("c2", 8192, 1.0)])
 def test_forward_padded_layout(gpu, key, T, cf):
     """Whole layer in the static capacity layout (MOE_PADDED): routing and
     row layout bit-exact against the oracle's padded dispatch, outputs within
