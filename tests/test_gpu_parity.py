@@ -298,6 +298,11 @@ SCALED = {
     "c6": scaled_config(get_config("c6"), T=600, D=1024, F=512),
     "c6cf": scaled_config(get_config("c6", cf=1.0), T=300, D=512, F=256, N=16, k=2, n_shared=1),
     "c1sh": scaled_config(get_config("c1"), T=256, init="normal0.02", n_shared=2, name="c1_shared"),
+    # fp32 with D and F multiples of 16 but not of 64: the last k step of both
+    # projections is partial, and so is the last 64-column tile
+    "c1k": scaled_config(get_config("c1"), T=300, D=80, F=208, name="c1_ragged_k"),
+    "c1sw": scaled_config(get_config("c1"), T=300, D=112, F=176, act="swiglu", expert_bias=False,
+                          init="normal0.02", name="c1_swiglu"),
     # few rows per expert -> fused weight-streaming path
     "c3dec": scaled_config(get_config("c3"), T=64, name="c3_skew_decode"),
     "c2dec": scaled_config(get_config("c2"), T=1000, name="c2_switch_decode"),
