@@ -417,10 +417,14 @@ def main():
         "router_stats": ({"aux_loss": float(summary[0]), "imbalance": float(summary[1]),
                           "drop_rate": float(summary[2])} if rstats else None),
         "roofline": {
-            "kernel": f"grouped_gemm_kernel, {launch} launch "
-                      f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "
-                      f"moe_expert_{'up' if launch == 'fc1' else 'down'}; with the split-K "
-                      f"finishing kernel when its last round of tiles is split)",
+            "kernel": (f"grouped_gemm_kernel, {launch} launch "
+                       f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "
+                       f"moe_expert_{'up' if launch == 'fc1' else 'down'}; with the split-K "
+                       f"finishing kernel when its last round of tiles is split)"
+                       if cfg.dtype == "bf16" else
+                       f"grouped_gemm_f32_kernel, {launch} launch "
+                       f"({'fc1 + ' + act_name if launch == 'fc1' else 'fc2'}; "
+                       f"moe_expert_{'up' if launch == 'fc1' else 'down'})"),
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": achieved / peak,
             "traffic": (measured_traffic(args.workload, launch)
