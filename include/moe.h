@@ -35,10 +35,12 @@
  *   validated on the host before any launch; on error nothing is launched.
  *   T = 0 is a valid no-op.  NaN/Inf inputs give unspecified results.
  *
- * Supported shapes: 1 <= N <= 256, 1 <= k <= min(N, 8), T < 2^31 / k.
- * bf16: D and F multiples of 64.  fp32: D and F multiples of 16.
- * SwiGLU experts carry no biases (MOE_HAS_BIAS with SWIGLU is unsupported).
- * T*D, T*k*D, T*k*F and F*D must stay below 2^32 (32-bit offsets).
+ * Supported shapes: 1 <= N + S <= 256 (S shared experts), 1 <= k <= min(N, 8),
+ * and the row bound B = S*T + T*k (+ N*C with MOE_PADDED, C = capacity) at
+ * most 2^31 - 1.  bf16: D and F multiples of 64.  fp32: D and F multiples of
+ * 16.  SwiGLU experts carry no biases (MOE_HAS_BIAS with SWIGLU is
+ * unsupported).  4*T*D, 4*B*D, 4*B*F and 4*F*D must stay below 2^32 (32-bit
+ * byte offsets inside the kernels).  Other shapes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -118,7 +120,11 @@ typedef struct moe_shape {
  * has S + N + 1 entries (offsets[s] = s*T for s <= S), routed slots are
  * shifted by S*T, perm and the row buffers (y_perm, the hidden rows) hold
  * S*T + T*k rows, and the combine adds the shared rows with gate 1.  counts
- * and n_dropped stay those of the N routed experts. */
+ * and n_dropped stay those of the N routed experts.
+ *
+ * Grouped rows: the row buffers of the expert stage (perm, y_perm and the
+ * hidden rows h) hold R = S*T + T*k rows, or R = S*T + N*C with MOE_PADDED
+ * (C = capacity); "[R, ...]" below means that count. */
 
 /* Per-expert slot budget of the notebook's "Capacity factor" section:
  * int(T*k/N * cf), evaluated left to right in double and truncated.
@@ -256,8 +262,8 @@ int moe_dispatch_reroute(const moe_shape* shape, int32_t n_fallback, const int32
 
 /* Expert MLPs on the grouped rows: for every expert e and every row r in
  * [offsets[e], offsets[e+1]), token t = perm[r] / k,
- *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [T*k, D];
- *                                        [S*T + T*k, D] with S shared experts)
+ *   y_perm[r, :] = MLP_e(x[t, :])       (dtype of the shape, [R, D], R the
+ *                                        grouped rows of moe_shape)
  * Rows past the last offset are left untouched.  One launch per layer (fc1+act)
  * and one for fc2, each a persistent grouped GEMM whose work list covers
  * column shards of w1/w3 and row shards of w2 for all experts at once (the
@@ -285,8 +291,8 @@ int moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
  * notebook's Expert: fc1 then GELU or ReLU, biases with MOE_HAS_BIAS; for
  * SwiGLU silu(x w1^T) times x w3^T, w1 the gated branch):
  *   h[r, :] = act(x[perm[r] / k, :] . w1[e]^T + b1[e])     r in [offsets[e], offsets[e+1])
- * h: [T*k, F] row-major in the shape's dtype, caller-owned; rows past
- * offsets[N] are left untouched.  fp32 accumulation, one rounding to the
+ * h: [R, F] row-major in the shape's dtype (R the grouped rows of
+ * moe_shape), caller-owned; rows past the last offset are left untouched.  fp32 accumulation, one rounding to the
  * dtype after the activation.  w3 may be NULL unless the act is SwiGLU. */
 int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm,
                   const int32_t* offsets, const void* w1, const void* b1, const void* w3,
@@ -294,7 +300,7 @@ int moe_expert_up(const moe_shape* shape, const void* x, const int32_t* perm,
 
 /* moe_expert_down: the expert's second projection (fc2):
  *   y_perm[r, :] = h[r, :] . w2[e]^T + b2[e]                r in [offsets[e], offsets[e+1])
- * h as written by moe_expert_up; y_perm [T*k, D] in the shape's dtype. */
+ * h as written by moe_expert_up; y_perm [R, D] in the shape's dtype. */
 int moe_expert_down(const moe_shape* shape, const void* h, const int32_t* offsets,
                     const void* w2, const void* b2, void* y_perm, void* ws, size_t ws_bytes,
                     moe_stream_t stream);
