@@ -292,3 +292,13 @@ def test_binding_rejects_undersized_buffers():
     with pytest.raises(ValueError, match="x: 4096 elements"):
         api.route(shape, FakeGpuTensor(4096), FakeGpuTensor(8 * 128), None,
                   FakeGpuTensor(128, torch.int32), FakeGpuTensor(128, torch.float32))
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With no built library the binding raises ImportError at the first
+    call; there is no CPU fallback to hide it."""
+    from mixture_experts_layer_expert_amd import _lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent" / "libmoe_mi355x.so"))
+    with pytest.raises(ImportError, match="not found"):
+        L.load()
