@@ -290,15 +290,18 @@ __device__ void logits_f32(const RouteArgs& a, int64_t t0, int tid, float* lg, i
   const f32x4* xr = (const f32x4*)(x + row * D);
   for (int e = tid % 8; e < a.N; e += 8) {
     const f32x4* we = (const f32x4*)(wr + (int64_t)e * D);
-    float s = 0.f;
+    // four partial sums (lane c of every chunk) instead of one chain, and
+    // four chunks' loads issued together: the loop is latency-bound
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 4
     for (int d = 0; d < D / 4; ++d) {
-      f32x4 xv = xr[d], wv = we[d];
-      s = fmaf(xv[0], wv[0], s);
-      s = fmaf(xv[1], wv[1], s);
-      s = fmaf(xv[2], wv[2], s);
-      s = fmaf(xv[3], wv[3], s);
+      const f32x4 xv = xr[d], wv = we[d];
+      s0 = fmaf(xv[0], wv[0], s0);
+      s1 = fmaf(xv[1], wv[1], s1);
+      s2 = fmaf(xv[2], wv[2], s2);
+      s3 = fmaf(xv[3], wv[3], s3);
     }
-    lg[r * ldl + e] = s + (a.has_bias ? a.br[e] : 0.f);
+    lg[r * ldl + e] = ((s0 + s1) + (s2 + s3)) + (a.has_bias ? a.br[e] : 0.f);
   }
 }
 
