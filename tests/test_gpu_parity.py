@@ -816,3 +816,21 @@ def test_graph_replay_matches_eager(gpu, key, scaled_cases):
         eager.forward(g["x"], g)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(eager.out, want)
+
+
+# ------------------------------------------------ every assignment dropped
+@pytest.mark.parametrize("key", ["c2", "c6cf"])
+def test_forward_capacity_zero(gpu, key):
+    """Capacity 0 drops every routed assignment: the grouped GEMMs see only
+    empty routed groups (and the shared groups, if any), and the output is
+    the residual plus the shared experts, against the oracle."""
+    base = SCALED[key]
+    cfg = scaled_config(base, cf=0.0, name=base.name + "_cap0")
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp)
+    _say(f"capacity 0 {key}: T={cfg.T} N={cfg.N} k={cfg.k} shared={cfg.n_shared}")
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g)
+    assert int(buf.n_dropped.cpu()) == cfg.T * cfg.k
+    check_routing(buf, ref, cfg)
+    check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
