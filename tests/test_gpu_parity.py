@@ -834,3 +834,18 @@ def test_forward_capacity_zero(gpu, key):
     assert int(buf.n_dropped.cpu()) == cfg.T * cfg.k
     check_routing(buf, ref, cfg)
     check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
+
+
+# ------------------------------------------------------ one or a few tokens
+@pytest.mark.parametrize("key,T", [("c5", 1), ("c5", 3), ("c4", 1), ("c1", 1), ("c6", 2)])
+def test_forward_few_tokens(gpu, key, T):
+    """Single-token and few-token batches (decode steps): one row per used
+    expert, every tile almost empty, against the oracle."""
+    cfg = scaled_config(SCALED[key], T=T, name=f"{SCALED[key].name}_T{T}")
+    inp = generate(cfg)
+    ref = oracle_layer(cfg, inp)
+    _say(f"few tokens {key}: T={T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k}")
+    g = to_gpu(inp)
+    buf = run_forward(cfg, g)
+    check_routing(buf, ref, cfg)
+    check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
