@@ -837,15 +837,17 @@ def test_forward_capacity_zero(gpu, key):
 
 
 # ------------------------------------------------------ one or a few tokens
-@pytest.mark.parametrize("key,T", [("c5", 1), ("c5", 3), ("c4", 1), ("c1", 1), ("c6", 2)])
-def test_forward_few_tokens(gpu, key, T):
+@pytest.mark.parametrize("key,T,fused", [("c5", 1, False), ("c5", 3, False), ("c4", 1, False), ("c1", 1, False),
+                                         ("c6", 2, False), ("c5", 1, True), ("c5", 3, True)])
+def test_forward_few_tokens(gpu, key, T, fused):
     """Single-token and few-token batches (decode steps): one row per used
-    expert, every tile almost empty, against the oracle."""
+    expert, every tile almost empty, against the oracle; also through the
+    fused decode kernel."""
     cfg = scaled_config(SCALED[key], T=T, name=f"{SCALED[key].name}_T{T}")
     inp = generate(cfg)
     ref = oracle_layer(cfg, inp)
-    _say(f"few tokens {key}: T={T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k}")
+    _say(f"few tokens {key}: T={T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k} fused={fused}")
     g = to_gpu(inp)
-    buf = run_forward(cfg, g)
+    buf = run_forward(cfg, g, fused_decode=fused)
     check_routing(buf, ref, cfg)
     check_outputs(buf.out.float().cpu().numpy().astype(np.float64), ref, cfg, inp["x"].double().numpy())
