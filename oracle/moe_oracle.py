@@ -122,9 +122,11 @@ def route(x, w_router, b_router, k: int, renorm: bool) -> dict:
 
 # ---------------------------------------------------------------- dispatch
 def expert_counts(idx: np.ndarray, N: int) -> np.ndarray:
-    """counts[e] = number of (token, choice) pairs routed to expert e."""
-    flat = np.asarray(idx).reshape(-1)
-    return np.array([(flat == e).sum() for e in range(N)], dtype=np.int64)
+    """counts[e] = number of (token, choice) pairs routed to expert e: a
+    histogram of the assignments, one increment per assignment."""
+    counts = np.zeros(N, dtype=np.int64)
+    np.add.at(counts, np.asarray(idx, dtype=np.int64).reshape(-1), 1)
+    return counts
 
 
 def capacity(T: int, k: int, N: int, cf: Optional[float]) -> Optional[int]:
@@ -296,11 +298,13 @@ def with_shared(disp: dict, T: int, k: int, n_shared: int) -> dict:
 
 
 def drop_rate(counts: np.ndarray, C: Optional[int]) -> float:
-    """Summed overflow max(0, count - C) over summed counts."""
-    counts = np.asarray(counts, dtype=np.int64)
+    """Share of the assignments that do not fit: each expert overflows by
+    max(0, count - C), and the total overflow is divided by the number of
+    assignments (the sum of the counts)."""
     if C is None:
         return 0.0
-    return float(np.clip(counts - C, 0, None).sum() / counts.sum())
+    overflow = sum(max(0, int(c) - C) for c in counts)
+    return float(overflow / int(np.sum(counts)))
 
 
 def imbalance(counts: np.ndarray, T: int, k: int, N: int) -> float:
@@ -308,29 +312,40 @@ def imbalance(counts: np.ndarray, T: int, k: int, N: int) -> float:
     return float(np.max(counts) / (T * k / N))
 
 
+def _choice_fraction(idx: np.ndarray, N: int) -> np.ndarray:
+    """f[e] = share of tokens that have expert e among their choices: mark
+    each (token, chosen expert) cell of a T x N table, then average each
+    column."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T = idx.shape[0]
+    chosen = np.zeros((T, N), dtype=bool)
+    chosen[np.repeat(np.arange(T), idx.shape[1]), idx.reshape(-1)] = True
+    return chosen.sum(axis=0) / T
+
+
+def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, N: int) -> float:
+    """The load-balancing loss of the notebook section "Switch Transformer
+    auxiliary loss": N times the sum over experts of f_e (the share of tokens
+    that chose e) times P_e (e's softmax probability averaged over the
+    tokens)."""
+    f = _choice_fraction(idx, N)
+    P = np.asarray(probs, dtype=np.float64).sum(axis=0) / np.asarray(probs).shape[0]
+    return float(N * np.dot(f, P))
+
+
 def router_stats(idx: np.ndarray, probs: np.ndarray, counts: np.ndarray, N: int, C: Optional[int]) -> dict:
-    """The router's load statistics for one batch: per expert the fraction
-    f_i of tokens with expert i among their choices and the mean softmax
-    probability P_i over all N experts (notebook section "Switch Transformer
-    auxiliary loss"), the auxiliary loss N * sum f_i P_i, the imbalance
+    """The router's load statistics for one batch: per expert the share f_e
+    of tokens with expert e among their choices and the mean softmax
+    probability P_e over all N experts, the auxiliary loss N * sum f_e P_e
+    (notebook section "Switch Transformer auxiliary loss"), the imbalance
     max count / (T*k/N) and the drop rate at capacity C (section "Capacity
     factor")."""
     idx = np.asarray(idx)
     T, k = idx.shape
-    f = np.array([(idx == e).any(axis=1).mean() for e in range(N)])
-    P = np.asarray(probs).mean(axis=0)
-    return {"frac": f, "prob_mean": P, "aux_loss": float(N * (f * P).sum()),
+    f = _choice_fraction(idx, N)
+    P = np.asarray(probs, dtype=np.float64).sum(axis=0) / T
+    return {"frac": f, "prob_mean": P, "aux_loss": switch_aux_loss(idx, probs, N),
             "imbalance": imbalance(counts, T, k, N), "drop_rate": drop_rate(counts, C)}
-
-
-def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, N: int) -> float:
-    """N * sum_i f_i * P_i with f_i the fraction of tokens having expert i
-    among their choices and P_i the mean router probability of expert i
-    (notebook section "Switch Transformer auxiliary loss")."""
-    idx = np.asarray(idx)
-    f = np.array([(idx == e).any(axis=1).mean() for e in range(N)])
-    P = np.asarray(probs).mean(axis=0)
-    return float(N * (f * P).sum())
 
 
 # ----------------------------------------------------------------- experts

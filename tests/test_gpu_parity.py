@@ -636,6 +636,47 @@ def test_route_fallback_full_size(gpu, key):
     assert np.abs(fb_gate.cpu().numpy() - want_gate).max() <= GATE_ATOL[cfg.dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_route_fallback_hand_example(gpu, dtype, renorm):
+    """moe_route_fallback against the hand-derived fixture (integer logits
+    with exact ties): the fallbacks are ranks k .. k+R-1 of the router order,
+    and their gates follow the closed forms exp(l_f) / sum over all experts
+    of exp(l), or over the k chosen experts with renorm.  D is padded with
+    zeros to the kernels' multiple, which leaves every logit unchanged."""
+    import json
+    import math
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fallback_tiny.json")) as f:
+        gold = json.load(f)
+    x0 = torch.tensor(gold["x"], dtype=torch.float32)
+    w0 = torch.tensor(gold["w_router"], dtype=torch.float32)
+    T, N, k = x0.shape[0], w0.shape[0], gold["k"]
+    D = 64
+    x = torch.zeros(T, D)
+    w = torch.zeros(N, D)
+    x[:, :x0.shape[1]] = x0
+    w[:, :w0.shape[1]] = w0
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    shape = api.MoeShape(T=T, D=D, F=64, N=N, k=k, dtype=dt, act="relu", renorm=renorm)
+    i32 = dict(dtype=torch.int32, device=gpu)
+    f32 = dict(dtype=torch.float32, device=gpu)
+    for R, key in ((2, "expected_fallback_R2"), (3, "expected_fallback_R3")):
+        _say(f"route fallback hand example {dt} renorm={renorm} R={R}")
+        idx, gate = torch.empty(T, k, **i32), torch.empty(T, k, **f32)
+        fb_idx, fb_gate = torch.empty(T, R, **i32), torch.empty(T, R, **f32)
+        api.route_fallback(shape, x.to(dtype).to(gpu), w.to(dtype).to(gpu), None, idx, gate, R, fb_idx, fb_gate)
+        torch.cuda.synchronize()
+        assert idx.cpu().tolist() == gold["expected_topk"]
+        assert fb_idx.cpu().tolist() == gold[key]
+        lg = gold["expected_logits"]
+        for t in range(T):
+            over = gold["expected_topk"][t] if renorm else range(N)
+            den = sum(math.exp(lg[t][c]) for c in over)
+            want = [math.exp(lg[t][e]) / den for e in gold[key][t]]
+            assert np.abs(fb_gate[t].cpu().numpy() - np.array(want)).max() <= GATE_ATOL["fp32"], (R, t)
+
+
 def _reroute_case(gpu, T, N, k, C, R, seed, priority="token", n_shared=0, skew=None):
     rng = np.random.default_rng(seed)
     order = np.stack([rng.choice(N, size=k + R, replace=False, p=skew) for _ in range(T)])
@@ -747,13 +788,29 @@ def test_forward_full_size(gpu, key):
     buf = run_forward(cfg, g)
     rng = np.random.default_rng(123)
     T = cfg.T
-    sample = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+    # The sample covers every expert's rows: for each expert with kept rows
+    # (from the oracle's own routing), the tokens of its first, last and one
+    # random kept row, so that every expert's first and last row tiles get an
+    # output check; then the first and last tokens and random ones.
+    r = oracle.route(inp["x"], inp["w_router"], inp["b_router"], cfg.k, cfg.renorm)
+    d = oracle.dispatch(r["idx"], cfg.N, capacity_of(cfg))
+    off, perm = d["offsets"], d["perm"]
+    per_expert = []
+    for e in range(cfg.N):
+        if off[e + 1] > off[e]:
+            rows = [off[e], off[e + 1] - 1, rng.integers(off[e], off[e + 1])]
+            per_expert += [int(perm[q]) // cfg.k for q in rows]
+    sample = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T), np.array(per_expert, dtype=np.int64),
                                        rng.choice(T, size=min(T, 112), replace=False)]))
+    covered = {int(e) for t in sample for j, e in enumerate(r["idx"][t]) if d["slot"][t * cfg.k + j] >= 0}
+    used = {e for e in range(cfg.N) if off[e + 1] > off[e]}
+    assert covered == used, f"experts without a sampled row: {sorted(used - covered)[:10]}"
     ref = oracle_layer(cfg, inp, tokens=sample)
     check_routing(buf, ref, cfg)
     y = buf.out.float().cpu().numpy().astype(np.float64)[sample]
     err = check_outputs(y, ref, cfg, inp["x"].double().numpy()[sample], tokens=sample)
-    _say(f"  row-rel err {err:.3e} over {sample.size} sampled tokens, dropped {ref['n_dropped']}")
+    _say(f"  row-rel err {err:.3e} over {sample.size} sampled tokens covering {len(used)} experts, "
+         f"dropped {ref['n_dropped']}")
 
 
 @pytest.mark.slow

@@ -1,5 +1,6 @@
 """Pins of the oracle's dispatch (counts, stable grouping, capacity drops)."""
 import json
+import math
 import os
 
 import numpy as np
@@ -375,3 +376,67 @@ def test_reroute_layer_matches_dense_gates():
             if out["slot"][t * cfg.k + j] >= 0:
                 y[t] += out["gate"][t, j] * Yall[out["idx"][t, j], t]
     assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+
+
+def _golden_fallback():
+    with open(os.path.join(GOLDEN, "fallback_tiny.json")) as f:
+        return json.load(f)
+
+
+def _exp_gate(logits_row, e, over):
+    """exp(l_e) / sum of exp(l) over the experts in ``over`` (exact-arithmetic
+    form of a softmax probability, or of one renormalised over ``over``)."""
+    return math.exp(logits_row[e]) / sum(math.exp(logits_row[c]) for c in over)
+
+
+def test_fallback_choices_hand_example():
+    """Ranks k .. k+R-1 of the router order, checked against the hand-derived
+    fixture; the renormalised gate divides by the k chosen probabilities
+    only (its closed form after the softmax denominator cancels)."""
+    g = _golden_fallback()
+    x = np.array(g["x"], dtype=np.float64)
+    w = np.array(g["w_router"], dtype=np.float64)
+    k = g["k"]
+    logits = oracle.router_logits(x, w)
+    assert np.array_equal(logits, np.array(g["expected_logits"], dtype=np.float64))
+    probs = oracle.softmax(logits)
+    assert np.array_equal(oracle.select_topk(logits, k), np.array(g["expected_topk"]))
+    for R, key in ((2, "expected_fallback_R2"), (3, "expected_fallback_R3")):
+        for renorm in (False, True):
+            fb_idx, fb_gate = oracle.fallback_choices(logits, probs, k, R, renorm)
+            assert np.array_equal(fb_idx, np.array(g[key])), (R, renorm)
+            for t in range(x.shape[0]):
+                chosen = g["expected_topk"][t]
+                over = chosen if renorm else range(w.shape[0])
+                want = [_exp_gate(g["expected_logits"][t], e, over) for e in g[key][t]]
+                assert np.allclose(fb_gate[t], want, rtol=1e-14, atol=0), (R, renorm, t)
+    _, fb_gate = oracle.fallback_choices(logits, probs, k, 2, True)
+    assert np.allclose(fb_gate[0], g["renorm_gate_x0_R2"]["value"], rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fallback_choices_against_sorted_with_ties(seed):
+    """Small-integer logits with many exact ties and duplicated router rows:
+    the fallbacks equal Python's sorted() of (-logit, expert) cut at
+    [k, k+R), for every k + R <= N including k + R = N."""
+    rng = np.random.default_rng(seed)
+    N, D, T = 7, 3, 60
+    w = rng.integers(-2, 3, size=(N, D)).astype(np.float64)
+    w[4] = w[1]  # duplicated rows force exact ties on every token
+    w[6] = w[2]
+    x = rng.integers(-2, 3, size=(T, D)).astype(np.float64)
+    l = oracle.router_logits(x, w)
+    p = oracle.softmax(l)
+    n_ties = sum(len(set(row)) < N for row in l.tolist())
+    assert n_ties == T
+    for k in range(1, N):
+        for R in range(1, N - k + 1):
+            fb_idx, fb_gate = oracle.fallback_choices(l, p, k, R, renorm=True)
+            _, fb_plain = oracle.fallback_choices(l, p, k, R, renorm=False)
+            for t in range(T):
+                order = sorted(range(N), key=lambda e: (-l[t, e], e))
+                assert fb_idx[t].tolist() == order[k:k + R], (k, R, t)
+                want = [_exp_gate(l[t], e, order[:k]) for e in order[k:k + R]]
+                assert np.allclose(fb_gate[t], want, rtol=1e-12, atol=0), (k, R, t)
+                want = [_exp_gate(l[t], e, range(N)) for e in order[k:k + R]]
+                assert np.allclose(fb_plain[t], want, rtol=1e-12, atol=0), (k, R, t)
