@@ -1,7 +1,8 @@
-"""The notebook's own checks ("Dispatch and gather", "Capacity factor",
-"Switch Transformer auxiliary loss" sections of "Mixture-of-experts and
-expert parallelism"), run through the oracle on the notebook's recipe
-(1024 tokens, D=256, 8 experts, top-2, Linear+GELU+Linear experts)."""
+"""The self-checks of the notebook "Mixture-of-experts and expert
+parallelism" (sections "Dispatch and gather", "Capacity factor" and "Switch
+Transformer auxiliary loss"), restated and run through the oracle on the
+tiny layer with the notebook's sizes and distributions (1024 tokens, D=256,
+8 experts, top-2, Linear+GELU+Linear experts)."""
 import numpy as np
 import pytest
 
@@ -40,7 +41,11 @@ def test_untrained_router_has_measurable_imbalance(c1_run):
 def test_aux_loss_imbalanced_higher_than_balanced(c1_run):
     cfg, inp, r = c1_run
     imb = oracle.switch_aux_loss(r["idx"], r["probs"], cfg.N)
-    bal_idx = (np.arange(cfg.T * cfg.k) % cfg.N).reshape(cfg.T, cfg.k)
+    # a perfectly balanced router: token t takes experts t, t+1, ..., t+k-1
+    # (mod N), so each expert holds T*k/N assignments, and every
+    # probability is 1/N
+    bal_idx = (np.arange(cfg.T)[:, None] + np.arange(cfg.k)[None, :]) % cfg.N
+    assert (oracle.expert_counts(bal_idx, cfg.N) == cfg.T * cfg.k // cfg.N).all()
     bal = oracle.switch_aux_loss(bal_idx, np.full((cfg.T, cfg.N), 1.0 / cfg.N), cfg.N)
     assert imb > bal
 

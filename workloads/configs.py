@@ -36,7 +36,7 @@ class MoeConfig:
     router_bias: Optional[str]  # None | "zipf1.2"
     cf: Optional[float]         # capacity factor; None = no limit
     residual: bool    # y = x + sum of kept expert outputs
-    init: str         # "p5" (notebook recipe) | "normal0.02"
+    init: str         # "linear_default" (the notebook's distributions) | "normal0.02"
     seed: int         # base seed for every stream of this config
     x_seed: int = 0   # x stream seed offset (near-tie rule)
     n_shared: int = 0  # always-on experts, applied to every token with gate 1
@@ -60,8 +60,8 @@ CONFIGS: dict[str, MoeConfig] = {
     "c1": MoeConfig(
         name="c1_tiny_fp32", T=1024, D=256, F=1024, N=8, k=2, act="gelu", dtype="fp32",
         expert_bias=True, renorm=False, router_bias=None, cf=None, residual=False,
-        init="p5", seed=0, x_seed=0,
-        description="Tiny fp32 layer, the notebook's own recipe: 1024 tokens, D=256, "
+        init="linear_default", seed=0, x_seed=0,
+        description="Tiny fp32 layer with the notebook's distributions: 1024 tokens, D=256, "
                     "8 experts, top-2 softmax router, Linear+GELU+Linear experts"),
     "c2": MoeConfig(
         name="c2_switch_bf16", T=16384, D=768, F=3072, N=128, k=1, act="relu", dtype="bf16",

@@ -2,13 +2,13 @@
 
 Two recipes:
 
-* ``"p5"`` replays the order of draws of the notebook "Mixture-of-experts and
-  expert parallelism" (sections "Top-k router" and "Dispatch and gather"):
-  global seed ``seed``, a bias-free ``nn.Linear(D, N)`` router whose weight is
-  then replaced by standard normals times 0.1, then x as standard normals;
-  global seed ``seed + 1``, then one ``Expert`` per index, each made of
-  ``nn.Linear(D, F)`` and ``nn.Linear(F, D)`` with PyTorch's default uniform
-  initialisation of weights and biases.
+* ``"linear_default"``, the distributions of the notebook "Mixture-of-experts
+  and expert parallelism" (sections "Top-k router" and "Dispatch and
+  gather"): x ~ N(0, 1); router weights ~ N(0, 0.1^2) and no router bias;
+  every expert weight and bias ~ U(-1/sqrt(fan_in), +1/sqrt(fan_in)) with
+  fan_in = D for fc1 and F for fc2 (PyTorch's default for a Linear layer).
+  The tensors are drawn from the same per-(tensor, expert) generators as the
+  other recipe, not in the notebook's order of draws.
 * ``"normal0.02"``: x ~ N(0, 1); router, expert weights and (when present)
   expert biases ~ N(0, 0.02^2).  Every (tensor, expert) pair has its own
   ``torch.Generator`` so that one expert can be regenerated alone and the
@@ -86,37 +86,29 @@ def expert_slice(cfg: MoeConfig, tensor: str, e: int) -> torch.Tensor:
     return _normal(shape, _stream_seed(cfg.seed, tensor, e), _STD_W, _TORCH_DTYPE[cfg.dtype])
 
 
-def _gen_p5(cfg: MoeConfig, parts: Iterable[str]) -> dict:
+def _uniform(shape, seed: int, bound: float) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(shape, generator=g, dtype=torch.float32).mul_(2.0 * bound).sub_(bound)
+
+
+def _gen_linear_default(cfg: MoeConfig, parts: Iterable[str]) -> dict:
     if cfg.dtype != "fp32":
-        raise ValueError("the notebook recipe is fp32")
-    if cfg.n_shared:
-        raise ValueError("the notebook recipe has no shared experts")
+        raise ValueError("the linear_default recipe is fp32")
+    if cfg.act == "swiglu":
+        raise ValueError("the linear_default recipe has fc1 and fc2 only")
     out: dict = {}
-    with torch.random.fork_rng(devices=[]):
-        torch.manual_seed(cfg.seed)
-        router = torch.nn.Linear(cfg.D, cfg.N, bias=False)
-        router.weight.data = torch.randn_like(router.weight.data) * 0.1
-        x = torch.randn(cfg.T, cfg.D)
-        if cfg.x_seed:
-            x = _normal((cfg.T, cfg.D), _stream_seed(cfg.seed, "x", cfg.x_seed), 1.0, torch.float32)
-        out["x"] = x.contiguous()
-        out["w_router"] = router.weight.data.clone().contiguous()
+    if "x" in parts:
+        out["x"] = _normal((cfg.T, cfg.D), _stream_seed(cfg.seed, "x", cfg.x_seed), 1.0, torch.float32)
+    if "router" in parts:
+        out["w_router"] = _normal((cfg.N, cfg.D), _stream_seed(cfg.seed, "router", 0), 0.1, torch.float32)
         out["b_router"] = None
-        if "experts" in parts:
-            torch.manual_seed(cfg.seed + 1)
-            w1, b1, w2, b2 = [], [], [], []
-            for _ in range(cfg.N):
-                fc1 = torch.nn.Linear(cfg.D, cfg.F)
-                fc2 = torch.nn.Linear(cfg.F, cfg.D)
-                w1.append(fc1.weight.data)
-                b1.append(fc1.bias.data)
-                w2.append(fc2.weight.data)
-                b2.append(fc2.bias.data)
-            out["w1"] = torch.stack(w1).contiguous()
-            out["b1"] = torch.stack(b1).contiguous()
-            out["w3"] = None
-            out["w2"] = torch.stack(w2).contiguous()
-            out["b2"] = torch.stack(b2).contiguous()
+    if "experts" in parts:
+        bound1, bound2 = 1.0 / math.sqrt(cfg.D), 1.0 / math.sqrt(cfg.F)
+        for name, shape, bound in (("w1", (cfg.F, cfg.D), bound1), ("b1", (cfg.F,), bound1),
+                                   ("w2", (cfg.D, cfg.F), bound2), ("b2", (cfg.D,), bound2)):
+            out[name] = torch.stack([_uniform(shape, _stream_seed(cfg.seed, name, e), bound)
+                                     for e in range(cfg.n_slots)]).contiguous()
+        out["w3"] = None
     return out
 
 
@@ -151,8 +143,8 @@ def _gen_normal(cfg: MoeConfig, parts: Iterable[str]) -> dict:
 def generate(cfg: MoeConfig, parts: Iterable[str] = _ALL_PARTS) -> dict:
     """Draw the tensors of one instance; ``parts`` may omit "experts"."""
     parts = tuple(parts)
-    if cfg.init == "p5":
-        return _gen_p5(cfg, parts)
+    if cfg.init == "linear_default":
+        return _gen_linear_default(cfg, parts)
     if cfg.init == "normal0.02":
         return _gen_normal(cfg, parts)
     raise ValueError(f"unknown init recipe {cfg.init!r}")
