@@ -123,9 +123,11 @@ def route(x, w_router, b_router, k: int, renorm: bool) -> dict:
 # ---------------------------------------------------------------- dispatch
 def expert_counts(idx: np.ndarray, N: int) -> np.ndarray:
     """counts[e] = number of (token, choice) pairs routed to expert e: a
-    histogram of the assignments, one increment per assignment."""
+    histogram of the assignments, one increment per assignment.  An id
+    outside [0, N) names no expert and is not counted."""
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
     counts = np.zeros(N, dtype=np.int64)
-    np.add.at(counts, np.asarray(idx, dtype=np.int64).reshape(-1), 1)
+    np.add.at(counts, flat[(flat >= 0) & (flat < N)], 1)
     return counts
 
 

@@ -302,3 +302,15 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent" / "libmoe_mi355x.so"))
     with pytest.raises(ImportError, match="not found"):
         L.load()
+
+
+def test_clock_probe_validates_on_the_host(lib):
+    from mixture_experts_layer_expert_amd import _lib as L
+    dummy = ctypes.c_void_p(0x1000)  # never dereferenced: each call fails validation
+    assert lib.moe_clock_probe(0, 0.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(65537, 0.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 0.0, 10.0, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, -1.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 0.0, 0.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 50000.0, 60000.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, float("nan"), 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG

@@ -440,3 +440,20 @@ def test_fallback_choices_against_sorted_with_ties(seed):
                 assert np.allclose(fb_gate[t], want, rtol=1e-12, atol=0), (k, R, t)
                 want = [_exp_gate(l[t], e, range(N)) for e in order[k:k + R]]
                 assert np.allclose(fb_plain[t], want, rtol=1e-12, atol=0), (k, R, t)
+
+
+def test_out_of_range_ids_are_neither_counted_nor_kept():
+    """An id outside [0, N) names no expert: it is not counted, never gets a
+    row and is dropped (the GPU dispatch treats it the same way)."""
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 8, size=(300, 2))
+    idx[::7, 0] = -1
+    idx[::11, 1] = 8
+    flat = idx.reshape(-1)
+    inside = flat[(flat >= 0) & (flat < 8)]
+    for C in (None, 30):
+        d = oracle.dispatch(idx, 8, C)
+        assert np.array_equal(d["counts"], np.bincount(inside, minlength=8))
+        bad = np.nonzero((flat < 0) | (flat >= 8))[0]
+        assert (d["slot"][bad] == -1).all()
+        assert not np.isin(bad, d["perm"]).any()
