@@ -326,6 +326,21 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 int32_t* slot, int32_t* n_dropped, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
 
+/* Measurement helper (not a step of the layer): the shader clock the GPU
+ * holds, for stating a kernel's throughput against the peak at the clock
+ * actually sustained (the MFMA peak scales with the core clock).  Launches
+ * `blocks` one-wave workgroups on `stream`; each waits delay_us, then counts
+ * shader-clock cycles (s_memtime) over window_us of the 100 MHz real-time
+ * counter (s_memrealtime) and writes stamps[4*b .. 4*b+3] = {realtime
+ * start, realtime end, cycles start, cycles end} (device memory, uint64,
+ * 4*blocks entries, caller-owned).  clock = (cycles) / (ticks) * 100 MHz.
+ * Launched on a second stream while a kernel runs, the waves share that
+ * kernel's compute units when its resources leave room for one more wave.
+ * Errors: MOE_ERR_INVALID_ARG for blocks outside [1, 65536], a null stamps,
+ * delay_us < 0, window_us <= 0 or delay_us + window_us > 100000. */
+int moe_clock_probe(int32_t blocks, double delay_us, double window_us, uint64_t* stamps,
+                    moe_stream_t stream);
+
 /* Static, human-readable text of a status code. */
 const char* moe_status_string(int status);
 

@@ -253,6 +253,24 @@ def forward(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, top
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def clock_probe(blocks: int, delay_us: float, window_us: float, stamps, stream=None):
+    """Shader-clock probe (moe_clock_probe): stamps is a device int64 tensor of
+    at least 4*blocks entries, filled with {realtime start, realtime end,
+    cycles start, cycles end} per workgroup."""
+    _check("moe_clock_probe", L.load().moe_clock_probe(
+        int(blocks), float(delay_us), float(window_us), _ptr(stamps, torch.int64, "stamps", 4 * int(blocks)),
+        _stream(stream)))
+
+
+def probe_clock_ghz(stamps) -> float:
+    """Median core clock in GHz over the probe's workgroups: shader cycles per
+    tick of the 100 MHz real-time counter, times 0.1 GHz (host arithmetic on
+    the copied-back stamps)."""
+    s = stamps.view(-1, 4).cpu().tolist()
+    rates = sorted((c1 - c0) / (r1 - r0) * 0.1 for r0, r1, c0, c1 in s if r1 > r0)
+    return rates[len(rates) // 2] if rates else float("nan")
+
+
 class MoeBuffers:
     """Device buffers of one layer call (outputs, routing tensors, workspace),
     allocated once with torch so that repeated calls allocate nothing."""
