@@ -326,6 +326,27 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 int32_t* slot, int32_t* n_dropped, void* ws, size_t ws_bytes,
                 moe_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * layer as moe_forward, same arguments and results, with the workspace
+ * taken from a device array inside the library instead of a caller buffer.
+ * The array holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB); each GPU the library
+ * runs on keeps its own copy until the process ends.  A layer whose
+ * moe_workspace_bytes exceeds that returns MOE_ERR_WORKSPACE before any
+ * launch.  The call allocates nothing (no hipMalloc, no library routine that
+ * allocates); the first call on a device looks up that device's copy of the
+ * array.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (different streams, or threads) race and must be ordered by the
+ * caller.  The array keeps the last call's contents; the layer writes
+ * every workspace byte it reads within the same call.  Returns MOE_ERR_HIP
+ * if the array's address cannot be looked up. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                        const float* b_router, const void* w1, const void* b1, const void* w3,
+                        const void* w2, const void* b2, void* out, int32_t* topk_idx,
+                        float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot, int32_t* n_dropped, moe_stream_t stream);
+
 /* Measurement helper (not a step of the layer): the shader clock the GPU
  * holds, for stating a kernel's throughput against the peak at the clock
  * actually sustained (the MFMA peak scales with the core clock).  Launches

@@ -28,11 +28,12 @@ MOE_ROUTER_BIAS = 8
 MOE_FUSED_DECODE = 16
 MOE_SLOT_MAJOR = 32
 MOE_PADDED = 64
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ("moe_capacity", "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_stats_workspace_bytes",
             "moe_route_stats", "moe_router_stats", "moe_route_fallback", "moe_dispatch_reroute",
-            "moe_status_string", "moe_clock_probe")
+            "moe_status_string", "moe_clock_probe", "moe_forward_noalloc")
 
 
 class MoeShapeC(ctypes.Structure):
@@ -73,6 +74,8 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_forward_noalloc": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_clock_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_double, ctypes.c_double, _vp, _vp]),
 }
 

@@ -253,6 +253,22 @@ def forward(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, top
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def forward_noalloc(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, out, topk_idx, topk_gate,
+                    counts, offsets, perm, slot, n_dropped, stream=None):
+    """moe_forward with the library's own device scratch as the workspace
+    (no workspace argument; layers up to MOE_NOALLOC_SCRATCH_BYTES)."""
+    dt = shape.torch_dtype
+    i32 = torch.int32
+    sc = shape.c()
+    _check("moe_forward_noalloc", L.load().moe_forward_noalloc(
+        ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
+        _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(w1, dt, "w1", _slots(shape) * shape.F * shape.D), _ptr(b1, dt, "b1", _slots(shape) * shape.F),
+        _ptr(w3, dt, "w3", _slots(shape) * shape.F * shape.D), _ptr(w2, dt, "w2", _slots(shape) * shape.D * shape.F), _ptr(b2, dt, "b2", _slots(shape) * shape.D), _ptr(out, dt, "out", shape.T * shape.D),
+        _ptr(topk_idx, i32, "topk_idx", shape.T * shape.k), _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k),
+        _ptr(counts, i32, "counts", shape.N), _ptr(offsets, i32, "offsets", shape.n_shared + shape.N + 1), _ptr(perm, i32, "perm", shape.group_rows),
+        _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
+
+
 def clock_probe(blocks: int, delay_us: float, window_us: float, stamps, stream=None):
     """Shader-clock probe (moe_clock_probe): stamps is a device int64 tensor of
     at least 4*blocks entries, filled with {realtime start, realtime end,

@@ -416,6 +416,58 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   return hip_status(launch_combine(s, y_perm, slot, topk_gate, x, out, st));
 }
 
+// ---- allocation-free forward -------------------------------------------
+// moe_forward_noalloc runs moe_forward with its workspace in `scratch`, a
+// file-scope device array of kNoAllocScratchBytes that every GPU the library
+// runs on holds until the process ends.  Host code never passes the array's
+// name to a kernel (in host code it is a stand-in, not a device address):
+// the first call on a device, with that device current, looks up the
+// array's device address with hipGetSymbolAddress and keeps it per device.
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (nullptr if the lookup fails).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  // a concurrent first call stores the same address
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
+                        const void* w1, const void* b1, const void* w3, const void* w2, const void* b2,
+                        void* out, int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* slot, int32_t* n_dropped, moe_stream_t stream) {
+  int v = validate(shape);
+  if (v != MOE_OK) return v;
+  const size_t need = forward_ws_bytes(*shape);
+  if (need > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  if (shape->T == 0) return MOE_OK;
+  void* ws = device_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  // the layer reads nothing from its workspace that it has not written in
+  // the same call, so the scratch's previous contents need no clearing
+  return moe_forward(shape, x, w_router, b_router, w1, b1, w3, w2, b2, out, topk_idx, topk_gate, counts, offsets,
+                     perm, slot, n_dropped, ws, need, stream);
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
