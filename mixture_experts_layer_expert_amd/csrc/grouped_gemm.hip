@@ -62,8 +62,20 @@ __device__ inline int swz(int row) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ inline void dma16(const void* g, lds_ptr_t l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Word 3 of a raw buffer resource: DATA_FORMAT = 32 bits (4 in bits 15-18),
+// which untyped loads need non-zero.  Loads at offsets past num_records
+// return zeros.
+constexpr int kBufferWord3 = 0x00020000;
+
+// HBM -> LDS copy of 16 bytes per lane through a buffer resource
+// (buffer_load_dwordx4 ... lds): lane l's bytes at voff + soff land at LDS
+// address l + 16 * lane.  The buffer form, unlike global_load_lds, leaves the
+// MFMA issue of the SIMD's other wave nearly undisturbed: with one wave per
+// SIMD streaming operands and one running MFMAs, the MFMA pipe stays about
+// 93% busy with buffer loads against about 62% with global loads (probe on
+// gfx950; GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES counters).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, lds_ptr_t l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, voff, soff, 0, 0);
 }
 
 // erf by formula 7.1.26 of Abramowitz and Stegun's Handbook of Mathematical
@@ -112,6 +124,7 @@ struct Tile {
 
 struct Params {
   const bf16* A;
+  uint32_t a_bytes;  // bytes addressable in A (the buffer resource's range)
   const int32_t* perm;
   int topk;
   const int32_t* offsets;
@@ -409,13 +422,21 @@ __device__ inline int* split_header(const Params& p, int G) {
 }
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES>
+// DW: the waves that issue the operand DMA (all NW, or NW/2 = one per SIMD).
+// A wave that issues a job's DMA stalls at issue while the texture unit takes
+// the CU's burst of 1 KiB instructions (about 20 cycles each); with one DMA
+// wave per SIMD the other wave keeps the MFMA pipe busy meanwhile.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES, int DW>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int CPR = TL::CPR, RPI = TL::RPI;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
   constexpr int BN_OUT = kSwiGLU ? BNB / 2 : BNB;  // output columns per tile
-  constexpr int NJ = TL::QA + TL::QB;               // dma instructions per job per wave
+  static_assert(DW == TL::NW || DW * 2 == TL::NW, "all waves or half of them issue the DMA");
+  constexpr int QA = BM / (RPI * DW);  // A dma instructions per DMA wave per stage
+  constexpr int QB = BNB / (RPI * DW); // B dma instructions per DMA wave per stage
+  static_assert(QA >= 1 && QB >= 1 && QA * RPI * DW == BM && QB * RPI * DW == BNB, "dma split");
+  constexpr int NJ = QA + QB;          // dma instructions per job per DMA wave
   static_assert(STAGES >= 2 && STAGES <= 8, "2..8 stages");
   static_assert((STAGES - 1) * NJ <= 63, "vmcnt range");
 
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   __shared__ int s_off[kMaxExperts + 1];
   // per wave, two slots of the perm entries of its A rows (fc1 gather): the
   // next tile's are brought in by DMA while the current tile is loading
-  constexpr int kRowsPerWave = TL::QA * RPI;
+  constexpr int kRowsPerWave = QA * RPI;
   static_assert(kRowsPerWave <= 64, "one dword DMA per wave");
   __shared__ int s_perm[TL::NW][2][64];
   // per wave, a ring of the bias values of its TN columns of a tile: filled by
@@ -442,6 +463,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   const int lane = tid % kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int KT = p.K / BK;
+  const bool dma_wave = wave < DW;  // wave-uniform
 
   WorkList<BM, BN_OUT> wl;
   wl.build(p, s_tile_start, s_scan, s_off, tid, TL::THREADS);
@@ -484,15 +506,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
 
   // ---- DMA side: per-lane 32-bit byte offsets of the tile being loaded,
   // added to wave-uniform base pointers (saddr + voffset addressing).
-  uint32_t offA[TL::QA], offB[TL::QB];
-  const char* b1e = (const char*)p.B;
-  const char* b2e = (const char*)p.B;
+  uint32_t offA[QA], offB[QB];
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, p.a_bytes, kBufferWord3);
+  const uint32_t b_bytes = (uint32_t)p.n_out * (uint32_t)p.K * 2u;  // one expert's weight matrix
+  __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)p.B, 0, b_bytes, kBufferWord3);
+  __amdgpu_buffer_rsrc_t rsB2 = rsB1;
   int i_dma = 0, kt_dma = 0, k1_dma = 0, job_issued = 0;
   // perm DMA for tile i into slot i & 1: lane l fetches the entry of tile
   // row wave*kRowsPerWave + l (clamped to the tile's last row, so always a
   // valid entry); only the first kRowsPerWave lanes' values are used.
   auto fetch_perm = [&](int i) {
-    if (!p.perm || i >= n_mine) return;
+    if (!p.perm || i >= n_mine || !dma_wave) return;
     const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
     int r = t.row0 + wave * kRowsPerWave + (lane < kRowsPerWave ? lane : 0);
     if (r > t.row_end - 1) r = t.row_end - 1;
@@ -501,18 +525,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   int jobs_since_fetch = 0;  // DMA jobs issued after the last perm fetch
   auto setup_dma = [&](int i) {
     const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
-    if (p.perm) {
+    if (p.perm && dma_wave) {
       // the fetch for tile i is older than every job issued since: wait for
       // it to land (in steady state an earlier wait already covered it)
       wait_dma<NJ, STAGES - 1>(jobs_since_fetch);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 #pragma unroll
-    for (int q = 0; q < TL::QA; ++q) {
-      const int trow = (wave * TL::QA + q) * RPI + lrow;  // row within the A tile
+    for (int q = 0; q < QA; ++q) {
+      const int trow = (wave * QA + q) * RPI + lrow;  // row within the A tile (DMA waves)
       int src = t.row0 + trow;
       if (src > t.row_end - 1) src = t.row_end - 1;  // tail rows re-load a valid row
-      if (p.perm) src = s_perm[wave][i & 1][q * RPI + lrow] / p.topk;
+      if (p.perm && dma_wave) src = s_perm[wave][i & 1][q * RPI + lrow] / p.topk;
       offA[q] = ((uint32_t)src * (uint32_t)p.K + (uint32_t)((lchunk ^ swz<CPR>(trow)) * 8)) * 2u;
     }
     fetch_perm(i + 1);
@@ -527,15 +551,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&s_bias[wave][i % kBiasSlots][0], 4, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < TL::QB; ++q) {
-      const int brow = (wave * TL::QB + q) * RPI + lrow;  // row within the B tile
+    for (int q = 0; q < QB; ++q) {
+      const int brow = (wave * QB + q) * RPI + lrow;  // row within the B tile (DMA waves)
       int feat = kSwiGLU ? t.n0 + (brow / 64) * 32 + (brow % 32) : t.n0 + brow;
       if (feat > p.n_out - 1) feat = p.n_out - 1;  // column tail
       offB[q] = ((uint32_t)feat * (uint32_t)p.K + (uint32_t)((lchunk ^ swz<CPR>(brow)) * 8)) * 2u;
     }
     const size_t eoff = (size_t)t.e * p.n_out * p.K * 2;
-    b1e = (const char*)p.B + eoff;
-    b2e = kSwiGLU ? (const char*)p.B2 + eoff : b1e;
+    rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.B + eoff), 0, b_bytes, kBufferWord3);
+    rsB2 = kSwiGLU ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.B2 + eoff), 0, b_bytes, kBufferWord3)
+                   : rsB1;
     kt_dma = tile_k0(i);
     k1_dma = tile_k1(i);
   };
@@ -544,18 +569,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     const int stage = job_issued % STAGES;
     bf16* a_dst = sA + stage * TL::kLdsA;
     bf16* b_dst = sB + stage * TL::kLdsB;
-    const size_t kbytes = (size_t)kt_dma * BK * 2;
-    const char* a_base = (const char*)p.A + kbytes;
+    const uint32_t kbytes = (uint32_t)kt_dma * BK * 2;
+    if (dma_wave) {
 #pragma unroll
-    for (int q = 0; q < TL::QA; ++q)
-      dma16(a_base + offA[q], (lds_ptr_t)(a_dst + (wave * TL::QA + q) * 512));
-    const char* b1 = b1e + kbytes;
-    const char* b2 = b2e + kbytes;
+      for (int q = 0; q < QA; ++q)
+        dma16(rsA, offA[q], kbytes, (lds_ptr_t)(a_dst + (wave * QA + q) * 512));
 #pragma unroll
-    for (int q = 0; q < TL::QB; ++q) {
-      // SwiGLU: 32-row groups alternate w1 (even) and w3 (odd)
-      const char* base = (kSwiGLU && ((((wave * TL::QB + q) * RPI) / 32) & 1)) ? b2 : b1;
-      dma16(base + offB[q], (lds_ptr_t)(b_dst + (wave * TL::QB + q) * 512));
+      for (int q = 0; q < QB; ++q) {
+        // SwiGLU: 32-row groups alternate w1 (even) and w3 (odd)
+        const bool w3 = kSwiGLU && ((((wave * QB + q) * RPI) / 32) & 1);
+        dma16(w3 ? rsB2 : rsB1, offB[q], kbytes, (lds_ptr_t)(b_dst + (wave * QB + q) * 512));
+      }
     }
     ++job_issued;
     ++jobs_since_fetch;
@@ -629,7 +653,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   if (n_jobs > 0) {
     tc = wl.info(p, s_tile_start, s_off, tile_L(0));
     len_cmp = tile_k1(0) - tile_k0(0);
-    wait_dma<NJ, STAGES - 1>(job_issued - 1);
+    if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - 1);
     ring_barrier();
     load_frags(0, 0, 0);
   }
@@ -644,7 +668,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
     // all fragments of this job are in registers: refill its stage later
     const bool more = job + 1 < n_jobs;
-    wait_dma<NJ, STAGES - 1>(job_issued - (job + 1) - 1);
+    if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - (job + 1) - 1);
     ring_barrier();
     issue_next();
     if (more) load_frags((job + 1) % STAGES, 0, KS & 1);
@@ -654,6 +678,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     // left-over tile (always this workgroup's last): its partial sums are
     // stored after the loop
     if (++kt_cmp == len_cmp && more) {
+      // a wave without tile DMA waits for its bias slice here
+      if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
                                                        (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
       kt_cmp = 0;
@@ -664,6 +690,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
   }
   if (n_jobs > 0) {
+    if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!has_rem || wl.S == 1) {
       store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
                                                        (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
@@ -734,11 +761,11 @@ __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
   }
 }
 
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int DW>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int S = TL::kStages;
-  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, BIAS, S>;
+  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, BIAS, S, DW>;
   // once per process and instantiation (thread-safe static initialisation)
   static const hipError_t attr_err = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::kLdsBytes);
@@ -755,23 +782,23 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BNB, int WM, int WN, int BK>
+template <int BM, int BNB, int WM, int WN, int BK, int DW>
 hipError_t launch_act(const Params& p, hipStream_t st) {
   const bool bias = p.bias != nullptr;
   switch (p.act) {
     case kActGelu:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActGelu, true>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActGelu, false>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActGelu, true, DW>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActGelu, false, DW>(p, st);
     case kActRelu:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true, DW>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false, DW>(p, st);
     case kActSwiGLU:
       // the SwiGLU epilogue pairs each wave's w1 and w3 32-row groups
-      if constexpr ((BNB / WN / 32) % 2 == 0) return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false>(p, st);
+      if constexpr ((BNB / WN / 32) % 2 == 0) return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false, DW>(p, st);
       else return hipErrorInvalidValue;
     default:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true, DW>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false, DW>(p, st);
   }
 }
 
@@ -780,10 +807,12 @@ hipError_t launch_act(const Params& p, hipStream_t st) {
 namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
-enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, kNumCfg };
-const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64"};
-const int kCfgBM[kNumCfg] = {256, 128, 128, 32};
-const int kCfgBN[kNumCfg] = {256, 256, 384, 256};
+enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, k256x256w8d4, k128x256w8d4,
+               k128x384w8d4, kNumCfg };
+const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
+                                       "256x256w8d4", "128x256w8d4", "128x384w8d4"};
+const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128};
+const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --
@@ -809,8 +838,8 @@ TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up) {
   if (forced)
     for (int c = 0; c < kNumCfg; ++c)
       if (!strcmp(forced, kCfgName[c])) return (TileCfg)c;
-  if (expected_rows >= 192) return k256x256w8k64;
-  if (expected_rows >= 48) return (up || max_rows > 128) ? k128x256w8k64 : k128x384w8k64;
+  if (expected_rows >= 192) return k256x256w8d4;
+  if (expected_rows >= 48) return (up || max_rows > 128) ? k128x256w8d4 : k128x384w8d4;
   return k32x256w4k64;
 }
 
@@ -845,6 +874,7 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
                                     hipStream_t st) {
   Params p;
   p.A = (const bf16*)g.A;
+  p.a_bytes = (uint32_t)(g.a_rows * g.K * 2);
   p.perm = g.perm;
   p.topk = g.topk;
   p.offsets = g.offsets;
@@ -859,10 +889,13 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   const TileCfg cfg = choose_cfg(expected_rows, max_rows, g.perm != nullptr);
   p.part = (g.part && allow_split(cfg, g, expected_rows, max_rows)) ? g.part : nullptr;
   switch (cfg) {
-    case k256x256w8k64: return launch_act<256, 256, 2, 4, 64>(p, st);
-    case k128x256w8k64: return launch_act<128, 256, 2, 4, 64>(p, st);
-    case k128x384w8k64: return launch_act<128, 384, 2, 4, 64>(p, st);
-    default: return launch_act<32, 256, 1, 4, 64>(p, st);
+    case k256x256w8k64: return launch_act<256, 256, 2, 4, 64, 8>(p, st);
+    case k128x256w8k64: return launch_act<128, 256, 2, 4, 64, 8>(p, st);
+    case k128x384w8k64: return launch_act<128, 384, 2, 4, 64, 8>(p, st);
+    case k256x256w8d4: return launch_act<256, 256, 2, 4, 64, 4>(p, st);
+    case k128x256w8d4: return launch_act<128, 256, 2, 4, 64, 4>(p, st);
+    case k128x384w8d4: return launch_act<128, 384, 2, 4, 64, 4>(p, st);
+    default: return launch_act<32, 256, 1, 4, 64, 4>(p, st);
   }
 }
 
