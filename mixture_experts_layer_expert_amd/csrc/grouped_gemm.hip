@@ -57,6 +57,7 @@ namespace {
 // groups.  128-byte rows (BK=64): (row>>1)&7; 64-byte rows (BK=32): (row>>2)&3.
 template <int CPR>
 __device__ inline int swz(int row) {
+  if constexpr (CPR == 16) return row & 15;  // 256-byte rows (BK=128)
   return CPR == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
@@ -116,7 +117,7 @@ struct Tile {
   static constexpr int kFit = (150 * 1024) / kStageBytes;
   static constexpr int kStages = kFit > 8 ? 8 : (kFit < 2 ? 2 : kFit);
   static constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;
-  static_assert(BK == 32 || BK == 64, "BK 32 or 64");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "BK 32, 64 or 128");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile multiple of 32");
   static_assert(QA >= 1 && QB >= 1 && QA * RPI * NW == BM && QB * RPI * NW == BNB, "dma split");
@@ -428,6 +429,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // wave per SIMD the other wave keeps the MFMA pipe busy meanwhile.
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES, int DW>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
+  // one row tile per group: each weight panel is streamed by a single tile
+  constexpr bool ROTATE_K = BM <= 32;
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int CPR = TL::CPR, RPI = TL::RPI;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
@@ -511,7 +514,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   const uint32_t b_bytes = (uint32_t)p.n_out * (uint32_t)p.K * 2u;  // one expert's weight matrix
   __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc((void*)p.B, 0, b_bytes, kBufferWord3);
   __amdgpu_buffer_rsrc_t rsB2 = rsB1;
-  int i_dma = 0, kt_dma = 0, k1_dma = 0, job_issued = 0;
+  // kt_dma counts the k steps of the tile being loaded from its first one
+  // (k0_dma) to its end (k1_dma); the step loaded is k0_dma + (kt_dma -
+  // k0_dma + rot_dma) mod (k1_dma - k0_dma).  rot_dma rotates the order for
+  // tiles whose weight panel no other tile reads (ROTATE_K): their rows lie
+  // K*2 bytes apart, and with every workgroup at the same k offset the
+  // requests of a 4 KiB or 8 KiB row stride fall on few HBM channels (the
+  // decode layer's up projection, K = 2048, streamed 4.5 TB/s against
+  // 5.1 TB/s at other strides).  Tiles that share panels through L2 keep the
+  // plain order, so that their readers stay in step.
+  int i_dma = 0, kt_dma = 0, k0_dma = 0, k1_dma = 0, rot_dma = 0, job_issued = 0;
   // perm DMA for tile i into slot i & 1: lane l fetches the entry of tile
   // row wave*kRowsPerWave + l (clamped to the tile's last row, so always a
   // valid entry); only the first kRowsPerWave lanes' values are used.
@@ -562,14 +574,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     rsB2 = kSwiGLU ? __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.B2 + eoff), 0, b_bytes, kBufferWord3)
                    : rsB1;
     kt_dma = tile_k0(i);
+    k0_dma = kt_dma;
     k1_dma = tile_k1(i);
+    if constexpr (ROTATE_K)
+      rot_dma = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 7u + (uint32_t)i * 3u) % (uint32_t)(k1_dma - k0_dma)));
   };
   auto issue_next = [&]() {
     if (i_dma >= n_mine) return;
     const int stage = job_issued % STAGES;
     bf16* a_dst = sA + stage * TL::kLdsA;
     bf16* b_dst = sB + stage * TL::kLdsB;
-    const uint32_t kbytes = (uint32_t)kt_dma * BK * 2;
+    int kt = kt_dma;
+    if constexpr (ROTATE_K) {
+      kt += rot_dma;
+      if (kt >= k1_dma) kt -= k1_dma - k0_dma;
+    }
+    const uint32_t kbytes = (uint32_t)kt * BK * 2;
     if (dma_wave) {
 #pragma unroll
       for (int q = 0; q < QA; ++q)
@@ -808,11 +828,13 @@ namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
 enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, k256x256w8d4, k128x256w8d4,
-               k128x384w8d4, kNumCfg };
+               k128x384w8d4, k32x256w4k128, k32x128w4k128, kNumCfg };
 const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
-                                       "256x256w8d4", "128x256w8d4", "128x384w8d4"};
-const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128};
-const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384};
+                                       "256x256w8d4", "128x256w8d4", "128x384w8d4", "32x256w4k128",
+                                       "32x128w4k128"};
+const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128, 32, 32};
+const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384, 256, 128};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --
@@ -830,7 +852,7 @@ const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384};
 // costs more than the narrower tile (measured).  MOE_GEMM_TILE (tuning) forces one of the
 // instantiated shapes for both projections, MOE_GEMM_TILE_UP /
 // MOE_GEMM_TILE_DOWN for one.
-TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up) {
+TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up, int K) {
   static const char* forced_all = getenv("MOE_GEMM_TILE");
   static const char* forced_up = getenv("MOE_GEMM_TILE_UP");
   static const char* forced_down = getenv("MOE_GEMM_TILE_DOWN");
@@ -840,7 +862,10 @@ TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up) {
       if (!strcmp(forced, kCfgName[c])) return (TileCfg)c;
   if (expected_rows >= 192) return k256x256w8d4;
   if (expected_rows >= 48) return (up || max_rows > 128) ? k128x256w8d4 : k128x384w8d4;
-  return k32x256w4k64;
+  // weight streaming: the up projection's 256-byte row pieces (BK = 128)
+  // stream faster than 128-byte ones (decode layer, K = 2048: 146.6 ->
+  // 140.6 us); the down projection measured the same either way
+  return (up && K % 128 == 0) ? k32x256w4k128 : k32x256w4k64;
 }
 
 // Whether to let the kernel split its last round (which costs a second
@@ -864,7 +889,8 @@ bool allow_split(TileCfg c, const GroupedGemm& g, int64_t expected_rows, int64_t
 }  // namespace
 
 size_t grouped_gemm_bf16_part_bytes(int64_t expected_rows, int64_t max_rows) {
-  const TileCfg u = choose_cfg(expected_rows, max_rows, true), d = choose_cfg(expected_rows, max_rows, false);
+  // (K only picks between tiles of the same shape)
+  const TileCfg u = choose_cfg(expected_rows, max_rows, true, 64), d = choose_cfg(expected_rows, max_rows, false, 64);
   const int a = kCfgBM[u] * kCfgBN[u], b = kCfgBM[d] * kCfgBN[d];
   const size_t G = (size_t)gemm_grid();
   return G * (size_t)(a > b ? a : b) * sizeof(float) + 16 * (G + 1);  // partial tiles + header
@@ -886,7 +912,8 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
   p.K = g.K;
   p.n_out = g.n_out;
   p.act = g.act;
-  const TileCfg cfg = choose_cfg(expected_rows, max_rows, g.perm != nullptr);
+  TileCfg cfg = choose_cfg(expected_rows, max_rows, g.perm != nullptr, g.K);
+  if (g.K % (kCfgBK[cfg]) != 0) cfg = k32x256w4k64;  // a forced BK=128 shape on a K it does not divide
   p.part = (g.part && allow_split(cfg, g, expected_rows, max_rows)) ? g.part : nullptr;
   switch (cfg) {
     case k256x256w8k64: return launch_act<256, 256, 2, 4, 64, 8>(p, st);
@@ -895,6 +922,8 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
     case k256x256w8d4: return launch_act<256, 256, 2, 4, 64, 4>(p, st);
     case k128x256w8d4: return launch_act<128, 256, 2, 4, 64, 4>(p, st);
     case k128x384w8d4: return launch_act<128, 384, 2, 4, 64, 4>(p, st);
+    case k32x256w4k128: return launch_act<32, 256, 1, 4, 128, 4>(p, st);
+    case k32x128w4k128: return launch_act<32, 128, 1, 4, 128, 4>(p, st);
     default: return launch_act<32, 256, 1, 4, 64, 4>(p, st);
   }
 }
