@@ -79,22 +79,30 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, voff, soff, 0, 0);
 }
 
-// erf by formula 7.1.26 of Abramowitz and Stegun's Handbook of Mathematical
-// Functions: 1 - t(a1 + t(a2 + ... + t a5)) exp(-x^2), t = 1 / (1 + p|x|),
-// sign restored; |error| <= 1.5e-7 in exact arithmetic, about 5e-7 in fp32,
-// far below the bf16 rounding of the hidden activations.  One exponential,
-// one reciprocal and five FMAs, with no branch on the argument's range.
-__device__ inline float erf_as(float x) {
-  const float a = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  return copysignf(1.f - poly * __expf(-a * a), x);
+// GELU in its erf form, z * Phi(z) with Phi the standard normal CDF, without
+// transcendental instructions (the epilogue of short-K tiles is bound by
+// them): Phi(z) = 0.5 + z * P(z^2) for |z| <= 4, P of degree 8, and
+// Phi = (z > 0) beyond.  P is a least-squares Chebyshev fit of
+// (Phi(sqrt(u)) - 0.5) / sqrt(u) on u in [0, 16] (fit_gelu_poly.py in this
+// folder derives it); the fp32 evaluation below is within 3.2e-5 of Phi
+// everywhere (the largest error is the tail beyond |z| = 4), so GELU is
+// within 1.3e-4 absolute, below the bf16 rounding of the hidden
+// activations it produces.
+__device__ inline float gelu_erf(float z) {
+  const float u = z * z;
+  float p = 9.408924819e-11f;
+  p = fmaf(p, u, -7.887303300e-09f);
+  p = fmaf(p, u, 2.954978125e-07f);
+  p = fmaf(p, u, -6.637191087e-06f);
+  p = fmaf(p, u, 1.017005944e-04f);
+  p = fmaf(p, u, -1.146868260e-03f);
+  p = fmaf(p, u, 9.909445771e-03f);
+  p = fmaf(p, u, -6.644644696e-02f);
+  p = fmaf(p, u, 3.989348236e-01f);
+  float phi = fmaf(z, p, 0.5f);
+  if (u > 16.f) phi = z > 0.f ? 1.f : 0.f;
+  return z * phi;
 }
-__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.f + erf_as(z * 0.70710678118654752f)); }
 __device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
 template <int BM, int BNB, int WM, int WN, int BK_>
