@@ -68,47 +68,48 @@ MIN_STEPS = {"c5": 200}        # graph replays timed for the short decode step
 CPU_SAMPLE_TOKENS = {"c1": 1024, "c2": 16384, "c3": 2048, "c4": 256, "c5": 128, "c6": 512}
 
 
-# HBM traffic of the dominant launch, from two rocprofv3 --pmc runs of the
-# default command of each workload (FETCH_SIZE, then WRITE_SIZE: KiB per
-# dispatch, averaged over the dispatches of that launch), each scaled by the
-# ratio of known bytes to the counter's reading for a plain copy
-# (--copy-calibration).  A figure is used only while the kernel sources hash
-# to the value it was measured with; otherwise traffic is null.
-PMC_KERNEL_SOURCES = ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
-                      "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h")
-PMC_TRAFFIC = {  # workload -> kernel sources hash, then per launch: KiB per dispatch
-    "c2": {"sources": "4649bdfacb8eed23",
-           "fc1": {"fetch_kib": 309457.2, "write_kib": 91794.2},
-           # grouped_gemm_kernel<128, 256, 2, 4, 64, 2, 0, 3>
-           "fc2": {"fetch_kib": 341009.7, "write_kib": 22970.5},
-           # grouped_gemm_kernel<128, 384, 2, 4, 64, 0, 0, 2>
-           },
-    "c4": {"sources": "4649bdfacb8eed23",
-           "fc1": {"fetch_kib": 3361892.7, "write_kib": 458916.3},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2>
-           "fc2": {"fetch_kib": 1751301.1, "write_kib": 207205.8},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
-           },
-    "c5": {"sources": "4649bdfacb8eed23",
-           "fc1": {"fetch_kib": 363830.1, "write_kib": 2117.5},
-           # grouped_gemm_kernel<32, 256, 1, 4, 64, 3, 0, 4>
-           "fc2": {"fetch_kib": 181424.5, "write_kib": 3072.1},
-           # grouped_gemm_kernel<32, 256, 1, 4, 64, 0, 0, 4>
-           },
-    "c3": {"sources": "4649bdfacb8eed23",
-           "fc1": {"fetch_kib": 148374.3, "write_kib": 141576.7},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 1, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 1, 1>
-           "fc2": {"fetch_kib": 212318.8, "write_kib": 89725.9},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 1, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 1>
-           },
-    "c6": {"sources": "4649bdfacb8eed23",
-           "fc1": {"fetch_kib": 584125.9, "write_kib": 90145.4},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 3, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 3, 0>
-           "fc2": {"fetch_kib": 266221.2, "write_kib": 133114.6},
-           # grouped_gemm_kernel<256, 256, 2, 4, 64, 0, 0, 2> + splitk_finish_kernel<256, 256, 2, 4, 64, 0, 0>
-           },
+# Counters of each launch, from rocprofv3 --pmc runs of the plain command of
+# each workload (bench.py --workload W --extra= --steps 5 --warmup 2
+# --no-cpu-baseline --no-clock; profiles/ has the commands and summaries):
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each pass its own run), scaled
+# by the ratio of known bytes to the counter's reading for a plain copy
+# (--copy-calibration); and GRBM_GUI_ACTIVE (busy cycles summed over the 8
+# XCDs) with SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) and the
+# dispatch's duration, which give the sustained core clock and the MFMA pipe's
+# busy share.  Values are averaged over the dispatches of the launch (its
+# split-K finishing kernel included for the byte counts).  A figure is used
+# only while the kernel sources hash to the value it was measured with;
+# otherwise it is reported as null.
+PMC_KERNEL_SOURCES = {
+    "bf16": ("mixture_experts_layer_expert_amd/csrc/grouped_gemm.hip",
+             "mixture_experts_layer_expert_amd/csrc/grouped_gemm.h"),
+    "fp32": ("mixture_experts_layer_expert_amd/csrc/grouped_gemm_f32.hip",),
+}
+PMC_TRAFFIC = {
+    "c1": {"sources": "80377bbb4578fa6f",
+           "fc1": {"fetch_kib": 20173.9, "write_kib": 8192.0, "grbm": 662008, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 28824},
+           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 747366, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33833}},
+    "c2": {"sources": "c710cac9ff2b10cd",
+           "fc1": {"fetch_kib": 309514.0, "write_kib": 92423.8, "grbm": 2728855, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 151156},
+           "fc2": {"fetch_kib": 340956.3, "write_kib": 22978.0, "grbm": 2646090, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 143346}},
+    "c3": {"sources": "c710cac9ff2b10cd",
+           "fc1": {"fetch_kib": 148411.8, "write_kib": 135624.7, "grbm": 3089810, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 191183},
+           "fc2": {"fetch_kib": 212814.1, "write_kib": 89228.6, "grbm": 2525118, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 157344}},
+    "c4": {"sources": "c710cac9ff2b10cd",
+           "fc1": {"fetch_kib": 3405963.7, "write_kib": 458912.3, "grbm": 43965162, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3417831},
+           "fc2": {"fetch_kib": 1910062.0, "write_kib": 206385.5, "grbm": 23426945, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1849418}},
+    "c5": {"sources": "c710cac9ff2b10cd",
+           "fc1": {"fetch_kib": 365935.8, "write_kib": 2115.4, "grbm": 2537468, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 129394},
+           "fc2": {"fetch_kib": 182883.4, "write_kib": 3072.0, "grbm": 1402153, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 67865}},
+    "c6": {"sources": "c710cac9ff2b10cd",
+           "fc1": {"fetch_kib": 585217.9, "write_kib": 90202.8, "grbm": 5888886, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 402066},
+           "fc2": {"fetch_kib": 307299.1, "write_kib": 136477.8, "grbm": 3721357, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 233303}},
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
+# GRBM_GUI_ACTIVE also counts the counter window around the dispatch (about
+# 15-20 thousand cycles per XCD, measured on 30-130 us launches): the clock it
+# gives is used only for launches long enough for that to be under 1 %.
+COUNTER_CLOCK_MIN_NS = 1_000_000
 
 
 def parse():
@@ -199,20 +200,45 @@ def _code_only(text):
     return "\n".join(ln for ln in lines if ln)
 
 
-def sources_sha():
+def pmc_sources(workload):
+    """The GEMM sources whose kernels the workload's expert launches run."""
+    from workloads import get_config
+    return PMC_KERNEL_SOURCES[get_config(workload).dtype]
+
+
+def sources_sha(files):
     h = hashlib.sha256()
-    for rel in PMC_KERNEL_SOURCES:
+    for rel in files:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, launch):
+def _pmc(workload, launch):
     rec = PMC_TRAFFIC.get(workload)
-    if rec is None or launch not in rec or rec["sources"] != sources_sha():
+    if rec is None or launch not in rec or rec["sources"] != sources_sha(pmc_sources(workload)):
         return None
-    return (rec[launch]["fetch_kib"] * 1024.0 * PMC_COPY_FACTOR["fetch"]
-            + rec[launch]["write_kib"] * 1024.0 * PMC_COPY_FACTOR["write"])
+    return rec[launch]
+
+
+def measured_traffic(workload, launch):
+    r = _pmc(workload, launch)
+    if r is None:
+        return None
+    return (r["fetch_kib"] * 1024.0 * PMC_COPY_FACTOR["fetch"]
+            + r["write_kib"] * 1024.0 * PMC_COPY_FACTOR["write"])
+
+
+def counter_clock(workload, launch):
+    """Sustained clock (GHz) and MFMA-busy share of the launch's main kernel
+    from the counter run: GRBM_GUI_ACTIVE / 8 XCDs / duration, and
+    SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / (GRBM_GUI_ACTIVE / 8)."""
+    r = _pmc(workload, launch)
+    if r is None or "grbm" not in r or r["dur_ns"] < COUNTER_CLOCK_MIN_NS:
+        return None
+    cycles = r["grbm"] / 8.0
+    return {"ghz": cycles / (r["dur_ns"]), "mfma_busy": r["mfma_busy"] / r["simds"] / cycles,
+            "source": "rocprofv3 counters of the same command (profiles/)"}
 
 
 def copy_calibration():
@@ -333,7 +359,8 @@ def run_workload(key, args, *, headline):
             api.route_fallback(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate,
                                opts.reroute, fb_idx, fb_gate, None, s)
         else:
-            api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s)
+            api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, None, s,
+                      ws=buf.ws)
         if opts.reroute:
             api.dispatch_reroute(shape, opts.reroute, fb_idx, fb_gate, buf.topk_idx, buf.topk_gate, buf.counts,
                                  buf.offsets, buf.perm, buf.slot, buf.n_dropped, s)
@@ -419,7 +446,11 @@ def run_workload(key, args, *, headline):
         n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
         stamps = torch.zeros(4 * n_cu, dtype=torch.int64, device=dev)
         launch_us = stages[launch] * 1e3
-        delay_us, window_us = launch_us / 6.0, launch_us / 2.0
+        # wait a sixth of the launch, then a chain that lasts about half of
+        # it at 2.4 GHz (longer at a lower clock): 4 clocks per add, 1024
+        # adds per block
+        delay_us = launch_us / 6.0
+        iters = max(1, min(1 << 16, int(launch_us * 2400.0 / 2.0 / 4096.0)))
         readings = []
         for i in range(3):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -432,7 +463,7 @@ def run_workload(key, args, *, headline):
                     # start with the launch: the probe stream waits for the
                     # event recorded just before it
                     ps.wait_event(_ev[_a])
-                    api.clock_probe(n_cu, delay_us, window_us, stamps, ps)
+                    api.clock_probe(n_cu, delay_us, iters, stamps, ps)
                     _pe.record(ps)
 
             step(gs[i % R], st, ev, probe)
@@ -443,8 +474,9 @@ def run_workload(key, args, *, headline):
         if good:
             ghz = good[len(good) // 2]
             clock = {"ghz": ghz, "probes_inside_launch": len(good), "probes": len(readings),
-                     "method": "s_memtime cycles over s_memrealtime (100 MHz) ticks, one wave per CU on a "
-                               "second stream, window = middle half of the dominant launch"}
+                     "method": "moe_clock_probe: a chain of dependent 32-bit adds (4 shader clocks each) timed "
+                               "with the 100 MHz real-time counter, one wave per CU on a second stream, inside "
+                               "the dominant launch"}
         else:
             clock = {"ghz": None, "probes_inside_launch": 0, "probes": len(readings),
                      "idle_ghz": [c for c, _ in readings]}
@@ -507,12 +539,16 @@ def run_workload(key, args, *, headline):
                                 "y_perm and partial tiles are implementation bytes; 2 flops per MAC over "
                                 "kept rows"},
     }
-    if clock is not None and clock.get("ghz"):
-        clock_peak = peak * clock["ghz"] / SPEC_CLOCK_GHZ if bound == "mfma" else None
-        roof["clock_ghz"] = clock["ghz"]
-        if clock_peak:
-            roof["peak_at_clock"] = clock_peak
-            roof["frac_at_clock"] = achieved / clock_peak
+    cclk = counter_clock(key, launch) if plain else None
+    if cclk is not None:
+        roof["counters"] = cclk
+    ghz = (clock or {}).get("ghz") or (cclk or {}).get("ghz")
+    if ghz:
+        roof["clock_ghz"] = ghz
+        roof["clock_source"] = "moe_clock_probe during the launch" if (clock or {}).get("ghz") else cclk["source"]
+        if bound == "mfma":
+            roof["peak_at_clock"] = peak * ghz / SPEC_CLOCK_GHZ
+            roof["frac_at_clock"] = achieved / roof["peak_at_clock"]
     block = {
         "workload": cfg.name,
         "value": cfg.T / step_s,

@@ -143,10 +143,21 @@ int moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
  * Logits are accumulated in fp32; a token whose top-(k+1) fp32 logits lie
  * within 1e-4 of each other has all N logits recomputed in fp64 from the
  * exact products before it is ranked.  logits_opt (fp32 [T,N], may be NULL)
- * receives the logits used for the ranking, rounded to fp32. */
+ * receives the logits used for the ranking, rounded to fp32.
+ *
+ * ws is optional device scratch, as for moe_dispatch: NULL, or at least
+ * moe_workspace_bytes(shape) bytes with 256-byte alignment
+ * (MOE_ERR_WORKSPACE or MOE_ERR_INVALID_ARG otherwise).  With it, bf16
+ * batches of at most 1024 tokens (D a multiple of 128) take two launches
+ * spread over many workgroups: fp32 partial logit tiles of 128-wide slices
+ * of D, then their sum in fixed slice order and the ranking.  moe_forward
+ * makes the same choice, so a stage chain given the same workspace repeats
+ * its results bit for bit.  Without ws the router is one launch; the two
+ * can differ in the last bits of the fp32 logits and gates (the selection
+ * is the same: it is exact either way). */
 int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               const float* b_router, int32_t* topk_idx, float* topk_gate,
-              float* logits_opt, moe_stream_t stream);
+              float* logits_opt, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Router load statistics, the notebook's "Switch Transformer auxiliary loss"
  * and "Capacity factor" sections, computed in two steps.
@@ -350,16 +361,18 @@ int moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_rou
 /* Measurement helper (not a step of the layer): the shader clock the GPU
  * holds, for stating a kernel's throughput against the peak at the clock
  * actually sustained (the MFMA peak scales with the core clock).  Launches
- * `blocks` one-wave workgroups on `stream`; each waits delay_us, then counts
- * shader-clock cycles (s_memtime) over window_us of the 100 MHz real-time
- * counter (s_memrealtime) and writes stamps[4*b .. 4*b+3] = {realtime
- * start, realtime end, cycles start, cycles end} (device memory, uint64,
- * 4*blocks entries, caller-owned).  clock = (cycles) / (ticks) * 100 MHz.
- * Launched on a second stream while a kernel runs, the waves share that
- * kernel's compute units when its resources leave room for one more wave.
+ * `blocks` one-wave workgroups on `stream`; each waits delay_us, then runs
+ * a chain of 1024*iters dependent 32-bit integer adds (one per 4 shader
+ * clocks on a 16-lane SIMD) and writes stamps[4*b .. 4*b+3] = {100 MHz
+ * real-time counter at the chain's start, at its end, adds in the chain,
+ * the chain's value} (device memory, uint64, 4*blocks entries,
+ * caller-owned).  clock = 4 * adds / (ticks / 100 MHz).  Launched on a second
+ * stream while a kernel runs, the waves share that kernel's compute units
+ * when its resources leave room for one more wave; a SIMD busy with other
+ * vector instructions slows the chain, so the figure is a lower bound.
  * Errors: MOE_ERR_INVALID_ARG for blocks outside [1, 65536], a null stamps,
- * delay_us < 0, window_us <= 0 or delay_us + window_us > 100000. */
-int moe_clock_probe(int32_t blocks, double delay_us, double window_us, uint64_t* stamps,
+ * delay_us outside [0, 100000] or iters outside [1, 2^16]. */
+int moe_clock_probe(int32_t blocks, double delay_us, int32_t iters, uint64_t* stamps,
                     moe_stream_t stream);
 
 /* Static, human-readable text of a status code. */

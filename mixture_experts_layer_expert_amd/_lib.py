@@ -56,7 +56,7 @@ _shape_p = ctypes.POINTER(MoeShapeC)
 _SIGS = {
     "moe_capacity": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]),
     "moe_workspace_bytes": (ctypes.c_int, [_shape_p, ctypes.POINTER(ctypes.c_size_t)]),
-    "moe_route": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_stats_workspace_bytes": (ctypes.c_int, [_shape_p, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route_stats": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_router_stats": (ctypes.c_int, [_shape_p, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -76,7 +76,7 @@ _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_forward_noalloc": (ctypes.c_int, [_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_clock_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_double, ctypes.c_double, _vp, _vp]),
+    "moe_clock_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_double, ctypes.c_int32, _vp, _vp]),
 }
 
 _lib = None

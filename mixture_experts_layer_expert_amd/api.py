@@ -118,14 +118,17 @@ def workspace_bytes(shape: MoeShape) -> int:
     return int(n.value)
 
 
-def route(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, logits=None, stream=None):
+def route(shape: MoeShape, x, w_router, b_router, topk_idx, topk_gate, logits=None, stream=None, ws=None):
+    """ws (optional, >= workspace_bytes) lets few-token bf16 batches use the
+    two-launch split router, as moe_forward does."""
     dt = shape.torch_dtype
     sc = shape.c()
+    wp, wn = _ws_arg(ws)
     _check("moe_route", L.load().moe_route(
         ctypes.byref(sc), _ptr(x, dt, "x", shape.T * shape.D), _ptr(w_router, dt, "w_router", shape.N * shape.D),
         _ptr(b_router, torch.float32, "b_router", shape.N), _ptr(topk_idx, torch.int32, "topk_idx", shape.T * shape.k),
         _ptr(topk_gate, torch.float32, "topk_gate", shape.T * shape.k), _ptr(logits, torch.float32, "logits", shape.T * shape.N),
-        _stream(stream)))
+        wp, wn, _stream(stream)))
 
 
 def stats_workspace_bytes(shape: MoeShape) -> int:
@@ -269,21 +272,22 @@ def forward_noalloc(shape: MoeShape, x, w_router, b_router, w1, b1, w3, w2, b2, 
         _ptr(slot, i32, "slot", shape.T * shape.k), _ptr(n_dropped, i32, "n_dropped", 1), _stream(stream)))
 
 
-def clock_probe(blocks: int, delay_us: float, window_us: float, stamps, stream=None):
-    """Shader-clock probe (moe_clock_probe): stamps is a device int64 tensor of
-    at least 4*blocks entries, filled with {realtime start, realtime end,
-    cycles start, cycles end} per workgroup."""
+def clock_probe(blocks: int, delay_us: float, iters: int, stamps, stream=None):
+    """Shader-clock probe (moe_clock_probe): a chain of 1024*iters dependent
+    adds per workgroup; stamps is a device int64 tensor of at least 4*blocks
+    entries, filled with {realtime start, realtime end, adds in the chain,
+    chain value} per workgroup."""
     _check("moe_clock_probe", L.load().moe_clock_probe(
-        int(blocks), float(delay_us), float(window_us), _ptr(stamps, torch.int64, "stamps", 4 * int(blocks)),
+        int(blocks), float(delay_us), int(iters), _ptr(stamps, torch.int64, "stamps", 4 * int(blocks)),
         _stream(stream)))
 
 
 def probe_clock_ghz(stamps) -> float:
-    """Median core clock in GHz over the probe's workgroups: shader cycles per
-    tick of the 100 MHz real-time counter, times 0.1 GHz (host arithmetic on
-    the copied-back stamps)."""
+    """Median core clock in GHz over the probe's workgroups: 4 shader clocks
+    per dependent add, over the elapsed ticks of the 100 MHz real-time
+    counter (host arithmetic on the copied-back stamps)."""
     s = stamps.view(-1, 4).cpu().tolist()
-    rates = sorted((c1 - c0) / (r1 - r0) * 0.1 for r0, r1, c0, c1 in s if r1 > r0)
+    rates = sorted(4.0 * n / ((r1 - r0) * 10.0) for r0, r1, n, _ in s if r1 > r0)
     return rates[len(rates) // 2] if rates else float("nan")
 
 

@@ -53,16 +53,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 #pragma unroll
       for (int u = 0; u < W; ++u) acc[u] += (float)yv[u];
     }
+    // every slot and gate first, then every kept row, then the sums: the
+    // loads of all k choices are in flight together (few-token batches
+    // are latency-bound here)
+    int sl[kMaxTopK];
+    float gv[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        const int s = slot[t * k + j];
-        if (s >= 0) {
-          const float g = gate[t * k + j];
-          V yv = *(const V*)(y + (int64_t)s * D + c * W);
+      sl[j] = (j < k) ? slot[t * k + j] : -1;
+      gv[j] = (j < k) ? gate[t * k + j] : 0.f;
+    }
+    V yv[kMaxTopK];
 #pragma unroll
-          for (int u = 0; u < W; ++u) acc[u] = fmaf(g, (float)yv[u], acc[u]);
-        }
+    for (int j = 0; j < kMaxTopK; ++j)
+      if (sl[j] >= 0) yv[j] = *(const V*)(y + (int64_t)sl[j] * D + c * W);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (sl[j] >= 0) {
+#pragma unroll
+        for (int u = 0; u < W; ++u) acc[u] = fmaf(gv[j], (float)yv[j][u], acc[u]);
       }
     }
     V o;

@@ -107,6 +107,13 @@ size_t forward_ws_bytes(const moe_shape& s) {
   return align_up((size_t)group_rows(s) * s.D * elem_size(s)) + ffn_ws_bytes(s);
 }
 
+// The split router's partial tiles go in the expert stage's part of the
+// workspace (moe_forward) or at its start (moe_route); the one test decides
+// for both, so the stage chain and moe_forward run the same kernels.
+bool split_route_fits(const moe_shape& s) {
+  return use_split_route(s) && route_split_bytes(s) <= ffn_ws_bytes(s);
+}
+
 // Expert stage.  With the decode path the fp32 shard partials stay in ws;
 // y_perm is produced from them only when y_perm is non-null (stage API).
 GemmAct up_act(const moe_shape& s) {
@@ -196,13 +203,21 @@ int moe_workspace_bytes(const moe_shape* shape, size_t* bytes) {
 }
 
 int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* b_router,
-              int32_t* topk_idx, float* topk_gate, float* logits_opt, moe_stream_t stream) {
+              int32_t* topk_idx, float* topk_gate, float* logits_opt, void* ws, size_t ws_bytes,
+              moe_stream_t stream) {
   int v = validate(shape);
   if (v != MOE_OK) return v;
   const moe_shape& s = *shape;
   if (s.T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if ((s.flags & MOE_ROUTER_BIAS) && !b_router) return MOE_ERR_INVALID_ARG;
+  if (ws) {
+    if (ws_bytes < forward_ws_bytes(s)) return MOE_ERR_WORKSPACE;
+    if ((uintptr_t)ws % kAlign) return MOE_ERR_INVALID_ARG;
+    if (split_route_fits(s))
+      return hip_status(launch_route_split(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, (float*)ws,
+                                           (hipStream_t)stream));
+  }
   return hip_status(launch_route(s, x, w_router, b_router, topk_idx, topk_gate, logits_opt, nullptr, 0,
                                  nullptr, nullptr, (hipStream_t)stream));
 }
@@ -402,8 +417,12 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   hipStream_t st = (hipStream_t)stream;
   void* y_perm = ws;
   void* ffn_ws = (unsigned char*)ws + align_up((size_t)group_rows(s) * s.D * elem_size(s));
-  hipError_t e = launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, 0, nullptr,
-                              nullptr, st);
+  // few tokens: the split router, its partial tiles in the expert stage's
+  // workspace (dead before the dispatch runs)
+  hipError_t e = split_route_fits(s)
+                     ? launch_route_split(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, (float*)ffn_ws, st)
+                     : launch_route(s, x, w_router, b_router, topk_idx, topk_gate, nullptr, nullptr, 0, nullptr,
+                                    nullptr, st);
   // the dispatch scratch lives where the expert stage's workspace will be
   if (e == hipSuccess) e = dispatch_any(s, topk_idx, counts, offsets, perm, slot, n_dropped, ffn_ws, st);
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -33,6 +33,14 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const
                         int32_t* idx, float* gate, float* logits, float* prob_part, int R, int32_t* fb_idx,
                         float* fb_gate, hipStream_t st);
 
+// Router of few-token bf16 batches in two launches over many waves (partial
+// logit tiles per 128-wide k chunk, then sum and rank); part is device
+// scratch of route_split_bytes(s) bytes.  Same selection as launch_route.
+bool use_split_route(const moe_shape& s);
+size_t route_split_bytes(const moe_shape& s);
+hipError_t launch_route_split(const moe_shape& s, const void* x, const void* wr, const float* br, int32_t* idx,
+                              float* gate, float* logits, float* part, hipStream_t st);
+
 // Router blocks of a launch (tokens per block depend on the shape and the
 // device's CU count); prob_part holds N * route_blocks(s) floats.
 int route_rows_per_block(const moe_shape& s);

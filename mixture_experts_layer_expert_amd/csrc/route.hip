@@ -701,6 +701,116 @@ __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
   rank_rows<bf16, NT, TB / 16>(a, lg, ldl, t0, wave, lane);
 }
 
+// Split router for batches of few tokens (bf16, D a multiple of 128).  With
+// few tokens the ring kernel has few blocks, and each streams the whole
+// router matrix through one CU.  Here the work is spread over
+// (16-token tile, 64-expert group, 128-wide k chunk) waves:
+//  route_partial_kernel: one wave computes the 16 x 64 partial logit tile of
+//    its k chunk with v_mfma_f32_16x16x32_bf16, operands loaded straight into
+//    registers (lane group q of a row reads 64 contiguous bytes; A and B take
+//    the same k positions in each lane group, so every product pairs matching
+//    k), and stores it to part[chunk][token][expert];
+//  route_rank_kernel: one wave per 4 tokens sums the chunks of each logit in
+//    increasing chunk order (fixed order, so the result does not depend on
+//    timing), adds the router bias and ranks the tokens as the other kernels
+//    do (group_rank, exact re-ranking of near-ties).
+constexpr int kSplitChunk = 128;  // k per partial tile
+constexpr int kRankRows = 4;      // tokens per ranking wave
+
+template <int NE>  // expert tiles of 16 per wave (1..4)
+__global__ __launch_bounds__(64) void route_partial_kernel(RouteArgs a, float* part, int np) {
+  const int lane = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int e0 = blockIdx.y * 16 * NE;
+  const int kc = blockIdx.z;
+  const int D = a.D;
+  const int q = lane >> 4, r16 = lane & 15;
+  int64_t row = t0 + r16;
+  if (row > a.T - 1) row = a.T - 1;
+  const int koff = kc * kSplitChunk + q * (kSplitChunk / 4);
+  const bf16x8* xa = (const bf16x8*)((const bf16*)a.x + row * D + koff);
+  bf16x8 av[4], bv[NE][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) av[u] = xa[u];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    int e = e0 + n * 16 + r16;
+    if (e > a.N - 1) e = a.N - 1;
+    const bf16x8* wb = (const bf16x8*)((const bf16*)a.wr + (int64_t)e * D + koff);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bv[n][u] = wb[u];
+  }
+  f32x4 acc[NE];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[n][u], acc[n], 0, 0, 0);
+  }
+  // C layout: lane holds tokens 4q .. 4q+3 of column r16
+  float* dst = part + ((int64_t)kc * a.T) * np;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 4 * q + i;
+    if (t < a.T) {
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        const int e = e0 + n * 16 + r16;
+        if (e < np) dst[t * np + e] = acc[n][i];
+      }
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(64) void route_rank_kernel(RouteArgs a, const float* part, int np, int nchunks) {
+  constexpr int NP = 16 * NT;
+  constexpr int ldl = NP + 1;
+  __shared__ float lg[kRankRows * ldl];
+  const int lane = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * kRankRows;
+  // value i of the lane: token r = i / (NP / 64 rounded up), expert e
+  constexpr int PER = (kRankRows * NP + 63) / 64;
+  constexpr int kBatch = 8;
+  float acc[PER];
+  int64_t base[PER];
+  bool valid[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = i * 64 + lane;
+    const int r = f / NP, e = f % NP;
+    int64_t t = t0 + r;
+    valid[i] = (r < kRankRows) && (e < a.N) && (t < a.T);
+    if (t > a.T - 1) t = a.T - 1;
+    base[i] = t * np + (e < np ? e : np - 1);
+    acc[i] = (valid[i] && a.has_bias) ? a.br[e] : 0.f;
+  }
+  const int64_t cstride = (int64_t)a.T * np;
+  for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+    float v[kBatch][PER];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = (c0 + b < nchunks) ? c0 + b : nchunks - 1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[b][i] = part[c * cstride + base[i]];
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      if (c0 + b < nchunks) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += v[b][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = i * 64 + lane;
+    const int r = f / NP, e = f % NP;
+    if (r < kRankRows) lg[r * ldl + e] = valid[i] ? acc[i] : 0.f;
+  }
+  __syncthreads();
+  rank_rows<bf16, NT, 1>(a, lg, ldl, t0, 0, lane);
+}
+
 template <int NT, int TB>
 hipError_t launch_ring(const RouteArgs& a, hipStream_t st) {
   using R = RouteRing<NT, TB>;
@@ -745,6 +855,35 @@ hipError_t launch_t(const RouteArgs& a, int rows, hipStream_t st) {
   if (a.N <= 64) return launch_nt<T, 4>(a, st);
   if (a.N <= 128) return launch_nt<T, 8>(a, st);
   return launch_nt<T, 16>(a, st);
+}
+
+template <int NE>
+hipError_t launch_partial(const RouteArgs& a, float* part, int np, hipStream_t st) {
+  const dim3 grid((unsigned)((a.T + 15) / 16), (unsigned)((a.N + 16 * NE - 1) / (16 * NE)),
+                  (unsigned)(a.D / kSplitChunk));
+  hipLaunchKernelGGL(route_partial_kernel<NE>, grid, dim3(64), 0, st, a, part, np);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_rank(const RouteArgs& a, const float* part, int np, hipStream_t st) {
+  const int64_t blocks = (a.T + kRankRows - 1) / kRankRows;
+  hipLaunchKernelGGL(route_rank_kernel<NT>, dim3((unsigned)blocks), dim3(64), 0, st, a, part, np,
+                     a.D / kSplitChunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const RouteArgs& a, float* part, hipStream_t st) {
+  const int np = (a.N + 15) / 16 * 16;
+  hipError_t e = (a.N <= 16)   ? launch_partial<1>(a, part, np, st)
+                 : (a.N <= 32) ? launch_partial<2>(a, part, np, st)
+                               : launch_partial<4>(a, part, np, st);
+  if (e != hipSuccess) return e;
+  if (a.N <= 16) return launch_rank<1>(a, part, np, st);
+  if (a.N <= 32) return launch_rank<2>(a, part, np, st);
+  if (a.N <= 64) return launch_rank<4>(a, part, np, st);
+  if (a.N <= 128) return launch_rank<8>(a, part, np, st);
+  return launch_rank<16>(a, part, np, st);
 }
 
 // Statistics, second pass, one wave per expert e (grid N): lane l adds the
@@ -855,6 +994,37 @@ hipError_t launch_router_stats(const moe_shape& s, const float* part, const int3
   hipLaunchKernelGGL(router_stats_kernel, dim3(s.N), dim3(kWave), 0, st, part, (int)route_blocks(s), s.N, s.T,
                      s.k, counts, n_dropped, prob_mean, frac, summary, stats_ticket(s, part));
   return hipGetLastError();
+}
+
+// The split router takes bf16 batches of at most kSplitRouteMaxT tokens with
+// D a multiple of 128; its partial tiles need route_split_bytes(s) of scratch.
+constexpr int64_t kSplitRouteMaxT = 1024;
+
+bool use_split_route(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.D % kSplitChunk == 0 && s.T > 0 && s.T <= kSplitRouteMaxT;
+}
+
+size_t route_split_bytes(const moe_shape& s) {
+  const size_t np = (size_t)(s.N + 15) / 16 * 16;
+  return (size_t)(s.D / kSplitChunk) * (size_t)s.T * np * sizeof(float);
+}
+
+hipError_t launch_route_split(const moe_shape& s, const void* x, const void* wr, const float* br, int32_t* idx,
+                              float* gate, float* logits, float* part, hipStream_t st) {
+  RouteArgs a{};
+  a.x = x;
+  a.wr = wr;
+  a.br = br;
+  a.T = s.T;
+  a.D = s.D;
+  a.N = s.N;
+  a.k = s.k;
+  a.renorm = (s.flags & MOE_RENORM) ? 1 : 0;
+  a.has_bias = (s.flags & MOE_ROUTER_BIAS) ? 1 : 0;
+  a.idx = idx;
+  a.gate = gate;
+  a.logits = logits;
+  return launch_split(a, part, st);
 }
 
 hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const float* br,

@@ -197,9 +197,13 @@ def test_entry_points_reject_null_pointers_before_launch(lib):
     from mixture_experts_layer_expert_amd import _lib as L
     s = ctypes.byref(_shape())
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
-    assert lib.moe_route(s, None, fake, None, fake, fake, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(s, None, fake, None, fake, fake, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(_shape(flags=L.MOE_ROUTER_BIAS)), fake, fake, None, fake, fake,
-                         None, None) == L.MOE_ERR_INVALID_ARG
+                         None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # the router's optional scratch: too small, misaligned
+    assert lib.moe_route(s, fake, fake, None, fake, fake, None, fake, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_route(s, fake, fake, None, fake, fake, None, ctypes.c_void_p(0x1001), 1 << 40,
+                         None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch(s, fake, None, fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_INVALID_ARG
     # optional scratch: too small, misaligned
     assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, fake, 16, None) == L.MOE_ERR_WORKSPACE
@@ -239,7 +243,7 @@ def test_zero_tokens_is_a_no_op(lib):
     from mixture_experts_layer_expert_amd import _lib as L
     s = ctypes.byref(_shape(T=0))
     fake = ctypes.c_void_p(0x1000)
-    assert lib.moe_route(s, fake, fake, None, fake, fake, None, None) == L.MOE_OK
+    assert lib.moe_route(s, fake, fake, None, fake, fake, None, None, 0, None) == L.MOE_OK
     assert lib.moe_dispatch(s, fake, fake, fake, fake, fake, fake, None, 0, None) == L.MOE_OK
     assert lib.moe_combine(s, fake, fake, fake, None, fake, None) == L.MOE_OK
     assert lib.moe_expert_up(s, fake, fake, fake, fake, None, fake, fake, None, 0, None) == L.MOE_OK
@@ -307,10 +311,11 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
 def test_clock_probe_validates_on_the_host(lib):
     from mixture_experts_layer_expert_amd import _lib as L
     dummy = ctypes.c_void_p(0x1000)  # never dereferenced: each call fails validation
-    assert lib.moe_clock_probe(0, 0.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(65537, 0.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(4, 0.0, 10.0, None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(4, -1.0, 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(4, 0.0, 0.0, dummy, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(4, 50000.0, 60000.0, dummy, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_clock_probe(4, float("nan"), 10.0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(0, 0.0, 10, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(65537, 0.0, 10, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 0.0, 10, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, -1.0, 10, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 0.0, 0, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 0.0, (1 << 16) + 1, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, 200000.0, 10, dummy, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_clock_probe(4, float("nan"), 10, dummy, None) == L.MOE_ERR_INVALID_ARG

@@ -24,10 +24,13 @@ def _say(*a):
 
 
 # --------------------------------------------------------------- router
-@pytest.mark.parametrize("key", sorted(CONFIGS))
+@pytest.mark.parametrize("key", sorted(CONFIGS) + ["c5:ws"])
 def test_route_full_size(gpu, key):
+    """Every workload's router at full size; "c5:ws" gives moe_route the
+    workspace, which sends its 128 tokens through the split router."""
+    key, _, mode = key.partition(":")
     cfg = CONFIGS[key]
-    _say(f"route {cfg.name}")
+    _say(f"route {cfg.name} {mode}")
     inp = generate(cfg, parts=("x", "router"))
     ref = oracle.route(inp["x"], inp["w_router"], inp["b_router"], cfg.k, cfg.renorm)
     g = to_gpu(inp)
@@ -35,7 +38,8 @@ def test_route_full_size(gpu, key):
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=gpu)
     gate = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=gpu)
     logits = torch.empty(cfg.T, cfg.N, dtype=torch.float32, device=gpu)
-    api.route(shape, g["x"], g["w_router"], g["b_router"], idx, gate, logits)
+    ws = torch.empty(api.workspace_bytes(shape), dtype=torch.uint8, device=gpu) if mode == "ws" else None
+    api.route(shape, g["x"], g["w_router"], g["b_router"], idx, gate, logits, ws=ws)
     torch.cuda.synchronize()
     gerr = np.abs(gate.cpu().numpy() - ref["gate"]).max()
     lerr = np.abs(logits.cpu().numpy() - ref["logits"]).max()
@@ -148,16 +152,24 @@ def test_router_stats_graph_replay(gpu):
         torch.cuda.synchronize()
 
 
-def _route_case(gpu, x, w, k, renorm=False, b=None):
+def _route_case(gpu, x, w, k, renorm=False, b=None, split=False):
+    """moe_route against the oracle.  split: with the workspace, so that bf16
+    batches of at most 1024 tokens with D a multiple of 128 take the split
+    router (F = 2048 leaves room for its partial tiles in the workspace)."""
     T, D = x.shape
     N = w.shape[0]
     dt = "bf16" if x.dtype == torch.bfloat16 else "fp32"
-    shape = api.MoeShape(T=T, D=D, F=64, N=N, k=k, dtype=dt, act="relu", renorm=renorm,
+    shape = api.MoeShape(T=T, D=D, F=2048 if split else 64, N=N, k=k, dtype=dt, act="relu", renorm=renorm,
                          router_bias=b is not None)
+    if split:  # the split router's conditions, and room for its partial tiles after y_perm
+        assert dt == "bf16" and D % 128 == 0 and T <= 1024
+        y_perm_bytes = (shape.group_rows * D * 2 + 255) // 256 * 256
+        assert (D // 128) * T * ((N + 15) // 16 * 16) * 4 <= api.workspace_bytes(shape) - y_perm_bytes
     idx = torch.empty(T, k, dtype=torch.int32, device=gpu)
     gate = torch.empty(T, k, dtype=torch.float32, device=gpu)
     logits = torch.empty(T, N, dtype=torch.float32, device=gpu)
-    api.route(shape, x.to(gpu), w.to(gpu), None if b is None else b.to(gpu), idx, gate, logits)
+    ws = torch.empty(api.workspace_bytes(shape), dtype=torch.uint8, device=gpu) if split else None
+    api.route(shape, x.to(gpu), w.to(gpu), None if b is None else b.to(gpu), idx, gate, logits, ws=ws)
     torch.cuda.synchronize()
     ref = oracle.route(x, w, b, k, renorm)
     got = idx.cpu().numpy()
@@ -170,32 +182,38 @@ def _route_case(gpu, x, w, k, renorm=False, b=None):
     return got, gate.cpu().numpy(), ref
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_route_exact_ties_go_to_lower_index(gpu, dtype):
+@pytest.mark.parametrize("dtype,D,split", [(torch.bfloat16, 64, False), (torch.float32, 64, False),
+                                           (torch.bfloat16, 256, True)])
+def test_route_exact_ties_go_to_lower_index(gpu, dtype, D, split):
     """Small-integer inputs make logits exact integers with many ties; a
-    duplicated router row ties two experts on every token."""
+    duplicated router row ties two experts on every token.  The split case
+    sums two exact partial tiles per logit."""
     g = torch.Generator().manual_seed(0)
-    T, D, N = 333, 64, 8
+    T, N = 333, 8
     x = torch.randint(-2, 3, (T, D), generator=g).to(dtype)
     w = torch.randint(-1, 2, (N, D), generator=g).to(dtype)
     w[7] = w[2]
     for k in (1, 2, 5, N):
-        idx, gate, ref = _route_case(gpu, x, w, k)
+        idx, gate, ref = _route_case(gpu, x, w, k, split=split)
         assert np.array_equal(idx, ref["idx"]), k
         assert np.abs(gate - ref["gate"]).max() <= 1e-6  # every token re-ranked in fp64
 
 
-@pytest.mark.parametrize("N,k", [(1, 1), (2, 2), (16, 8), (64, 6), (200, 3), (256, 8), (256, 1)])
+@pytest.mark.parametrize("N,k", [(1, 1), (2, 2), (16, 8), (40, 3), (64, 6), (200, 3), (256, 8), (256, 1)])
 def test_route_shapes(gpu, N, k):
+    """Ragged token counts against the 64-, 16- and 4-token blocks, the one-
+    and the split router (D = 384: three partial tiles per logit), expert
+    counts that fill 16-wide tiles partly."""
     g = torch.Generator().manual_seed(N * 10 + k)
-    T, D = 1000, 128  # ragged against the 64-token blocks
+    T, D = 1000, 384
     x = torch.randn(T, D, generator=g).to(torch.bfloat16)
     w = (torch.randn(N, D, generator=g) * 0.05).to(torch.bfloat16)
     b = torch.randn(N, generator=g) * 0.1
-    for renorm in (False, True):
-        idx, gate, ref = _route_case(gpu, x, w, k, renorm, b)
-        assert np.array_equal(idx, ref["idx"])
-        assert np.abs(gate - ref["gate"]).max() <= GATE_ATOL["bf16"]
+    for split in (False, True):
+        for renorm in (False, True):
+            idx, gate, ref = _route_case(gpu, x, w, k, renorm, b, split)
+            assert np.array_equal(idx, ref["idx"]), (split, renorm)
+            assert np.abs(gate - ref["gate"]).max() <= GATE_ATOL["bf16"]
 
 
 # ------------------------------------------------------------- dispatch
@@ -354,7 +372,8 @@ def test_stage_chain(gpu, key, scaled_cases):
     g = to_gpu(inp)
     shape = api.MoeShape.from_config(cfg, fused_decode=fused)
     buf = api.MoeBuffers(shape)
-    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
+    # given the workspace, the router makes moe_forward's choice of kernels
+    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, ws=buf.ws)
     api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
     A = shape.group_rows
     y_perm = torch.empty(A, cfg.D, dtype=shape.torch_dtype, device=gpu)
@@ -402,7 +421,8 @@ def test_expert_up_down(gpu, key, scaled_cases):
     g = to_gpu(inp)
     shape = api.MoeShape.from_config(cfg)
     buf = api.MoeBuffers(shape)
-    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
+    # given the workspace, the router makes moe_forward's choice of kernels
+    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, ws=buf.ws)
     api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
     A = shape.group_rows
     h = torch.empty(A, cfg.F, dtype=shape.torch_dtype, device=gpu)
@@ -515,7 +535,8 @@ def test_split_last_round(gpu, key):
     g = to_gpu(inp)
     shape = api.MoeShape.from_config(cfg)
     buf = api.MoeBuffers(shape)
-    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate)
+    # given the workspace, the router makes moe_forward's choice of kernels
+    api.route(shape, g["x"], g["w_router"], g["b_router"], buf.topk_idx, buf.topk_gate, ws=buf.ws)
     api.dispatch(shape, buf.topk_idx, buf.counts, buf.offsets, buf.perm, buf.slot, buf.n_dropped)
     A = shape.group_rows
     K = int(off[-1])
