@@ -118,15 +118,34 @@ __device__ inline void wave_bases(int (*wcnt)[kMaxExperts], int* tot, int N, int
   }
 }
 
-// Inclusive scan of v[0..N) in place (all threads call it).
+// Inclusive scan of v[0..N) in LDS (N <= kMaxExperts) by the block's first
+// wave, 4 entries per lane (a shuffle scan of the lane totals), then a block
+// barrier: one barrier instead of two per doubling step.  Every thread calls
+// it, after a barrier that completes v.
 __device__ inline void block_scan(int* v, int N, int tid) {
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
-    int x = 0;
-    if (tid < N && tid >= d) x = v[tid - d];
-    __syncthreads();
-    if (tid < N && tid >= d) v[tid] += x;
-    __syncthreads();
+  static_assert(kMaxExperts <= 4 * kWave, "entries per lane");
+  if (tid < kWave) {
+    int a[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid * 4 + j;
+      s += (i < N) ? v[i] : 0;
+      a[j] = s;
+    }
+    int incl = s;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (tid >= off) incl += y;
+    }
+    const int base = incl - s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid * 4 + j;
+      if (i < N) v[i] = a[j] + base;
+    }
   }
+  __syncthreads();
 }
 
 // BITS >= 0: the expert-id bit count, fixed; -1: computed.  CH > 0: each
@@ -515,21 +534,7 @@ __global__ __launch_bounds__(kSegWaves * kWave) void dispatch_place_kernel(
   }
   __syncthreads();
   // offsets: exclusive scan of the kept counts (compact) or e*C (padded)
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
-    int v[kMaxExperts / kThr > 0 ? kMaxExperts / kThr : 1];
-#pragma unroll
-    for (int u = 0; u < (kMaxExperts + kThr - 1) / kThr; ++u) {
-      const int e = tid + u * kThr;
-      v[u] = (e < N && e >= d) ? scan[e - d] : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < (kMaxExperts + kThr - 1) / kThr; ++u) {
-      const int e = tid + u * kThr;
-      if (e < N && e >= d) scan[e] += v[u];
-    }
-    __syncthreads();
-  }
+  block_scan(scan, N, tid);
   const int ST = S * (int)T;
   for (int e = tid; e < N; e += kThr) {
     const int kept = scan[e] - (e > 0 ? scan[e - 1] : 0);

@@ -233,21 +233,31 @@ struct WorkList {
       }
     }
     __syncthreads();
-    for (int d = 1; d < N; d <<= 1) {
-      int v[kPer];
+    // inclusive scan of scan[0..N) by the first wave, kPer entries per lane
+    // (a shuffle scan of the lane totals): one barrier instead of two per
+    // doubling step, before the first tile's loads can be issued
+    if (tid < 64) {
+      int a[kPer], sum = 0;
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int e = tid + u * nthreads;
-        v[u] = (e < N && e >= d) ? scan[e - d] : 0;
+      for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        sum += (e < N) ? scan[e] : 0;
+        a[j] = sum;
       }
-      __syncthreads();
+      int incl = sum;
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int e = tid + u * nthreads;
-        if (e < N && e >= d) scan[e] += v[u];
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
       }
-      __syncthreads();
+      const int base = incl - sum;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int e = tid * kPer + j;
+        if (e < N) scan[e] = a[j] + base;
+      }
     }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = tid + u * nthreads;
