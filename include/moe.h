@@ -228,9 +228,9 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* count
                  int32_t* offsets, int32_t* perm, int32_t* slot, int32_t* n_dropped,
                  void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* Overflow fallback. The notebook's "What" section sends capacity overflow
- * to a fallback path. The first page's tuning tricks reroute rejected tokens
- * to less busy experts. Two calls implement this with R = n_fallback levels.
+/* Overflow fallback. The notebook's "What" section lets capacity overflow
+ * take a fallback instead of being dropped; among the first page's tuning
+ * tricks is moving rejected tokens to experts with spare room. Two calls implement this with R = n_fallback levels.
  * R must be >= 1 (MOE_ERR_INVALID_ARG otherwise). k + R must not exceed
  * min(8, N), and the layout must be compact, not MOE_PADDED; otherwise the
  * call returns MOE_ERR_UNSUPPORTED. T = 0 is a no-op.

@@ -103,7 +103,6 @@ __device__ inline float gelu_erf(float z) {
   if (u > 16.f) phi = z > 0.f ? 1.f : 0.f;
   return z * phi;
 }
-__device__ inline float silu(float z) { return z / (1.f + expf(-z)); }
 
 template <int BM, int BNB, int WM, int WN, int BK_>
 struct Tile {
@@ -448,7 +447,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES, int DW>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
   // one row tile per group: each weight panel is streamed by a single tile
-  constexpr bool ROTATE_K = BM <= 32;
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int CPR = TL::CPR, RPI = TL::RPI;
   constexpr bool kSwiGLU = (ACT == kActSwiGLU);
@@ -534,13 +532,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   __amdgpu_buffer_rsrc_t rsB2 = rsB1;
   // kt_dma counts the k steps of the tile being loaded from its first one
   // (k0_dma) to its end (k1_dma); the step loaded is k0_dma + (kt_dma -
-  // k0_dma + rot_dma) mod (k1_dma - k0_dma).  rot_dma rotates the order for
-  // tiles whose weight panel no other tile reads (ROTATE_K): their rows lie
-  // K*2 bytes apart, and with every workgroup at the same k offset the
-  // requests of a 4 KiB or 8 KiB row stride fall on few HBM channels (the
-  // decode layer's up projection, K = 2048, streamed 4.5 TB/s against
-  // 5.1 TB/s at other strides).  Tiles that share panels through L2 keep the
-  // plain order, so that their readers stay in step.
+  // k0_dma + rot_dma) mod (k1_dma - k0_dma).  Operand rows lie K*2 bytes
+  // apart, and with every workgroup at the same k offset the requests of a
+  // 4 KiB or 8 KiB row stride fall on few HBM channels (the decode layer's up
+  // projection, K = 2048, streamed 4.5 TB/s against 5.1 TB/s at other
+  // strides).  rot_dma therefore rotates the k order: per workgroup for
+  // 32-row tiles, whose weight panel no other tile reads; per XCD for larger
+  // tiles, which share panels through their XCD's L2, so that the readers of
+  // a panel stay in step while the XCDs start at different offsets.
   int i_dma = 0, kt_dma = 0, k0_dma = 0, k1_dma = 0, rot_dma = 0, job_issued = 0;
   // perm DMA for tile i into slot i & 1: lane l fetches the entry of tile
   // row wave*kRowsPerWave + l (clamped to the tile's last row, so always a
@@ -594,19 +593,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     kt_dma = tile_k0(i);
     k0_dma = kt_dma;
     k1_dma = tile_k1(i);
-    if constexpr (ROTATE_K)
+    if constexpr (BM <= 32)
       rot_dma = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 7u + (uint32_t)i * 3u) % (uint32_t)(k1_dma - k0_dma)));
+    else  // workgroup b runs on XCD b % 8
+      rot_dma = __builtin_amdgcn_readfirstlane((int)(((blockIdx.x & 7u) * (uint32_t)(k1_dma - k0_dma)) / 8u));
   };
   auto issue_next = [&]() {
     if (i_dma >= n_mine) return;
     const int stage = job_issued % STAGES;
     bf16* a_dst = sA + stage * TL::kLdsA;
     bf16* b_dst = sB + stage * TL::kLdsB;
-    int kt = kt_dma;
-    if constexpr (ROTATE_K) {
-      kt += rot_dma;
-      if (kt >= k1_dma) kt -= k1_dma - k0_dma;
-    }
+    int kt = kt_dma + rot_dma;
+    if (kt >= k1_dma) kt -= k1_dma - k0_dma;
     const uint32_t kbytes = (uint32_t)kt * BK * 2;
     if (dma_wave) {
 #pragma unroll

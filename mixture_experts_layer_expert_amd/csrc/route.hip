@@ -479,21 +479,22 @@ __device__ void exact_rank_wave(const RouteArgs& a, const float* lgrow, int64_t 
 // ranked (pacc[i]: expert l16 + 16 i).  Here the four groups of a wave are
 // summed with two xor shuffles, then the four waves in LDS, in a fixed
 // order.  Block 0 also clears the ticket of the second pass.
+// red: 4 * 16 * NT floats of LDS, not otherwise in use.
 template <int NT>
-__device__ void block_prob_sums(const RouteArgs& a, float (&pacc)[NT], int wave, int lane, int tid) {
+__device__ void block_prob_sums(const RouteArgs& a, float (&pacc)[NT], int wave, int lane, int tid, float* red) {
   constexpr int NP = 16 * NT;
-  __shared__ float red[4][NP];
   if (blockIdx.x == 0 && tid == 0) *a.stats_ticket = 0ull;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     float x = pacc[i];
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
-    if (lane < 16) red[wave][lane + 16 * i] = x;
+    if (lane < 16) red[wave * NP + lane + 16 * i] = x;
   }
   __syncthreads();
   for (int e = tid; e < a.N; e += 256)
-    a.prob_part[(int64_t)e * gridDim.x + blockIdx.x] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    a.prob_part[(int64_t)e * gridDim.x + blockIdx.x] =
+        ((red[e] + red[NP + e]) + red[2 * NP + e]) + red[3 * NP + e];
 }
 
 // Ranks the rows r = it*16 + wave*4 + group of the block's logits (16-lane
@@ -501,7 +502,7 @@ __device__ void block_prob_sums(const RouteArgs& a, float (&pacc)[NT], int wave,
 // then ranked again, one after the other, by the whole wave.
 template <typename T, int NT, int ITERS>
 __device__ void rank_rows(const RouteArgs& a, const float* lg, int ldl, int64_t t0, int wave,
-                          int lane) {
+                          int lane, float* red) {
   constexpr int NJ = (16 * NT + 63) / 64;
   const int grp = lane >> 4, l16 = lane & 15;
   float pacc[NT];
@@ -521,7 +522,7 @@ __device__ void rank_rows(const RouteArgs& a, const float* lg, int ldl, int64_t 
     for (int g = 0; g < 4; ++g)
       if ((bad >> (16 * g)) & 1ull) marked |= 1u << (it * 4 + g);
   }
-  if (stats) block_prob_sums<NT>(a, pacc, wave, lane, threadIdx.x);
+  if (stats) block_prob_sums<NT>(a, pacc, wave, lane, threadIdx.x, red);
   marked = __builtin_amdgcn_readfirstlane(marked);
   while (marked) {
     const int m = __builtin_ctz(marked);
@@ -538,6 +539,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   // k steps whose operands are loaded together (loads in flight per wave)
   constexpr int U = NT >= 16 ? 2 : (NT >= 8 ? 3 : (NT >= 4 ? 6 : 8));
   __shared__ float lg[32 * ldl];  // logits of the block's 32 tokens
+  __shared__ float red[4 * 16 * NT];  // statistics: per-wave probability sums
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int64_t t0 = (int64_t)blockIdx.x * 32;
@@ -549,7 +551,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  rank_rows<T, NT, 2>(a, lg, ldl, t0, wave, lane);
+  rank_rows<T, NT, 2>(a, lg, ldl, t0, wave, lane, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,7 +562,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 // block (64, 32 or 16): wave w computes m-tile w % (TB/16) over the k
 // sub-steps congruent to w / (TB/16); partial tiles are summed in LDS in
 // fixed wave order.  Selection and near-tie marking as above.
-template <int NT, int TB>
+// TWO: the ring is sized so that two blocks share a CU (80 KiB each),
+// so that one block's ranking overlaps the other's loads; otherwise it takes
+// up to 140 KiB.
+template <int NT, int TB, bool TWO>
 struct RouteRing {
   static constexpr int NP = 16 * NT;          // expert rows held (padded)
   static constexpr int MT = TB / 16;          // 16-token m-tiles per block
@@ -570,12 +575,15 @@ struct RouteRing {
   static constexpr int NJ = (IA + IB) / 4;    // per wave per stage
   static constexpr int kStageElems = (TB + NP) * 128;
   static constexpr int kStageBytes = kStageElems * 2;
-  static constexpr int S0 = (140 * 1024) / kStageBytes;
+  static constexpr int S0 = ((TWO ? 80 : 140) * 1024) / kStageBytes;
   static constexpr int S = S0 > 8 ? 8 : S0;
   static constexpr int kLogitFloats = KSPLIT * TB * (NP + 1);
-  static constexpr int kBytes =
-      (S * kStageBytes > kLogitFloats * 4) ? S * kStageBytes : kLogitFloats * 4;
+  static constexpr int kRedFloats = 4 * NP;  // statistics, after the logits
+  static constexpr int kBytes = (S * kStageBytes > (kLogitFloats + kRedFloats) * 4)
+                                    ? S * kStageBytes
+                                    : (kLogitFloats + kRedFloats) * 4;
   static_assert(S >= 2, "ring needs two stages");
+  static_assert(!TWO || kBytes <= 80 * 1024, "two blocks per CU");
   static_assert((IA + IB) % 4 == 0, "even dma split");
   static_assert(NJ * (S - 1) <= 63, "vmcnt range");
 };
@@ -598,9 +606,9 @@ __device__ inline void dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)l, 16, 0, 0);
 }
 
-template <int NT, int TB>
+template <int NT, int TB, bool TWO>
 __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
-  using R = RouteRing<NT, TB>;
+  using R = RouteRing<NT, TB, TWO>;
   constexpr int ldl = R::NP + 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* ring = (bf16*)smem_raw;
@@ -698,7 +706,7 @@ __global__ __launch_bounds__(256) void route_ring_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  rank_rows<bf16, NT, TB / 16>(a, lg, ldl, t0, wave, lane);
+  rank_rows<bf16, NT, TB / 16>(a, lg, ldl, t0, wave, lane, lg + R::kLogitFloats);
 }
 
 // Split router for batches of few tokens (bf16, D a multiple of 128).  With
@@ -808,13 +816,13 @@ __global__ __launch_bounds__(64) void route_rank_kernel(RouteArgs a, const float
     if (r < kRankRows) lg[r * ldl + e] = valid[i] ? acc[i] : 0.f;
   }
   __syncthreads();
-  rank_rows<bf16, NT, 1>(a, lg, ldl, t0, 0, lane);
+  rank_rows<bf16, NT, 1>(a, lg, ldl, t0, 0, lane, nullptr);  // never with statistics
 }
 
-template <int NT, int TB>
+template <int NT, int TB, bool TWO>
 hipError_t launch_ring(const RouteArgs& a, hipStream_t st) {
-  using R = RouteRing<NT, TB>;
-  auto kern = route_ring_kernel<NT, TB>;
+  using R = RouteRing<NT, TB, TWO>;
+  auto kern = route_ring_kernel<NT, TB, TWO>;
   static const hipError_t attr_err =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, R::kBytes);
   if (attr_err != hipSuccess) return attr_err;
@@ -823,13 +831,17 @@ hipError_t launch_ring(const RouteArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// rows < 0: -rows tokens per block, two blocks per CU
 template <int NT>
 hipError_t launch_ring_nt(const RouteArgs& a, int rows, hipStream_t st) {
   if constexpr (NT < 16) {
-    if (rows == 64) return launch_ring<NT, 64>(a, st);
-    if (rows == 32) return launch_ring<NT, 32>(a, st);
+    if (rows == 64) return launch_ring<NT, 64, false>(a, st);
+    if (rows == 32) return launch_ring<NT, 32, false>(a, st);
   }
-  return launch_ring<NT, 16>(a, st);
+  if constexpr (NT == 8) {
+    if (rows == -32) return launch_ring<NT, 32, true>(a, st);
+  }
+  return launch_ring<NT, 16, false>(a, st);
 }
 
 template <typename T, int NT>
@@ -961,20 +973,27 @@ __global__ __launch_bounds__(64) void router_stats_kernel(const float* part, int
 
 }  // namespace
 
-// Tokens per router block.  bf16 with D a multiple of 128 uses the DMA ring
-// kernel: as many tokens as keep >= ~2 blocks per CU busy, 16 for the widest
-// expert counts (their ring stages are large) and for at most 16 experts
-// (8 KiB stages: an 8-deep ring and two blocks per CU beat fewer, larger
-// blocks); otherwise 32.
-int route_rows_per_block(const moe_shape& s) {
+// Tokens per router block, negated when the ring is sized for two blocks
+// per CU.  bf16 with D a multiple of 128 uses the DMA ring kernel: as many
+// tokens as keep >= ~2 blocks per CU busy, 16 for the widest expert counts
+// (their ring stages are large) and for at most 16 experts (8 KiB stages: an
+// 8-deep ring and two blocks per CU beat fewer, larger blocks); with 65-128
+// experts and at least 64 tokens per CU, 32-token blocks two to a CU, so
+// that one block ranks while the other loads; otherwise 32.
+static int route_block_mode(const moe_shape& s) {
   if (s.dtype == MOE_DTYPE_BF16 && s.D % 128 == 0) {
     if (s.N > 128 || s.N <= 16) return 16;
     const int64_t cus = device_cu_count();
-    if (s.T >= 64 * cus) return 64;
+    if (s.T >= 64 * cus) return s.N > 64 ? -32 : 64;
     if (s.T >= 32 * cus) return 32;
     return 16;
   }
   return 32;
+}
+
+int route_rows_per_block(const moe_shape& s) {
+  const int m = route_block_mode(s);
+  return m < 0 ? -m : m;
 }
 
 int64_t route_blocks(const moe_shape& s) {
@@ -1048,7 +1067,7 @@ hipError_t launch_route(const moe_shape& s, const void* x, const void* wr, const
   a.fb_gate = fb_gate;
   a.prob_part = prob_part;
   a.stats_ticket = prob_part ? stats_ticket(s, prob_part) : nullptr;
-  const int rows = route_rows_per_block(s);
+  const int rows = route_block_mode(s);
   if (s.dtype == MOE_DTYPE_BF16) return launch_t<bf16>(a, rows, st);
   return launch_t<float>(a, rows, st);
 }

@@ -208,8 +208,8 @@ def reroute(disp: dict, idx: np.ndarray, gate: np.ndarray, fb_idx: np.ndarray, f
             N: int, C: Optional[int]) -> dict:
     """Overflow fallback after the capacity cut: a dropped assignment is sent
     to the token's next-best expert that still has room (the notebook's
-    "What" section names a fallback path for the overflow; rerouting rejected
-    tokens to less busy experts is the first page's tuning trick).
+    "What" section allows a fallback for the overflow; moving rejected tokens
+    to experts with spare room is one of the first page's tuning tricks).
 
     Level r = 0 .. R-1: every token with a dropped assignment left offers its
     lowest-j one to its expert of rank k + r (``fb_idx[t, r]``); each expert
