@@ -7,8 +7,8 @@
 One step is one whole layer forward (router, dispatch with capacity, expert
 MLPs, combine) over the workload's batch, inputs and weights already resident
 in HBM.  The step runs the C-ABI chain moe_route -> moe_dispatch ->
-moe_expert_up -> moe_expert_down -> moe_combine (the kernels of moe_forward,
-in the same order) with HIP events between the launches on the launch
+moe_expert_up -> moe_expert_down -> moe_combine, each given the workspace
+(the kernels of moe_forward, in the same order) with HIP events between the launches on the launch
 stream, so every launch's duration is measured live.  Consecutive steps
 cycle over --copies separate copies of x and the weights, so that no step
 finds its weights in the 256 MB last-level cache from the step before.

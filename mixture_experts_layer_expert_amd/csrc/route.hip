@@ -779,7 +779,7 @@ __global__ __launch_bounds__(64) void route_rank_kernel(RouteArgs a, const float
   const int64_t t0 = (int64_t)blockIdx.x * kRankRows;
   // value i of the lane: token r = i / (NP / 64 rounded up), expert e
   constexpr int PER = (kRankRows * NP + 63) / 64;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;  // partial loads in flight per value (one batch for D <= 2048)
   float acc[PER];
   int64_t base[PER];
   bool valid[PER];
