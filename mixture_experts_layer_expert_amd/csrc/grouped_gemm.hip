@@ -43,6 +43,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -421,6 +423,26 @@ __device__ inline void store_tile(const Params& p, const TileInfo& tc,
   }
 }
 
+// store_tile for a wave holding FMX 32-token blocks, the first of which is
+// block jbase of the tile (the asymmetric split of the token blocks).
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int FMX>
+__device__ inline void store_tile_x(const Params& p, const TileInfo& tc,
+                                    f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][FMX], int jbase, int wn, int lane,
+                                    const bf16* bias_lds) {
+  using TL = Tile<BM, BNB, WM, WN, BK>;
+  constexpr int PAIR = (ACT == kActSwiGLU) ? 2 : 1;
+#pragma unroll
+  for (int j = 0; j < FMX; ++j) {
+#pragma unroll
+    for (int u = 0; u < TL::FN / PAIR; ++u) {
+      // wm = 0 with block index jbase + j: the row is row0 + (jbase + j) * 32
+      store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc[u * PAIR][j], acc[u * PAIR + PAIR - 1][j], 0, wn,
+                                                      jbase + j, u, lane, bias_lds);
+      __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
+    }
+  }
+}
+
 // Partial tile q of the split last round: element (wave, i, j, r, lane) of
 // the accumulators at a fixed position, so that stores and loads are whole
 // 256-byte wave rows.
@@ -441,10 +463,12 @@ __device__ inline int* split_header(const Params& p, int G) {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // DW: the waves that issue the operand DMA (all NW, or NW/2 = one per SIMD).
+// FMD: 0, or the 32-token MFMA blocks of a DMA wave when the two waves of a
+// SIMD split the tile's 2 * FM blocks unevenly (DW = NW/2, WM = 2).
 // A wave that issues a job's DMA stalls at issue while the texture unit takes
 // the CU's burst of 1 KiB instructions (about 20 cycles each); with one DMA
 // wave per SIMD the other wave keeps the MFMA pipe busy meanwhile.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES, int DW>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int STAGES, int DW, int FMD>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p) {
   // one row tile per group: each weight panel is streamed by a single tile
   using TL = Tile<BM, BNB, WM, WN, BK>;
@@ -544,7 +568,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   // perm DMA for tile i into slot i & 1: lane l fetches the entry of tile
   // row wave*kRowsPerWave + l (clamped to the tile's last row, so always a
   // valid entry); only the first kRowsPerWave lanes' values are used.
-  auto fetch_perm = [&](int i) {
+  auto fetch_perm = [&](int i) __attribute__((always_inline)) {
     if (!p.perm || i >= n_mine || !dma_wave) return;
     const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
     int r = t.row0 + wave * kRowsPerWave + (lane < kRowsPerWave ? lane : 0);
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     __builtin_amdgcn_global_load_lds(p.perm + r, (lds_ptr_t)&s_perm[wave][i & 1][0], 4, 0, 0);
   };
   int jobs_since_fetch = 0;  // DMA jobs issued after the last perm fetch
-  auto setup_dma = [&](int i) {
+  auto setup_dma = [&](int i) __attribute__((always_inline)) {
     const TileInfo t = wl.info(p, s_tile_start, s_off, tile_L(i));
     if (p.perm && dma_wave) {
       // the fetch for tile i is older than every job issued since: wait for
@@ -598,7 +622,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     else  // workgroup b runs on XCD b % 8
       rot_dma = __builtin_amdgcn_readfirstlane((int)(((blockIdx.x & 7u) * (uint32_t)(k1_dma - k0_dma)) / 8u));
   };
-  auto issue_next = [&]() {
+  auto issue_next = [&]() __attribute__((always_inline)) {
     if (i_dma >= n_mine) return;
     const int stage = job_issued % STAGES;
     bf16* a_dst = sA + stage * TL::kLdsA;
@@ -641,106 +665,126 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   // next job are read while the last sub-step's MFMAs run.
   constexpr int KS = BK / 16;
   const int n_jobs = wl.rounds * KT + (has_rem ? k1_rem - k0_rem : 0);
-  bf16x8 bf[2][TL::FN], af[2][TL::FM];
-  auto load_frags = [&](int stage, int ks, int buf) {
-    const bf16* a_s = sA + stage * TL::kLdsA;
-    const bf16* b_s = sB + stage * TL::kLdsB;
-    const int c = 2 * ks + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TL::FN; ++i) {
-      const int row = wn * TL::TN + i * 32 + (lane & 31);
-      bf[buf][i] = *(const bf16x8*)(b_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
-    }
-#pragma unroll
-    for (int j = 0; j < TL::FM; ++j) {
-      const int row = wm * TL::TM + j * 32 + (lane & 31);
-      af[buf][j] = *(const bf16x8*)(a_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
-    }
-  };
-  f32x16 acc[TL::FN][TL::FM];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::FM; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  };
-  auto mfmas = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[buf][i], af[buf][j], acc[i][j], 0, 0, 0);
-  };
-  // interleave: one fragment read per (FN*FM)/(FN+FM) MFMAs
-  auto interleave = [&]() {
-    constexpr int NR = TL::FN + TL::FM, NM = TL::FN * TL::FM;
-    constexpr int PER = NM / NR > 0 ? NM / NR : 1;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
-    }
-  };
-
-  int i_cmp = 0, kt_cmp = 0, len_cmp = 0;
-  TileInfo tc;
-  if (n_jobs > 0) {
-    tc = wl.info(p, s_tile_start, s_off, tile_L(0));
-    len_cmp = tile_k1(0) - tile_k0(0);
-    if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - 1);
-    ring_barrier();
-    load_frags(0, 0, 0);
-  }
-  zero_acc();
-  for (int job = 0; job < n_jobs; ++job) {
-    const int stage = job % STAGES;
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      load_frags(stage, ks + 1, (ks + 1) & 1);
-      mfmas(ks & 1);
-      interleave();
-    }
-    // all fragments of this job are in registers: refill its stage later
-    const bool more = job + 1 < n_jobs;
-    if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - (job + 1) - 1);
-    ring_barrier();
-    issue_next();
-    if (more) load_frags((job + 1) % STAGES, 0, KS & 1);
-    mfmas((KS - 1) & 1);
-    if (more) interleave();
-    // a finished tile goes through the epilogue, except a K chunk of a split
-    // left-over tile (always this workgroup's last): its partial sums are
-    // stored after the loop
-    if (++kt_cmp == len_cmp && more) {
-      // a wave without tile DMA waits for its bias slice here
-      if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
-                                                       (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
-      kt_cmp = 0;
-      ++i_cmp;
-      tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
-      len_cmp = tile_k1(i_cmp) - tile_k0(i_cmp);
-      zero_acc();
-    }
-  }
-  if (n_jobs > 0) {
-    if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (!has_rem || wl.S == 1) {
-      store_tile<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc, wm, wn, lane,
-                                                       (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
-    } else {
-      float* dst = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, wave, lane);
-#pragma unroll
+  // Token blocks of this wave: FM 32-token blocks from wm * FM, or with an
+  // asymmetric split (FMD > 0) FMD blocks for the DMA wave of a SIMD and the
+  // rest of the 2 * FM blocks for the other wave, so that the wave that also
+  // issues the operand DMA has fewer MFMAs to issue.
+  constexpr int FM_DMA = FMD > 0 ? FMD : TL::FM;
+  constexpr int FM_OTHER = FMD > 0 ? 2 * TL::FM - FMD : TL::FM;
+  static_assert(FMD == 0 || (WM == 2 && DW * 2 == TL::NW && FMD >= 1 && FMD < 2 * TL::FM), "asymmetric split");
+  const int jbase = FMD > 0 ? (dma_wave ? 0 : FMD) : wm * TL::FM;
+  auto run = [&](auto fm_tag) __attribute__((always_inline)) {
+    constexpr int FMX = decltype(fm_tag)::value;
+    bf16x8 bf[2][TL::FN], af[2][FMX];
+    auto load_frags = [&](int stage, int ks, int buf) __attribute__((always_inline)) {
+      const bf16* a_s = sA + stage * TL::kLdsA;
+      const bf16* b_s = sB + stage * TL::kLdsB;
+      const int c = 2 * ks + (lane >> 5);
+  #pragma unroll
+      for (int i = 0; i < TL::FN; ++i) {
+        const int row = wn * TL::TN + i * 32 + (lane & 31);
+        bf[buf][i] = *(const bf16x8*)(b_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
+      }
+  #pragma unroll
+      for (int j = 0; j < FMX; ++j) {
+        const int row = (jbase + j) * 32 + (lane & 31);
+        af[buf][j] = *(const bf16x8*)(a_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
+      }
+    };
+    f32x16 acc[TL::FN][FMX];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+  #pragma unroll
       for (int i = 0; i < TL::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::FM; ++j) {
-          float* d = dst + (i * TL::FM + j) * 1024;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) d[r * 64] = acc[i][j][r];
-        }
+  #pragma unroll
+        for (int j = 0; j < FMX; ++j)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    };
+    auto mfmas = [&](int buf) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int i = 0; i < TL::FN; ++i)
+  #pragma unroll
+        for (int j = 0; j < FMX; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[buf][i], af[buf][j], acc[i][j], 0, 0, 0);
+    };
+    // interleave: one fragment read per (FN*FM)/(FN+FM) MFMAs
+    auto interleave = [&]() __attribute__((always_inline)) {
+      constexpr int NR = TL::FN + FMX, NM = TL::FN * FMX;
+      constexpr int PER = NM / NR > 0 ? NM / NR : 1;
+  #pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
+      }
+    };
+
+    int i_cmp = 0, kt_cmp = 0, len_cmp = 0;
+    TileInfo tc;
+    if (n_jobs > 0) {
+      tc = wl.info(p, s_tile_start, s_off, tile_L(0));
+      len_cmp = tile_k1(0) - tile_k0(0);
+      if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - 1);
+      ring_barrier();
+      load_frags(0, 0, 0);
     }
+    zero_acc();
+    for (int job = 0; job < n_jobs; ++job) {
+      const int stage = job % STAGES;
+  #pragma unroll
+      for (int ks = 0; ks < KS - 1; ++ks) {
+        load_frags(stage, ks + 1, (ks + 1) & 1);
+        mfmas(ks & 1);
+        interleave();
+      }
+      // all fragments of this job are in registers: refill its stage later
+      const bool more = job + 1 < n_jobs;
+      if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - (job + 1) - 1);
+      ring_barrier();
+      issue_next();
+      if (more) load_frags((job + 1) % STAGES, 0, KS & 1);
+      mfmas((KS - 1) & 1);
+      if (more) interleave();
+      // a finished tile goes through the epilogue, except a K chunk of a split
+      // left-over tile (always this workgroup's last): its partial sums are
+      // stored after the loop
+      if (++kt_cmp == len_cmp && more) {
+        // a wave without tile DMA waits for its bias slice here
+        if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, BIAS, FMX>(p, tc, acc, jbase, wn, lane,
+                                                         (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
+        kt_cmp = 0;
+        ++i_cmp;
+        tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
+        len_cmp = tile_k1(i_cmp) - tile_k0(i_cmp);
+        zero_acc();
+      }
+    }
+    if (n_jobs > 0) {
+      if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (!has_rem || wl.S == 1) {
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, BIAS, FMX>(p, tc, acc, jbase, wn, lane,
+                                                         (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
+      } else {
+        // in the symmetric layout the finishing kernel reads: block g of the
+        // tile's 32-token blocks belongs to wave (g / FM) * WN + wn, slot g % FM
+  #pragma unroll
+        for (int i = 0; i < TL::FN; ++i)
+  #pragma unroll
+          for (int j = 0; j < FMX; ++j) {
+            const int g = jbase + j;
+            float* d = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, (g / TL::FM) * WN + wn, lane) +
+                       (i * TL::FM + g % TL::FM) * 1024;
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) d[r * 64] = acc[i][j][r];
+          }
+      }
+    }
+  };
+  if constexpr (FMD > 0) {
+    if (dma_wave) run(std::integral_constant<int, FM_DMA>{});
+    else run(std::integral_constant<int, FM_OTHER>{});
+  } else {
+    run(std::integral_constant<int, TL::FM>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -797,11 +841,11 @@ __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
   }
 }
 
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int DW>
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int DW, int FMD>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int S = TL::kStages;
-  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, BIAS, S, DW>;
+  auto kern = grouped_gemm_kernel<BM, BNB, WM, WN, BK, ACT, BIAS, S, DW, FMD>;
   // once per process and instantiation (thread-safe static initialisation)
   static const hipError_t attr_err = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)TL::kLdsBytes);
@@ -818,23 +862,23 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BNB, int WM, int WN, int BK, int DW>
+template <int BM, int BNB, int WM, int WN, int BK, int DW, int FMD = 0>
 hipError_t launch_act(const Params& p, hipStream_t st) {
   const bool bias = p.bias != nullptr;
   switch (p.act) {
     case kActGelu:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActGelu, true, DW>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActGelu, false, DW>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActGelu, true, DW, FMD>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActGelu, false, DW, FMD>(p, st);
     case kActRelu:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true, DW>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false, DW>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActRelu, true, DW, FMD>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActRelu, false, DW, FMD>(p, st);
     case kActSwiGLU:
       // the SwiGLU epilogue pairs each wave's w1 and w3 32-row groups
-      if constexpr ((BNB / WN / 32) % 2 == 0) return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false, DW>(p, st);
+      if constexpr ((BNB / WN / 32) % 2 == 0) return launch_cfg<BM, BNB, WM, WN, BK, kActSwiGLU, false, DW, FMD>(p, st);
       else return hipErrorInvalidValue;
     default:
-      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true, DW>(p, st)
-                  : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false, DW>(p, st);
+      return bias ? launch_cfg<BM, BNB, WM, WN, BK, kActNone, true, DW, FMD>(p, st)
+                  : launch_cfg<BM, BNB, WM, WN, BK, kActNone, false, DW, FMD>(p, st);
   }
 }
 
@@ -844,13 +888,13 @@ namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
 enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, k256x256w8d4, k128x256w8d4,
-               k128x384w8d4, k32x256w4k128, k32x128w4k128, kNumCfg };
+               k128x384w8d4, k32x256w4k128, k32x128w4k128, k256x256w8a3, k128x256w8a1, kNumCfg };
 const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
                                        "256x256w8d4", "128x256w8d4", "128x384w8d4", "32x256w4k128",
-                                       "32x128w4k128"};
+                                       "32x128w4k128", "256x256w8a3", "128x256w8a1"};
 const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128, 32, 32};
 const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384, 256, 128};
-const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128, 64, 64};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --
@@ -876,7 +920,11 @@ TileCfg choose_cfg(int64_t expected_rows, int64_t max_rows, bool up, int K) {
   if (forced)
     for (int c = 0; c < kNumCfg; ++c)
       if (!strcmp(forced, kCfgName[c])) return (TileCfg)c;
-  if (expected_rows >= 192) return k256x256w8d4;
+  // 256x256 up projections split the token blocks 3:5 between the DMA wave
+  // and the other wave of each SIMD (Mixtral fc1 3261 -> 3067 us, the
+  // shared-expert layer's 420 -> 408 us, the skewed layer's even); the down
+  // projections measured slower that way (1685 -> 1822 us, 166 -> 199 us)
+  if (expected_rows >= 192) return up ? k256x256w8a3 : k256x256w8d4;
   if (expected_rows >= 48) return (up || max_rows > 128) ? k128x256w8d4 : k128x384w8d4;
   // weight streaming: the up projection's 256-byte row pieces (BK = 128)
   // stream faster than 128-byte ones (decode layer, K = 2048: 146.6 ->
@@ -936,6 +984,8 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
     case k128x256w8k64: return launch_act<128, 256, 2, 4, 64, 8>(p, st);
     case k128x384w8k64: return launch_act<128, 384, 2, 4, 64, 8>(p, st);
     case k256x256w8d4: return launch_act<256, 256, 2, 4, 64, 4>(p, st);
+    case k256x256w8a3: return launch_act<256, 256, 2, 4, 64, 4, 3>(p, st);
+    case k128x256w8a1: return launch_act<128, 256, 2, 4, 64, 4, 1>(p, st);
     case k128x256w8d4: return launch_act<128, 256, 2, 4, 64, 4>(p, st);
     case k128x384w8d4: return launch_act<128, 384, 2, 4, 64, 4>(p, st);
     case k32x256w4k128: return launch_act<32, 256, 1, 4, 128, 4>(p, st);
