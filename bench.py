@@ -87,23 +87,23 @@ PMC_KERNEL_SOURCES = {
 }
 PMC_TRAFFIC = {
     "c1": {"sources": "80377bbb4578fa6f",
-           "fc1": {"fetch_kib": 20173.9, "write_kib": 8192.0, "grbm": 662008, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 28824},
-           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 747366, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33833}},
-    "c2": {"sources": "c710cac9ff2b10cd",
-           "fc1": {"fetch_kib": 309514.0, "write_kib": 92423.8, "grbm": 2728855, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 151156},
-           "fc2": {"fetch_kib": 340956.3, "write_kib": 22978.0, "grbm": 2646090, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 143346}},
-    "c3": {"sources": "c710cac9ff2b10cd",
-           "fc1": {"fetch_kib": 148411.8, "write_kib": 135624.7, "grbm": 3089810, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 191183},
-           "fc2": {"fetch_kib": 212814.1, "write_kib": 89228.6, "grbm": 2525118, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 157344}},
-    "c4": {"sources": "c710cac9ff2b10cd",
-           "fc1": {"fetch_kib": 3405963.7, "write_kib": 458912.3, "grbm": 43965162, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3417831},
-           "fc2": {"fetch_kib": 1910062.0, "write_kib": 206385.5, "grbm": 23426945, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1849418}},
-    "c5": {"sources": "c710cac9ff2b10cd",
-           "fc1": {"fetch_kib": 365935.8, "write_kib": 2115.4, "grbm": 2537468, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 129394},
-           "fc2": {"fetch_kib": 182883.4, "write_kib": 3072.0, "grbm": 1402153, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 67865}},
-    "c6": {"sources": "c710cac9ff2b10cd",
-           "fc1": {"fetch_kib": 585217.9, "write_kib": 90202.8, "grbm": 5888886, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 402066},
-           "fc2": {"fetch_kib": 307299.1, "write_kib": 136477.8, "grbm": 3721357, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 233303}},
+           "fc1": {"fetch_kib": 20173.0, "write_kib": 8192.0, "grbm": 664488, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29816},
+           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 747661, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 34353}},
+    "c2": {"sources": "18f612464ae290fc",
+           "fc1": {"fetch_kib": 309557.9, "write_kib": 92330.1, "grbm": 2784692, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 151322},
+           "fc2": {"fetch_kib": 340957.8, "write_kib": 22962.0, "grbm": 2765449, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 147022}},
+    "c3": {"sources": "18f612464ae290fc",
+           "fc1": {"fetch_kib": 149098.9, "write_kib": 148257.8, "grbm": 3174007, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 190548},
+           "fc2": {"fetch_kib": 212657.2, "write_kib": 89134.4, "grbm": 2520103, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 151887}},
+    "c4": {"sources": "18f612464ae290fc",
+           "fc1": {"fetch_kib": 3357566.8, "write_kib": 458940.0, "grbm": 42111000, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3221386},
+           "fc2": {"fetch_kib": 1906965.3, "write_kib": 208673.1, "grbm": 23308786, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1840958}},
+    "c5": {"sources": "18f612464ae290fc",
+           "fc1": {"fetch_kib": 365947.4, "write_kib": 2115.6, "grbm": 2586668, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 132276},
+           "fc2": {"fetch_kib": 182886.5, "write_kib": 3072.1, "grbm": 1408028, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 69518}},
+    "c6": {"sources": "18f612464ae290fc",
+           "fc1": {"fetch_kib": 584163.5, "write_kib": 90178.7, "grbm": 5701260, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 376223},
+           "fc2": {"fetch_kib": 266006.7, "write_kib": 136211.2, "grbm": 3758739, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 230277}},
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
 # GRBM_GUI_ACTIVE also counts the counter window around the dispatch (about
