@@ -777,7 +777,8 @@ __global__ __launch_bounds__(64) void route_rank_kernel(RouteArgs a, const float
   __shared__ float lg[kRankRows * ldl];
   const int lane = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * kRankRows;
-  // value i of the lane: token r = i / (NP / 64 rounded up), expert e
+  // value i of the lane is entry f = 64 i + lane of the block's 4 x NP logit
+  // tile: token f / NP, expert f % NP
   constexpr int PER = (kRankRows * NP + 63) / 64;
   constexpr int kBatch = 16;  // partial loads in flight per value (one batch for D <= 2048)
   float acc[PER];
