@@ -216,6 +216,24 @@ def test_route_shapes(gpu, N, k):
             assert np.abs(gate - ref["gate"]).max() <= GATE_ATOL["bf16"]
 
 
+@pytest.mark.parametrize("T,N,k", [(1, 8, 2), (15, 40, 3), (16, 64, 6), (17, 256, 8), (1024, 1, 1),
+                                   (1024, 129, 1)])
+def test_route_split_edges(gpu, T, N, k):
+    """The split router (moe_route given the workspace) at its edges: fewer
+    tokens than one 16-token tile, one tile plus one token, its largest
+    batch, expert counts off the 16-wide tiles and the widest expert count
+    (four 64-expert groups per token tile)."""
+    g = torch.Generator().manual_seed(T * 1000 + N)
+    D = 256  # two partial slices per logit
+    x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, D, generator=g) * 0.05).to(torch.bfloat16)
+    b = torch.randn(N, generator=g) * 0.1
+    for renorm in (False, True):
+        idx, gate, ref = _route_case(gpu, x, w, k, renorm, b, split=True)
+        assert np.array_equal(idx, ref["idx"]), renorm
+        assert np.abs(gate - ref["gate"]).max() <= GATE_ATOL["bf16"]
+
+
 # ------------------------------------------------------------- dispatch
 def _dispatch_case(gpu, idx_np, N, C, priority="token", padded=False):
     """Both dispatch paths against the oracle: one workgroup (no scratch; its
