@@ -26,7 +26,11 @@ struct Vec<float> {
   typedef f32x4 type;
 };
 
-template <typename T>
+// NI items per thread per pass (a pass covers NI * the grid's threads): the
+// slot and gate loads of all NI items go out together, then their row loads,
+// so a wave has NI times the rows in flight per round trip.  KM >= k bounds
+// the choices held in registers (2 for top-1 and top-2 layers, else 8).
+template <typename T, int NI, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot,
                                                       const float* __restrict__ gate,
                                                       const T* __restrict__ x, T* __restrict__ out,
@@ -35,49 +39,69 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   typedef typename Vec<T>::type V;
   const int chunks = D / W;
   const int64_t items = T_ * chunks;  // one 16-byte chunk of one token each
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = i / chunks;
-    const int c = (int)(i - t * chunks);
-    float acc[W];
-    if (x) {
-      V xv = *(const V*)(x + t * D + c * W);
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < items; i0 += NI * nthreads) {
+    int64_t t[NI];
+    int c[NI];
+    bool in[NI];
 #pragma unroll
-      for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
-    } else {
-#pragma unroll
-      for (int u = 0; u < W; ++u) acc[u] = 0.f;
+    for (int n = 0; n < NI; ++n) {
+      const int64_t i = i0 + n * nthreads;
+      in[n] = i < items;
+      const int64_t ii = in[n] ? i : i0;  // a valid item: its loads stay in bounds
+      t[n] = ii / chunks;
+      c[n] = (int)(ii - t[n] * chunks);
     }
-    for (int sh = 0; sh < S; ++sh) {
-      V yv = *(const V*)(y + ((int64_t)sh * T_ + t) * D + c * W);
+    float acc[NI][W];
 #pragma unroll
-      for (int u = 0; u < W; ++u) acc[u] += (float)yv[u];
-    }
-    // every slot and gate first, then every kept row, then the sums: the
-    // loads of all k choices are in flight together (few-token batches
-    // are latency-bound here)
-    int sl[kMaxTopK];
-    float gv[kMaxTopK];
+    for (int n = 0; n < NI; ++n) {
+      if (x) {
+        V xv = *(const V*)(x + t[n] * D + c[n] * W);
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      sl[j] = (j < k) ? slot[t * k + j] : -1;
-      gv[j] = (j < k) ? gate[t * k + j] : 0.f;
-    }
-    V yv[kMaxTopK];
+        for (int u = 0; u < W; ++u) acc[n][u] = (float)xv[u];
+      } else {
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (sl[j] >= 0) yv[j] = *(const V*)(y + (int64_t)sl[j] * D + c * W);
+        for (int u = 0; u < W; ++u) acc[n][u] = 0.f;
+      }
+      for (int sh = 0; sh < S; ++sh) {
+        V yv = *(const V*)(y + ((int64_t)sh * T_ + t[n]) * D + c[n] * W);
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (sl[j] >= 0) {
-#pragma unroll
-        for (int u = 0; u < W; ++u) acc[u] = fmaf(gv[j], (float)yv[j][u], acc[u]);
+        for (int u = 0; u < W; ++u) acc[n][u] += (float)yv[u];
       }
     }
-    V o;
+    // every slot and gate first, then every kept row, then the sums: the
+    // loads of all k choices (of all NI items) are in flight together
+    int sl[NI][KM];
+    float gv[NI][KM];
 #pragma unroll
-    for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
-    *(V*)(out + t * D + c * W) = o;
+    for (int n = 0; n < NI; ++n)
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        sl[n][j] = (j < k) ? slot[t[n] * k + j] : -1;
+        gv[n][j] = (j < k) ? gate[t[n] * k + j] : 0.f;
+      }
+    V yv[NI][KM];
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (sl[n][j] >= 0) yv[n][j] = *(const V*)(y + (int64_t)sl[n][j] * D + c[n] * W);
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (sl[n][j] >= 0) {
+#pragma unroll
+          for (int u = 0; u < W; ++u) acc[n][u] = fmaf(gv[n][j], (float)yv[n][j][u], acc[n][u]);
+        }
+      }
+      if (in[n]) {
+        V o;
+#pragma unroll
+        for (int u = 0; u < W; ++u) o[u] = (T)acc[n][u];
+        *(V*)(out + t[n] * D + c[n] * W) = o;
+      }
+    }
   }
 }
 
@@ -145,16 +169,28 @@ hipError_t launch_combine(const moe_shape& s, const void* y_perm, const int32_t*
                           const float* gate, const void* x_res, void* out, hipStream_t st) {
   const int W = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;
   const int64_t items = s.T * (s.D / W);
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  const int64_t blocks = (items + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;  // blocks of 256: 32 waves per CU
+  // two items per thread once a full grid would still loop over the items
+  // (top-1 and top-2 layers: with up to 8 choices in registers the kernel's
+  // occupancy would halve)
+  const bool two = items >= 2 * cap * 256 && s.k <= 2 && s.dtype == MOE_DTYPE_BF16;
+  const int64_t per = two ? 512 : 256;
+  const int64_t blocks = (items + per - 1) / per;
   const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
   const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
-  if (s.dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)y_perm, slot, gate,
-                       (const bf16*)xr, (bf16*)out, s.T, s.D, s.k, s.n_shared);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, (const float*)y_perm, slot, gate,
-                       (const float*)xr, (float*)out, s.T, s.D, s.k, s.n_shared);
+  const bool k2 = s.k <= 2;
+#define MOE_COMBINE(TY, NI, KM)                                                                          \
+  hipLaunchKernelGGL((combine_kernel<TY, NI, KM>), grid, dim3(256), 0, st, (const TY*)y_perm, slot, gate, \
+                     (const TY*)xr, (TY*)out, s.T, s.D, s.k, s.n_shared)
+  if (s.dtype == MOE_DTYPE_BF16) {
+    if (two) MOE_COMBINE(bf16, 2, 2);
+    else if (k2) MOE_COMBINE(bf16, 1, 2);
+    else MOE_COMBINE(bf16, 1, kMaxTopK);
+  } else {
+    if (k2) MOE_COMBINE(float, 1, 2);
+    else MOE_COMBINE(float, 1, kMaxTopK);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
