@@ -87,23 +87,23 @@ PMC_KERNEL_SOURCES = {
 }
 PMC_TRAFFIC = {
     "c1": {"sources": "80377bbb4578fa6f",
-           "fc1": {"fetch_kib": 20173.0, "write_kib": 8192.0, "grbm": 664488, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29816},
-           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 747661, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 34353}},
+           "fc1": {"fetch_kib": 20173.6, "write_kib": 8192.0, "grbm": 661343, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29088},
+           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 743772, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33799}},
     "c2": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 309557.9, "write_kib": 92330.1, "grbm": 2784692, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 151322},
-           "fc2": {"fetch_kib": 340957.8, "write_kib": 22962.0, "grbm": 2765449, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 147022}},
+           "fc1": {"fetch_kib": 309541.6, "write_kib": 92393.5, "grbm": 2789048, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 153335},
+           "fc2": {"fetch_kib": 340940.9, "write_kib": 22963.7, "grbm": 2706146, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146382}},
     "c3": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 149098.9, "write_kib": 148257.8, "grbm": 3174007, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 190548},
-           "fc2": {"fetch_kib": 212657.2, "write_kib": 89134.4, "grbm": 2520103, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 151887}},
+           "fc1": {"fetch_kib": 149071.8, "write_kib": 149096.1, "grbm": 3149856, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 196261},
+           "fc2": {"fetch_kib": 212629.2, "write_kib": 89176.4, "grbm": 2514511, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 156343}},
     "c4": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 3357566.8, "write_kib": 458940.0, "grbm": 42111000, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3221386},
-           "fc2": {"fetch_kib": 1906965.3, "write_kib": 208673.1, "grbm": 23308786, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1840958}},
+           "fc1": {"fetch_kib": 3357677.3, "write_kib": 458939.4, "grbm": 42466627, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3325166},
+           "fc2": {"fetch_kib": 1902730.3, "write_kib": 208512.0, "grbm": 23427220, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1848796}},
     "c5": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 365947.4, "write_kib": 2115.6, "grbm": 2586668, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 132276},
-           "fc2": {"fetch_kib": 182886.5, "write_kib": 3072.1, "grbm": 1408028, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 69518}},
+           "fc1": {"fetch_kib": 365936.9, "write_kib": 2114.0, "grbm": 2596232, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 132420},
+           "fc2": {"fetch_kib": 182864.0, "write_kib": 3072.1, "grbm": 1413694, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68977}},
     "c6": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 584163.5, "write_kib": 90178.7, "grbm": 5701260, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 376223},
-           "fc2": {"fetch_kib": 266006.7, "write_kib": 136211.2, "grbm": 3758739, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 230277}},
+           "fc1": {"fetch_kib": 584118.1, "write_kib": 90162.8, "grbm": 5752215, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 401281},
+           "fc2": {"fetch_kib": 274879.3, "write_kib": 136474.9, "grbm": 3753717, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 237424}},
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
 # GRBM_GUI_ACTIVE also counts the counter window around the dispatch (about
