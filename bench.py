@@ -87,23 +87,23 @@ PMC_KERNEL_SOURCES = {
 }
 PMC_TRAFFIC = {
     "c1": {"sources": "80377bbb4578fa6f",
-           "fc1": {"fetch_kib": 20173.6, "write_kib": 8192.0, "grbm": 661343, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29088},
-           "fc2": {"fetch_kib": 40244.8, "write_kib": 2048.0, "grbm": 743772, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33799}},
-    "c2": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 309541.6, "write_kib": 92393.5, "grbm": 2789048, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 153335},
-           "fc2": {"fetch_kib": 340940.9, "write_kib": 22963.7, "grbm": 2706146, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146382}},
-    "c3": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 149071.8, "write_kib": 149096.1, "grbm": 3149856, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 196261},
-           "fc2": {"fetch_kib": 212629.2, "write_kib": 89176.4, "grbm": 2514511, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 156343}},
-    "c4": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 3357677.3, "write_kib": 458939.4, "grbm": 42466627, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3325166},
-           "fc2": {"fetch_kib": 1902730.3, "write_kib": 208512.0, "grbm": 23427220, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1848796}},
-    "c5": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 365936.9, "write_kib": 2114.0, "grbm": 2596232, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 132420},
-           "fc2": {"fetch_kib": 182864.0, "write_kib": 3072.1, "grbm": 1413694, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68977}},
-    "c6": {"sources": "18f612464ae290fc",
-           "fc1": {"fetch_kib": 584118.1, "write_kib": 90162.8, "grbm": 5752215, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 401281},
-           "fc2": {"fetch_kib": 274879.3, "write_kib": 136474.9, "grbm": 3753717, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 237424}},
+           "fc1": {"fetch_kib": 20173.7, "write_kib": 8192.0, "grbm": 661032, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29050},
+           "fc2": {"fetch_kib": 40244.6, "write_kib": 2048.0, "grbm": 748271, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33490}},
+    "c2": {"sources": "19e7521965d1f75e",
+           "fc1": {"fetch_kib": 309544.9, "write_kib": 92347.0, "grbm": 2763233, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 152061},
+           "fc2": {"fetch_kib": 340936.6, "write_kib": 22968.9, "grbm": 2721325, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146864}},
+    "c3": {"sources": "19e7521965d1f75e",
+           "fc1": {"fetch_kib": 149120.7, "write_kib": 150171.3, "grbm": 3150746, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 194315},
+           "fc2": {"fetch_kib": 212699.7, "write_kib": 89159.6, "grbm": 2540822, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 156480}},
+    "c4": {"sources": "19e7521965d1f75e",
+           "fc1": {"fetch_kib": 3357794.6, "write_kib": 458926.0, "grbm": 42800876, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3347721},
+           "fc2": {"fetch_kib": 1895418.2, "write_kib": 209438.1, "grbm": 23749742, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1875191}},
+    "c5": {"sources": "19e7521965d1f75e",
+           "fc1": {"fetch_kib": 365922.4, "write_kib": 2113.3, "grbm": 2580198, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 131926},
+           "fc2": {"fetch_kib": 182858.6, "write_kib": 3072.1, "grbm": 1407252, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68705}},
+    "c6": {"sources": "19e7521965d1f75e",
+           "fc1": {"fetch_kib": 584094.6, "write_kib": 90157.5, "grbm": 5704647, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 391899},
+           "fc2": {"fetch_kib": 281800.8, "write_kib": 136294.9, "grbm": 3740144, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 234013}},
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
 # GRBM_GUI_ACTIVE also counts the counter window around the dispatch (about

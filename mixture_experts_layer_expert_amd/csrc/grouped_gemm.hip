@@ -888,13 +888,13 @@ namespace {
 
 // The instantiated tile shapes (BM x BNB, waves, BK).
 enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, k256x256w8d4, k128x256w8d4,
-               k128x384w8d4, k32x256w4k128, k32x128w4k128, k256x256w8a3, k128x256w8a1, kNumCfg };
+               k128x384w8d4, k32x256w4k128, k32x128w4k128, k256x256w8a3, kNumCfg };
 const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
                                        "256x256w8d4", "128x256w8d4", "128x384w8d4", "32x256w4k128",
-                                       "32x128w4k128", "256x256w8a3", "128x256w8a1"};
+                                       "32x128w4k128", "256x256w8a3"};
 const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128, 32, 32};
 const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384, 256, 128};
-const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128, 64, 64};
+const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128, 64};
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --
@@ -985,7 +985,6 @@ hipError_t launch_grouped_gemm_bf16(const GroupedGemm& g, int64_t expected_rows,
     case k128x384w8k64: return launch_act<128, 384, 2, 4, 64, 8>(p, st);
     case k256x256w8d4: return launch_act<256, 256, 2, 4, 64, 4>(p, st);
     case k256x256w8a3: return launch_act<256, 256, 2, 4, 64, 4, 3>(p, st);
-    case k128x256w8a1: return launch_act<128, 256, 2, 4, 64, 4, 1>(p, st);
     case k128x256w8d4: return launch_act<128, 256, 2, 4, 64, 4>(p, st);
     case k128x384w8d4: return launch_act<128, 384, 2, 4, 64, 4>(p, st);
     case k32x256w4k128: return launch_act<32, 256, 1, 4, 128, 4>(p, st);
