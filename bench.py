@@ -86,22 +86,22 @@ PMC_KERNEL_SOURCES = {
     "fp32": ("mixture_experts_layer_expert_amd/csrc/grouped_gemm_f32.hip",),
 }
 PMC_TRAFFIC = {
-    "c1": {"sources": "80377bbb4578fa6f",
+    "c1": {"sources": "49e725d5e2507400",
            "fc1": {"fetch_kib": 20173.7, "write_kib": 8192.0, "grbm": 661032, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29050},
            "fc2": {"fetch_kib": 40244.6, "write_kib": 2048.0, "grbm": 748271, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33490}},
-    "c2": {"sources": "19e7521965d1f75e",
+    "c2": {"sources": "6a905f0a9fbb8225",
            "fc1": {"fetch_kib": 309544.9, "write_kib": 92347.0, "grbm": 2763233, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 152061},
            "fc2": {"fetch_kib": 340936.6, "write_kib": 22968.9, "grbm": 2721325, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146864}},
-    "c3": {"sources": "19e7521965d1f75e",
+    "c3": {"sources": "6a905f0a9fbb8225",
            "fc1": {"fetch_kib": 149120.7, "write_kib": 150171.3, "grbm": 3150746, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 194315},
            "fc2": {"fetch_kib": 212699.7, "write_kib": 89159.6, "grbm": 2540822, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 156480}},
-    "c4": {"sources": "19e7521965d1f75e",
+    "c4": {"sources": "6a905f0a9fbb8225",
            "fc1": {"fetch_kib": 3357794.6, "write_kib": 458926.0, "grbm": 42800876, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3347721},
            "fc2": {"fetch_kib": 1895418.2, "write_kib": 209438.1, "grbm": 23749742, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1875191}},
-    "c5": {"sources": "19e7521965d1f75e",
+    "c5": {"sources": "6a905f0a9fbb8225",
            "fc1": {"fetch_kib": 365922.4, "write_kib": 2113.3, "grbm": 2580198, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 131926},
            "fc2": {"fetch_kib": 182858.6, "write_kib": 3072.1, "grbm": 1407252, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68705}},
-    "c6": {"sources": "19e7521965d1f75e",
+    "c6": {"sources": "6a905f0a9fbb8225",
            "fc1": {"fetch_kib": 584094.6, "write_kib": 90157.5, "grbm": 5704647, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 391899},
            "fc2": {"fetch_kib": 281800.8, "write_kib": 136294.9, "grbm": 3740144, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 234013}},
 }
@@ -193,10 +193,11 @@ def layer_work(cfg, kept, used):
 
 
 def _code_only(text):
-    """Source text without comments, trailing blanks and empty lines: edits to
-    comments alone leave the kernel, and so its counters, unchanged."""
+    """Source text without comments, indentation, trailing blanks and empty
+    lines: edits to comments or layout alone leave the kernel, and so its
+    counters, unchanged."""
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    lines = (re.sub(r"//.*$", "", ln).strip() for ln in text.splitlines())
     return "\n".join(ln for ln in lines if ln)
 
 

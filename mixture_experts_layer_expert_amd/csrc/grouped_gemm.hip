@@ -680,12 +680,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       const bf16* a_s = sA + stage * TL::kLdsA;
       const bf16* b_s = sB + stage * TL::kLdsB;
       const int c = 2 * ks + (lane >> 5);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < TL::FN; ++i) {
         const int row = wn * TL::TN + i * 32 + (lane & 31);
         bf[buf][i] = *(const bf16x8*)(b_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
       }
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < FMX; ++j) {
         const int row = (jbase + j) * 32 + (lane & 31);
         af[buf][j] = *(const bf16x8*)(a_s + row * BK + ((c ^ swz<CPR>(row)) * 8));
@@ -693,17 +693,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     };
     f32x16 acc[TL::FN][FMX];
     auto zero_acc = [&]() __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < TL::FN; ++i)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < FMX; ++j)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     };
     auto mfmas = [&](int buf) __attribute__((always_inline)) {
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < TL::FN; ++i)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < FMX; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[buf][i], af[buf][j], acc[i][j], 0, 0, 0);
     };
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     auto interleave = [&]() __attribute__((always_inline)) {
       constexpr int NR = TL::FN + FMX, NM = TL::FN * FMX;
       constexpr int PER = NM / NR > 0 ? NM / NR : 1;
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < NR; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 DS read
         __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // PER MFMAs
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     zero_acc();
     for (int job = 0; job < n_jobs; ++job) {
       const int stage = job % STAGES;
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS - 1; ++ks) {
         load_frags(stage, ks + 1, (ks + 1) & 1);
         mfmas(ks & 1);
@@ -767,14 +767,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       } else {
         // in the symmetric layout the finishing kernel reads: block g of the
         // tile's 32-token blocks belongs to wave (g / FM) * WN + wn, slot g % FM
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < TL::FN; ++i)
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < FMX; ++j) {
             const int g = jbase + j;
             float* d = part_ptr<TL::FN, TL::FM>(p, q_rem, TL::NW, (g / TL::FM) * WN + wn, lane) +
                        (i * TL::FM + g % TL::FM) * 1024;
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) d[r * 64] = acc[i][j][r];
           }
       }

@@ -47,9 +47,9 @@ def test_biased_layer_counts_its_biases():
     assert w["fc2"]["bytes"] == 3 * (256 * 1024 + 256) * 4
 
 
-def test_code_hash_ignores_comments_only():
+def test_code_hash_ignores_comments_and_layout_only():
     a = "int f(int x) {\n  // old note\n  return x + 1;  /* tail */\n}\n"
-    b = "int f(int x) {\n\n  // a different note\n  return x + 1;\n}\n"
+    b = "int f(int x) {\n\n  // a different note\n      return x + 1;\n}\n"
     c = "int f(int x) {\n  return x + 2;\n}\n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
