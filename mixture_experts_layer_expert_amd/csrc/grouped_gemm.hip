@@ -83,15 +83,18 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t 
 
 // GELU in its erf form, z * Phi(z) with Phi the standard normal CDF, without
 // transcendental instructions (the epilogue of short-K tiles is bound by
-// them): Phi(z) = 0.5 + z * P(z^2) for |z| <= 4, P of degree 8, and
-// Phi = (z > 0) beyond.  P is a least-squares Chebyshev fit of
-// (Phi(sqrt(u)) - 0.5) / sqrt(u) on u in [0, 16] (fit_gelu_poly.py in this
-// folder derives it); the fp32 evaluation below is within 3.2e-5 of Phi
-// everywhere (the largest error is the tail beyond |z| = 4), so GELU is
-// within 1.3e-4 absolute, below the bf16 rounding of the hidden
-// activations it produces.
+// them): Phi(z) = 0.5 + z * P(z^2) for |z| <= 4, P of degree 8.  P is a
+// least-squares Chebyshev fit of (Phi(sqrt(u)) - 0.5) / sqrt(u) on u in
+// [0, 16] (fit_gelu_poly.py in this folder derives it).  Beyond |z| = 4 the
+// polynomial is evaluated at u = 16 and the result clamped to [0, 1]: P(16)
+// is about 1/8, so 0.5 + z * P(16) leaves [0, 1] by |z| = 4.001, and in
+// between it stays within the fit's error of Phi.  The clamp is the free
+// output modifier of the last FMA, so there is no branch or select.  The fp32
+// evaluation is within 3.2e-5 of Phi everywhere (the largest error is the
+// tail beyond |z| = 4), so GELU is within 1.3e-4 absolute, below the bf16
+// rounding of the hidden activations it produces.
 __device__ inline float gelu_erf(float z) {
-  const float u = z * z;
+  const float u = fminf(z * z, 16.f);
   float p = 9.408924819e-11f;
   p = fmaf(p, u, -7.887303300e-09f);
   p = fmaf(p, u, 2.954978125e-07f);
@@ -101,9 +104,7 @@ __device__ inline float gelu_erf(float z) {
   p = fmaf(p, u, 9.909445771e-03f);
   p = fmaf(p, u, -6.644644696e-02f);
   p = fmaf(p, u, 3.989348236e-01f);
-  float phi = fmaf(z, p, 0.5f);
-  if (u > 16.f) phi = z > 0.f ? 1.f : 0.f;
-  return z * phi;
+  return z * __builtin_amdgcn_fmed3f(fmaf(z, p, 0.5f), 0.f, 1.f);
 }
 
 template <int BM, int BNB, int WM, int WN, int BK_>
@@ -346,8 +347,10 @@ __device__ inline void store_block32(bf16* crow, int fbase, bool ok, const uint3
 }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-  const bf16 x = (bf16)a, y = (bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  // one round-to-nearest-even conversion of both values
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
 
 // Epilogue of one unit of a wave's share of an output tile: the 32 tokens of
@@ -392,7 +395,8 @@ __device__ inline void store_unit(const Params& p, const TileInfo& tc, const f32
       float v[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        float z = a0[q * 4 + t] + (float)bv[t];
+        float z = a0[q * 4 + t];
+        if constexpr (BIAS) z += (float)bv[t];
         if constexpr (ACT == kActGelu) z = gelu_erf(z);
         if constexpr (ACT == kActRelu) z = fmaxf(z, 0.f);
         v[t] = z;
@@ -700,6 +704,33 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     };
+    // With a bias, a whole tile's accumulators start at its bias values, so
+    // the epilogue adds none: row r of a lane's 32-row block is feature
+    // (r/4)*8 + (lane/32)*4 + r%4, the same for every token block.  A K chunk
+    // of a split tile starts at zero; its finishing kernel adds the bias once.
+    // The tile's bias slice has landed by then: DMA waves waited for the
+    // tile's first job, which was issued after it, and the other waves wait
+    // for all their loads.
+    auto init_acc = [&](int i) __attribute__((always_inline)) {
+      if constexpr (BIAS) {
+        if (i < wl.rounds || wl.S == 1) {
+          const bf16* bl = (const bf16*)&s_bias[wave][i % kBiasSlots][0];
+          const int h4 = (lane >> 5) * 4;
+#pragma unroll
+          for (int fi = 0; fi < TL::FN; ++fi)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bf16x4 bv = *(const bf16x4*)(bl + fi * 32 + q * 8 + h4);
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int j = 0; j < FMX; ++j) acc[fi][j][q * 4 + t] = (float)bv[t];
+            }
+          return;
+        }
+      }
+      zero_acc();
+    };
     auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < TL::FN; ++i)
@@ -724,10 +755,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       tc = wl.info(p, s_tile_start, s_off, tile_L(0));
       len_cmp = tile_k1(0) - tile_k0(0);
       if (dma_wave) wait_dma<NJ, STAGES - 1>(job_issued - 1);
+      if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       ring_barrier();
       load_frags(0, 0, 0);
+      init_acc(0);
+    } else {
+      zero_acc();
     }
-    zero_acc();
     for (int job = 0; job < n_jobs; ++job) {
       const int stage = job % STAGES;
 #pragma unroll
@@ -748,22 +782,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
       // left-over tile (always this workgroup's last): its partial sums are
       // stored after the loop
       if (++kt_cmp == len_cmp && more) {
-        // a wave without tile DMA waits for its bias slice here
+        // A wave without tile DMA waits here for the next tile's bias slice,
+        // which it fetched when the DMA side moved on to that tile, STAGES
+        // jobs ago; waiting before the epilogue leaves its stores in flight.
         if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_tile_x<BM, BNB, WM, WN, BK, ACT, BIAS, FMX>(p, tc, acc, jbase, wn, lane,
-                                                         (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
+        // the bias is in the accumulators already
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, false, FMX>(p, tc, acc, jbase, wn, lane, nullptr);
         kt_cmp = 0;
         ++i_cmp;
         tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
         len_cmp = tile_k1(i_cmp) - tile_k0(i_cmp);
-        zero_acc();
+        init_acc(i_cmp);
       }
     }
     if (n_jobs > 0) {
-      if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (!has_rem || wl.S == 1) {
-        store_tile_x<BM, BNB, WM, WN, BK, ACT, BIAS, FMX>(p, tc, acc, jbase, wn, lane,
-                                                         (const bf16*)&s_bias[BIAS ? wave : 0][i_cmp % kBiasSlots][0]);
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, false, FMX>(p, tc, acc, jbase, wn, lane, nullptr);
       } else {
         // in the symmetric layout the finishing kernel reads: block g of the
         // tile's 32-token blocks belongs to wave (g / FM) * WN + wn, slot g % FM
