@@ -923,12 +923,15 @@ namespace {
 // The instantiated tile shapes (BM x BNB, waves, BK).
 enum TileCfg { k256x256w8k64, k128x256w8k64, k128x384w8k64, k32x256w4k64, k256x256w8d4, k128x256w8d4,
                k128x384w8d4, k32x256w4k128, k32x128w4k128, k256x256w8a3, kNumCfg };
-const char* const kCfgName[kNumCfg] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
-                                       "256x256w8d4", "128x256w8d4", "128x384w8d4", "32x256w4k128",
-                                       "32x128w4k128", "256x256w8a3"};
-const int kCfgBM[kNumCfg] = {256, 128, 128, 32, 256, 128, 128, 32, 32};
-const int kCfgBN[kNumCfg] = {256, 256, 384, 256, 256, 256, 384, 256, 128};
-const int kCfgBK[kNumCfg] = {64, 64, 64, 64, 64, 64, 64, 128, 128, 64};
+const char* const kCfgName[] = {"256x256w8k64", "128x256w8k64", "128x384w8k64", "32x256w4k64",
+                                "256x256w8d4", "128x256w8d4", "128x384w8d4", "32x256w4k128",
+                                "32x128w4k128", "256x256w8a3"};
+const int kCfgBM[] = {256, 128, 128, 32, 256, 128, 128, 32, 32, 256};
+const int kCfgBN[] = {256, 256, 384, 256, 256, 256, 384, 256, 128, 256};
+const int kCfgBK[] = {64, 64, 64, 64, 64, 64, 64, 128, 128, 64};
+static_assert(sizeof(kCfgName) / sizeof(kCfgName[0]) == kNumCfg && sizeof(kCfgBM) / sizeof(int) == kNumCfg &&
+                  sizeof(kCfgBN) / sizeof(int) == kNumCfg && sizeof(kCfgBK) / sizeof(int) == kNumCfg,
+              "one entry per tile shape");
 
 // Tile choice from the mean rows per expert: large groups use 256x256
 // tiles (8 waves of 128x64), mid-size groups 128x256 (8 waves of 64x64) --

@@ -526,9 +526,12 @@ SPLIT_CASES = {
                                   expert_bias=True, residual=False, name="split_gelu_bias_s8"),
     "swiglu_S8": scaled_config(get_config("c2", cf=1.0), T=1024, D=512, F=1024, N=16, k=2, act="swiglu",
                                residual=False, name="split_swiglu_s8"),
-    # large groups: 256x256 tiles, few of them
+    # large groups: 256x256 tiles, few of them (the up projection on the
+    # tile whose two waves per SIMD hold 3 and 5 of its 8 token blocks)
     "relu_256": scaled_config(get_config("c2", cf=None), T=1024, D=512, F=1024, N=8, k=2, act="relu",
                               expert_bias=True, residual=False, name="split_relu_256"),
+    "swiglu_256": scaled_config(get_config("c2", cf=None), T=1024, D=512, F=1024, N=8, k=2, act="swiglu",
+                                residual=False, name="split_swiglu_256"),
 }
 
 
@@ -550,6 +553,8 @@ def test_split_last_round(gpu, key):
          f"down={plans[1]}")
     if G == 256:  # the cases are sized for a 256-CU part
         assert max(p["S"] for p in plans) >= 2
+        if key.endswith("_256"):
+            assert plans[0]["S"] >= 2  # the up projection's tile splits too
     g = to_gpu(inp)
     shape = api.MoeShape.from_config(cfg)
     buf = api.MoeBuffers(shape)
