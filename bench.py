@@ -89,21 +89,21 @@ PMC_TRAFFIC = {
     "c1": {"sources": "49e725d5e2507400",
            "fc1": {"fetch_kib": 20173.7, "write_kib": 8192.0, "grbm": 661032, "mfma_busy": 17825792, "simds": 1024, "dur_ns": 29050},
            "fc2": {"fetch_kib": 40244.6, "write_kib": 2048.0, "grbm": 748271, "mfma_busy": 17301504, "simds": 1024, "dur_ns": 33490}},
-    "c2": {"sources": "7dc4d6819f6faaad",
-           "fc1": {"fetch_kib": 309567.9, "write_kib": 92483.9, "grbm": 2818997, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 152212},
-           "fc2": {"fetch_kib": 340927.6, "write_kib": 22960.1, "grbm": 2746421, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146498}},
-    "c3": {"sources": "7dc4d6819f6faaad",
-           "fc1": {"fetch_kib": 148752.9, "write_kib": 141548.1, "grbm": 2874150, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 175966},
-           "fc2": {"fetch_kib": 212587.3, "write_kib": 90009.9, "grbm": 2501787, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 151754}},
-    "c4": {"sources": "7dc4d6819f6faaad",
-           "fc1": {"fetch_kib": 3357383.2, "write_kib": 458870.3, "grbm": 41952815, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3243650},
-           "fc2": {"fetch_kib": 1905325.1, "write_kib": 208602.7, "grbm": 23436779, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1832409}},
-    "c5": {"sources": "7dc4d6819f6faaad",
-           "fc1": {"fetch_kib": 365945.5, "write_kib": 2114.1, "grbm": 2598559, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 132489},
-           "fc2": {"fetch_kib": 182864.1, "write_kib": 3072.2, "grbm": 1406513, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68377}},
-    "c6": {"sources": "7dc4d6819f6faaad",
-           "fc1": {"fetch_kib": 584096.3, "write_kib": 90161.7, "grbm": 5633847, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 375972},
-           "fc2": {"fetch_kib": 263773.4, "write_kib": 135743.7, "grbm": 3793545, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 227482}},
+    "c2": {"sources": "ed6681ec74ca2f0c",
+           "fc1": {"fetch_kib": 309543.8, "write_kib": 92417.9, "grbm": 2765270, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 150877},
+           "fc2": {"fetch_kib": 340927.3, "write_kib": 22955.1, "grbm": 2739026, "mfma_busy": 75497472, "simds": 1024, "dur_ns": 146675}},
+    "c3": {"sources": "ed6681ec74ca2f0c",
+           "fc1": {"fetch_kib": 148745.8, "write_kib": 141793.3, "grbm": 2868067, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 176008},
+           "fc2": {"fetch_kib": 212622.9, "write_kib": 90011.0, "grbm": 2488982, "mfma_busy": 157286400, "simds": 1024, "dur_ns": 151083}},
+    "c4": {"sources": "ed6681ec74ca2f0c",
+           "fc1": {"fetch_kib": 3357288.2, "write_kib": 458877.3, "grbm": 42515886, "mfma_busy": 3992977408, "simds": 1024, "dur_ns": 3320489},
+           "fc2": {"fetch_kib": 1904527.8, "write_kib": 208097.4, "grbm": 23433479, "mfma_busy": 1996488704, "simds": 1024, "dur_ns": 1848790}},
+    "c5": {"sources": "ed6681ec74ca2f0c",
+           "fc1": {"fetch_kib": 365940.4, "write_kib": 2114.0, "grbm": 2610259, "mfma_busy": 23068672, "simds": 1024, "dur_ns": 133482},
+           "fc2": {"fetch_kib": 182876.2, "write_kib": 3072.1, "grbm": 1395272, "mfma_busy": 11534336, "simds": 1024, "dur_ns": 68048}},
+    "c6": {"sources": "ed6681ec74ca2f0c",
+           "fc1": {"fetch_kib": 584096.7, "write_kib": 90165.7, "grbm": 5644770, "mfma_busy": 461373440, "simds": 1024, "dur_ns": 379958},
+           "fc2": {"fetch_kib": 270326.3, "write_kib": 135866.8, "grbm": 3769852, "mfma_busy": 230686720, "simds": 1024, "dur_ns": 229206}},
 }
 PMC_COPY_FACTOR = {"fetch": 1.99997, "write": 1.0}  # bytes per counter byte
 # GRBM_GUI_ACTIVE also counts the counter window around the dispatch (about

@@ -359,11 +359,11 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // 2u + 1 of the weight tile, otherwise unit u is group u).  A lane owns token
 // column (lane & 31) and output rows (r/4)*8 + (lane/32)*4 + r%4 of the 32x32
 // block; rows of one token are gathered into 16-byte stores by store_block32.
-// LDS_BIAS: bias_lds holds this wave's TN bias values of the tile (the
-// pipelined kernel); otherwise they are read from global memory.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, bool LDS_BIAS>
+// BIAS: add the bias, read from global memory (the split-K finishing kernel;
+// the pipelined kernel starts its accumulators at the bias instead).
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS>
 __device__ inline void store_unit(const Params& p, const TileInfo& tc, const f32x16& a0, const f32x16& a1,
-                                  int wm, int wn, int j, int u, int lane, const bf16* bias_lds) {
+                                  int wm, int wn, int j, int u, int lane) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   const int h4 = (lane >> 5) * 4;
   const int r_out = tc.row0 + wm * TL::TM + j * 32 + (lane & 31);
@@ -387,10 +387,7 @@ __device__ inline void store_unit(const Params& p, const TileInfo& tc, const f32
     for (int q = 0; q < 4; ++q) {
       const int f = fbase + q * 8 + h4;
       bf16x4 bv = {};
-      // (no global load in the pipelined kernel: the compiler's wait for
-      // one would also drain the DMA already in flight)
-      if constexpr (BIAS && LDS_BIAS) bv = *(const bf16x4*)(bias_lds + u * 32 + q * 8 + h4);
-      if constexpr (BIAS && !LDS_BIAS)
+      if constexpr (BIAS)
         if (f < p.n_out) bv = *(const bf16x4*)(p.bias + (size_t)tc.e * p.n_out + f);
       float v[4];
 #pragma unroll
@@ -409,30 +406,13 @@ __device__ inline void store_unit(const Params& p, const TileInfo& tc, const f32
 }
 
 // Epilogue of a wave's whole share of an output tile (acc: its 32x32
-// sub-tiles, weight rows x tokens), unit by unit.
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, bool LDS_BIAS>
-__device__ inline void store_tile(const Params& p, const TileInfo& tc,
-                                  f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][Tile<BM, BNB, WM, WN, BK>::FM],
-                                  int wm, int wn, int lane, const bf16* bias_lds) {
-  using TL = Tile<BM, BNB, WM, WN, BK>;
-  constexpr int PAIR = (ACT == kActSwiGLU) ? 2 : 1;
-#pragma unroll
-  for (int j = 0; j < TL::FM; ++j) {
-#pragma unroll
-    for (int u = 0; u < TL::FN / PAIR; ++u) {
-      store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, LDS_BIAS>(p, tc, acc[u * PAIR][j], acc[u * PAIR + PAIR - 1][j], wm,
-                                                          wn, j, u, lane, bias_lds);
-      __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
-    }
-  }
-}
-
-// store_tile for a wave holding FMX 32-token blocks, the first of which is
-// block jbase of the tile (the asymmetric split of the token blocks).
-template <int BM, int BNB, int WM, int WN, int BK, int ACT, bool BIAS, int FMX>
+// sub-tiles, weight rows x tokens), unit by unit, for a wave holding FMX
+// 32-token blocks, the first of which is block jbase of the tile (with the
+// asymmetric split of the token blocks, jbase and FMX differ by wave).  The
+// accumulators already hold any bias.
+template <int BM, int BNB, int WM, int WN, int BK, int ACT, int FMX>
 __device__ inline void store_tile_x(const Params& p, const TileInfo& tc,
-                                    f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][FMX], int jbase, int wn, int lane,
-                                    const bf16* bias_lds) {
+                                    f32x16 (&acc)[Tile<BM, BNB, WM, WN, BK>::FN][FMX], int jbase, int wn, int lane) {
   using TL = Tile<BM, BNB, WM, WN, BK>;
   constexpr int PAIR = (ACT == kActSwiGLU) ? 2 : 1;
 #pragma unroll
@@ -440,8 +420,8 @@ __device__ inline void store_tile_x(const Params& p, const TileInfo& tc,
 #pragma unroll
     for (int u = 0; u < TL::FN / PAIR; ++u) {
       // wm = 0 with block index jbase + j: the row is row0 + (jbase + j) * 32
-      store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, true>(p, tc, acc[u * PAIR][j], acc[u * PAIR + PAIR - 1][j], 0, wn,
-                                                      jbase + j, u, lane, bias_lds);
+      store_unit<BM, BNB, WM, WN, BK, ACT, false>(p, tc, acc[u * PAIR][j], acc[u * PAIR + PAIR - 1][j], 0, wn,
+                                                 jbase + j, u, lane);
       __builtin_amdgcn_sched_barrier(0);  // keep accumulator reads chunked
     }
   }
@@ -499,8 +479,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
   static_assert(kRowsPerWave <= 64, "one dword DMA per wave");
   __shared__ int s_perm[TL::NW][2][64];
   // per wave, a ring of the bias values of its TN columns of a tile: filled by
-  // DMA when the tile's loads start, read by its epilogue.  The DMA side is at
-  // most STAGES jobs (so STAGES tiles) ahead, hence STAGES + 1 slots.
+  // DMA when the tile's loads start, read when the tile's accumulators are
+  // initialised.  The DMA side is at most STAGES jobs (so STAGES tiles)
+  // ahead, hence STAGES + 1 slots.
   constexpr int kBiasSlots = BIAS ? STAGES + 1 : 1;
   static_assert(!BIAS || TL::TN <= 128, "bias slice of at most 128 columns per wave");
   __shared__ uint32_t s_bias[BIAS ? TL::NW : 1][kBiasSlots][64];
@@ -786,8 +767,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
         // which it fetched when the DMA side moved on to that tile, STAGES
         // jobs ago; waiting before the epilogue leaves its stores in flight.
         if (BIAS && !dma_wave) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // the bias is in the accumulators already
-        store_tile_x<BM, BNB, WM, WN, BK, ACT, false, FMX>(p, tc, acc, jbase, wn, lane, nullptr);
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, FMX>(p, tc, acc, jbase, wn, lane);
         kt_cmp = 0;
         ++i_cmp;
         tc = wl.info(p, s_tile_start, s_off, tile_L(i_cmp));
@@ -797,7 +777,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(Params p)
     }
     if (n_jobs > 0) {
       if (!has_rem || wl.S == 1) {
-        store_tile_x<BM, BNB, WM, WN, BK, ACT, false, FMX>(p, tc, acc, jbase, wn, lane, nullptr);
+        store_tile_x<BM, BNB, WM, WN, BK, ACT, FMX>(p, tc, acc, jbase, wn, lane);
       } else {
         // in the symmetric layout the finishing kernel reads: block g of the
         // tile's 32-token blocks belongs to wave (g / FM) * WN + wn, slot g % FM
@@ -871,7 +851,7 @@ __global__ __launch_bounds__(64) void splitk_finish_kernel(Params p, int G) {
 #pragma unroll
           for (int pr = 0; pr < PAIR; ++pr) acc[pr] += v[b][pr];
     }
-    store_unit<BM, BNB, WM, WN, BK, ACT, BIAS, false>(p, tc, acc[0], acc[PAIR - 1], wm, wn, j, u, lane, nullptr);
+    store_unit<BM, BNB, WM, WN, BK, ACT, BIAS>(p, tc, acc[0], acc[PAIR - 1], wm, wn, j, u, lane);
   }
 }
 
