@@ -113,11 +113,11 @@ def test_workspace_bytes_and_validation(lib):
     assert rc == L.MOE_OK
     assert n == 64 * 2 * 128 * 4 + 64 * 2 * 256 * 4
     # ... and with the fused decode kernel y_perm + fp32 partials of the F
-    # shards; 8 experts -> 32 shards wanted, reduced until F/shards is a
-    # multiple of 32 -> 8 shards of 32 columns
+    # shards; 8 experts -> 32 shards wanted, reduced until the shard is one
+    # of the compiled widths (128, 256, 352, 384 columns) -> 2 shards of 128
     rc, n = _ws(lib, _shape(T=64, flags=L.MOE_FUSED_DECODE))
     assert rc == L.MOE_OK
-    assert n == 64 * 2 * 128 * 2 + 8 * 64 * 2 * 128 * 4
+    assert n == 64 * 2 * 128 * 2 + 2 * 64 * 2 * 128 * 4
     bad = [
         (dict(k=0), L.MOE_ERR_INVALID_ARG), (dict(k=9, N=16), L.MOE_ERR_UNSUPPORTED),
         (dict(k=9), L.MOE_ERR_INVALID_ARG), (dict(N=300, k=2), L.MOE_ERR_UNSUPPORTED),
