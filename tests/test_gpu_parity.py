@@ -216,6 +216,34 @@ def test_route_shapes(gpu, N, k):
             assert np.abs(gate - ref["gate"]).max() <= GATE_ATOL["bf16"]
 
 
+@pytest.mark.parametrize("N,D,k,bias,renorm,ties", [(128, 768, 1, False, False, False),
+                                                     (100, 256, 2, True, True, False),
+                                                     (65, 128, 8, True, False, False),
+                                                     (128, 768, 2, False, False, True)])
+def test_route_two_blocks_per_cu(gpu, N, D, k, bias, renorm, ties):
+    """The ring router's mode for 65-128 experts and at least 64 tokens per
+    CU (32-token blocks, two to a CU, the Switch layer's): a ragged last
+    block, expert counts off the 16-wide tiles, 1, 2 and 6 k steps of 128,
+    router bias and renormalisation, and small-integer inputs with a
+    duplicated router row, where every token ties and is re-ranked from
+    exact products."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 64 * cus + 45
+    g = torch.Generator().manual_seed(N * 100 + D + k)
+    if ties:
+        x = torch.randint(-2, 3, (T, D), generator=g).to(torch.bfloat16)
+        w = torch.randint(-1, 2, (N, D), generator=g).to(torch.bfloat16)
+        w[N - 1] = w[3]
+    else:
+        x = torch.randn(T, D, generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, D, generator=g) * 0.02).to(torch.bfloat16)
+    b = torch.randn(N, generator=g) * 0.1 if bias else None
+    _say(f"router, two blocks per CU: T={T} N={N} D={D} k={k} bias={bias} renorm={renorm} ties={ties}")
+    idx, gate, ref = _route_case(gpu, x, w, k, renorm, b)
+    assert np.array_equal(idx, ref["idx"])
+    assert np.abs(gate - ref["gate"]).max() <= (1e-6 if ties else GATE_ATOL["bf16"])
+
+
 @pytest.mark.parametrize("T,N,k", [(1, 8, 2), (15, 40, 3), (16, 64, 6), (17, 256, 8), (1024, 1, 1),
                                    (1024, 129, 1)])
 def test_route_split_edges(gpu, T, N, k):
