@@ -370,6 +370,8 @@ SCALED = {
     # few rows per expert -> fused weight-streaming path
     "c3dec": scaled_config(get_config("c3"), T=64, name="c3_skew_decode"),
     "c2dec": scaled_config(get_config("c2"), T=1000, name="c2_switch_decode"),
+    # decode shape with F = 512: the fused kernel's 128-column shards
+    "c5f512": scaled_config(get_config("c5"), F=512, name="c5_decode_f512"),
 }
 
 
@@ -386,7 +388,7 @@ def _scaled(key, cache):
     return cache[key]
 
 
-FUSED = {"c5", "c3dec", "c2dec"}  # few rows per expert: also run the fused decode kernel
+FUSED = {"c5", "c3dec", "c2dec", "c5f512"}  # few rows per expert: also run the fused decode kernel
 
 
 @pytest.mark.parametrize("key", sorted(SCALED) + sorted(k + ":fused" for k in FUSED))
