@@ -908,21 +908,24 @@ def test_forward_large_batch(gpu):
 
 
 # ------------------------------------------ HIP-graph capture of the layer
-@pytest.mark.parametrize("key", ["c2", "c5", "split:gelu_bias_S8", "split:swiglu_S8", "split:relu_256"])
+@pytest.mark.parametrize("key", ["c2", "c5", "c5:fused", "c3dec:fused", "split:gelu_bias_S8", "split:swiglu_S8",
+                                 "split:relu_256"])
 def test_graph_replay_matches_eager(gpu, key, scaled_cases):
     """moe_forward captured into a HIP graph: every replay, with eager work
     and synchronisations in between, equals the eager result bit for bit.
     The split cases replay layers whose last round of tiles is cut along K
     (partial sums and the tile header in the workspace, a finishing
-    launch)."""
+    launch); the fused cases the fused decode kernel and its shard-summing
+    combine."""
+    fused = key.endswith(":fused")
     if key.startswith("split:"):
         cfg = SPLIT_CASES[key.split(":", 1)[1]]
         inp = generate(cfg)
     else:
-        cfg, inp, _ = _scaled(key, scaled_cases)
+        cfg, inp, _ = _scaled(key.partition(":")[0], scaled_cases)
     _say(f"graph replay {key}: T={cfg.T} D={cfg.D} F={cfg.F} N={cfg.N} k={cfg.k}")
     g = to_gpu(inp)
-    shape = api.MoeShape.from_config(cfg)
+    shape = api.MoeShape.from_config(cfg, fused_decode=fused)
     eager = api.MoeBuffers(shape)
     eager.forward(g["x"], g)
     torch.cuda.synchronize()
