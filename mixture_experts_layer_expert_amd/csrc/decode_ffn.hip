@@ -11,10 +11,17 @@
 // of decomposed expert computations, same abstract).
 //
 //  phase 1  H[g rows, Fs] = act(X_e[g rows] . W1_s^T (+b1))   (SwiGLU: with W3_s)
-//           weight rows go straight from global memory into MFMA operand
-//           registers (each byte is used once); H goes to LDS as bf16.
+//           the item's x rows sit in LDS; weight rows go straight from
+//           global memory into MFMA operand registers (each byte is used
+//           once); H goes to LDS as bf16.
 //  phase 2  P[s][row, D] = H . W2[:, s]^T (+b2 on shard 0), fp32 partials.
 // The shard partials are summed (in fixed shard order) by the combine.
+//
+// A direct-to-register operand load gives each lane 16 bytes of one weight
+// row, so one load instruction covers 16 rows x 64 bytes (half cache lines);
+// the grouped GEMM's DMA ring moves 256-byte row pieces.  Per byte this
+// kernel makes twice the memory requests, which is why it streams more
+// slowly than the two grouped-GEMM launches it replaces.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 with the weight as the first operand (16
 // weight rows x 32 k) and the activations as the second (32 k x 16 tokens):
@@ -31,7 +38,7 @@ constexpr int U1 = 4;        // phase-1 k sub-steps (of 32) per job
 constexpr int NB1 = 2;       // phase-1 jobs per wave in flight (register buffers)
 constexpr int kGather = 16;  // x chunks per thread loaded together
 constexpr int NB2 = 2;       // phase-2 jobs per wave in flight
-// Dynamic LDS of one item (x rows, hidden tile, bias slices) at most; the
+// Most dynamic LDS of one item (x rows, hidden tile, bias slices); the
 // static arrays of the work list take about 2 KiB more.
 constexpr size_t kDecodeLds = 152 * 1024;
 
@@ -92,7 +99,8 @@ __device__ __attribute__((always_inline)) inline void pipeline(int n, int preloa
 }
 
 // Per item, once: the item's x rows (gathered through perm) go to LDS, so
-// that the weight loads are the only global loads of the streaming phases.  Weight rows go straight into MFMA operand registers, job by job
+// that the weight loads are the only global loads of the streaming phases.
+// Weight rows go straight into MFMA operand registers, job by job
 // (phase 1: U1 k sub-steps of one 16-row tile of W1 (and W3); phase 2: the
 // KS2 k sub-steps of one 16-row tile of W2), through the pipeline above.
 // D is a multiple of 32 * U1 and KS2 = Fs / 32 is a compile-time constant,
@@ -159,10 +167,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_ffn_kernel(DecodeParams p)
     const bf16* w2e = p.w2 + (int64_t)e * D * F + (int64_t)s * Fs;
     float* pout = p.part + (int64_t)s * p.rows_cap * D;
 
-    // NTT: 16-token tiles
+    // NTT: 16-token MFMA tiles per item
     auto run = [&](auto ntt_tag) __attribute__((always_inline)) {
       constexpr int NTT = decltype(ntt_tag)::value;
-      constexpr int rows_g = NTT * 16;
 
       // ---- phase 1: lane (l16, lq) loads 16 bytes of weight row
       // ft*16 + l16 of the shard at k = ks*32 + lq*8
