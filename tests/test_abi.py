@@ -138,6 +138,27 @@ def test_workspace_bytes_and_validation(lib):
     assert _ws(lib, _shape(dtype=L.MOE_DTYPE_F32, D=40, F=80))[0] == L.MOE_ERR_UNSUPPORTED
 
 
+def test_fused_decode_flag_applies_only_to_the_compiled_shapes(lib):
+    """The fused decode kernel takes bf16 layers of at most 16 rows per
+    expert, D a multiple of 128 and an F shard of 128, 256, 352 or 384
+    columns; elsewhere the flag falls back to the grouped GEMMs, whose
+    workspace then equals the one without the flag."""
+    from mixture_experts_layer_expert_amd import _lib as L
+    decode = dict(T=128, D=2048, F=1408, N=64, k=6)
+
+    def ws(flags, **kw):
+        rc, n = _ws(lib, _shape(**{**decode, **kw, "flags": flags}))
+        assert rc == L.MOE_OK
+        return n
+
+    F = L.MOE_FUSED_DECODE
+    # taken: 4 shards of 352 columns, fp32 partials of every assignment row
+    assert ws(F) == 768 * 2048 * 2 + 4 * 768 * 2048 * 4
+    assert ws(F) != ws(0)
+    for kw in (dict(D=192), dict(F=1600), dict(T=4096), dict(dtype=L.MOE_DTYPE_F32, act=L.MOE_ACT_GELU)):
+        assert ws(F, **kw) == ws(0, **kw), kw
+
+
 def test_stats_workspace_bytes_and_validation(lib):
     """One fp32 partial per (router block, expert), rounded up to 256 bytes,
     then 256 bytes for the ticket of the second pass: bf16 with D % 128 == 0

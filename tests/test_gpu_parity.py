@@ -372,6 +372,11 @@ SCALED = {
     "c2dec": scaled_config(get_config("c2"), T=1000, name="c2_switch_decode"),
     # decode shape with F = 512: the fused kernel's 128-column shards
     "c5f512": scaled_config(get_config("c5"), F=512, name="c5_decode_f512"),
+    # decode shapes the fused kernel does not take (D not a multiple of 128;
+    # no shard of F among its compiled widths): the flag falls back to the
+    # grouped GEMMs
+    "c5d192": scaled_config(get_config("c5"), D=192, name="c5_decode_d192"),
+    "c5f1600": scaled_config(get_config("c5"), F=1600, name="c5_decode_f1600"),
 }
 
 
@@ -388,7 +393,7 @@ def _scaled(key, cache):
     return cache[key]
 
 
-FUSED = {"c5", "c3dec", "c2dec", "c5f512"}  # few rows per expert: also run the fused decode kernel
+FUSED = {"c5", "c3dec", "c2dec", "c5f512", "c5d192", "c5f1600"}  # also run with the fused decode flag
 
 
 @pytest.mark.parametrize("key", sorted(SCALED) + sorted(k + ":fused" for k in FUSED))
