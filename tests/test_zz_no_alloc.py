@@ -30,11 +30,11 @@ def _poison(buf):
             t.fill_(-7)
 
 
-def _case(gpu, cfg):
-    print(f"no-alloc forward {cfg.name}: T={cfg.T}", flush=True)
+def _case(gpu, cfg, fused=False):
+    print(f"no-alloc forward {cfg.name}: T={cfg.T} fused_decode={fused}", flush=True)
     inp = generate(cfg)
     g = {k: (None if v is None else v.to(gpu).contiguous()) for k, v in inp.items()}
-    shape = api.MoeShape.from_config(cfg)
+    shape = api.MoeShape.from_config(cfg, fused_decode=fused)
     assert api.workspace_bytes(shape) <= L.MOE_NOALLOC_SCRATCH_BYTES
     ref = api.MoeBuffers(shape, device=gpu)
     got = api.MoeBuffers(shape, device=gpu)
@@ -55,6 +55,13 @@ def test_noalloc_matches_forward_twice_second_smaller(gpu):
     base = get_config("c5")
     _case(gpu, base)
     _case(gpu, scaled_config(base, T=40, name="c5_decode_bf16_T40"))
+
+
+def test_noalloc_fused_decode_twice_second_smaller(gpu):
+    """The fused decode kernel's fp32 shard partials in the scratch."""
+    base = get_config("c5")
+    _case(gpu, base, fused=True)
+    _case(gpu, scaled_config(base, T=40, name="c5_decode_bf16_T40"), fused=True)
 
 
 def test_noalloc_fp32_layer_then_smaller(gpu):
