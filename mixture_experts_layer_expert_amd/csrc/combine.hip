@@ -106,60 +106,76 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 }
 
 // Same combine, reading fp32 partial rows of NS shards (summed in shard
-// order) instead of one y_perm row.
-template <typename T>
+// order) instead of one y_perm row.  A thread takes 4 columns of one token:
+// it loads the token's slots and gates, then the partial pieces of every
+// choice for up to kShardBatch shards at once (a dropped choice reads row 0,
+// in range, and is selected away), so that its loads are in flight
+// together rather than one dependent load after another.  Per choice the
+// shards are summed in increasing order and the choices are added in
+// increasing order, so the result does not depend on the batching.
+constexpr int kShardBatch = 4;
+
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void combine_shards_kernel(const float* __restrict__ part, int NS,
                                                              int64_t rows_cap,
                                                              const int32_t* __restrict__ slot,
                                                              const float* __restrict__ gate,
                                                              const T* __restrict__ x, T* __restrict__ out,
                                                              int64_t T_, int D, int k) {
-  constexpr int W = Vec<T>::W;
-  typedef typename Vec<T>::type V;
-  const int chunks = D / W;
+  const int chunks = D / 4;
   const int64_t items = T_ * chunks;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / chunks;
     const int c = (int)(i - t * chunks);
-    float acc[W];
-    if (x) {
-      V xv = *(const V*)(x + t * D + c * W);
+    int sl[KM];
+    float g[KM];
 #pragma unroll
-      for (int u = 0; u < W; ++u) acc[u] = (float)xv[u];
+    for (int j = 0; j < KM; ++j) {
+      sl[j] = j < k ? slot[t * k + j] : -1;
+      g[j] = j < k ? gate[t * k + j] : 0.f;
+    }
+    float acc[4];
+    if (x) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = (float)x[t * D + c * 4 + u];
     } else {
 #pragma unroll
-      for (int u = 0; u < W; ++u) acc[u] = 0.f;
+      for (int u = 0; u < 4; ++u) acc[u] = 0.f;
     }
+    f32x4 y[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        const int sl = slot[t * k + j];
-        if (sl >= 0) {
-          const float g = gate[t * k + j];
-          float y[W];
+    for (int j = 0; j < KM; ++j) y[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < NS; s0 += kShardBatch) {
+      f32x4 v[KM][kShardBatch];
 #pragma unroll
-          for (int u = 0; u < W; ++u) y[u] = 0.f;
-          for (int s = 0; s < NS; ++s) {
-            const float* src = part + ((int64_t)s * rows_cap + sl) * D + c * W;
+      for (int j = 0; j < KM; ++j)
 #pragma unroll
-            for (int u = 0; u < W; u += 4) {
-              const f32x4 v = *(const f32x4*)(src + u);
-              y[u] += v[0];
-              y[u + 1] += v[1];
-              y[u + 2] += v[2];
-              y[u + 3] += v[3];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < W; ++u) acc[u] = fmaf(g, y[u], acc[u]);
+        for (int b = 0; b < kShardBatch; ++b) {
+          const int sh = s0 + b < NS ? s0 + b : NS - 1;
+          const int64_t row = sl[j] >= 0 ? sl[j] : 0;
+          v[j][b] = *(const f32x4*)(part + ((int64_t)sh * rows_cap + row) * D + c * 4);
         }
-      }
-    }
-    V o;
 #pragma unroll
-    for (int u = 0; u < W; ++u) o[u] = (T)acc[u];
-    *(V*)(out + t * D + c * W) = o;
+      for (int j = 0; j < KM; ++j)
+#pragma unroll
+        for (int b = 0; b < kShardBatch; ++b)
+          if (s0 + b < NS) y[j] += v[j][b];
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const bool kept = sl[j] >= 0;  // also false for j >= k
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = kept ? fmaf(g[j], y[j][u], acc[u]) : acc[u];
+    }
+    if constexpr (sizeof(T) == 2) {
+      bf16x4 o;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = (bf16)acc[u];
+      *(bf16x4*)(out + t * D + c * 4) = o;
+    } else {
+      *(f32x4*)(out + t * D + c * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    }
   }
 }
 
@@ -200,19 +216,23 @@ namespace moe {
 hipError_t launch_combine_shards(const moe_shape& s, const float* part, int n_shards,
                                  const int32_t* slot, const float* gate, const void* x_res, void* out,
                                  hipStream_t st) {
-  const int W = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;
-  const int64_t items = s.T * (s.D / W);
+  const int64_t items = s.T * (s.D / 4);
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int64_t blocks = (items + 255) / 256;
   const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
   const void* xr = (s.flags & MOE_RESIDUAL) ? x_res : nullptr;
   const int64_t rows_cap = s.T * (int64_t)s.k;
-  if (s.dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(combine_shards_kernel<bf16>, grid, dim3(256), 0, st, part, n_shards, rows_cap, slot,
-                       gate, (const bf16*)xr, (bf16*)out, s.T, s.D, s.k);
-  else
-    hipLaunchKernelGGL(combine_shards_kernel<float>, grid, dim3(256), 0, st, part, n_shards, rows_cap, slot,
-                       gate, (const float*)xr, (float*)out, s.T, s.D, s.k);
+#define MOE_COMBINE_SHARDS(TY, KM)                                                                        \
+  hipLaunchKernelGGL((combine_shards_kernel<TY, KM>), grid, dim3(256), 0, st, part, n_shards, rows_cap, slot, \
+                     gate, (const TY*)xr, (TY*)out, s.T, s.D, s.k)
+  if (s.dtype == MOE_DTYPE_BF16) {
+    if (s.k <= 2) MOE_COMBINE_SHARDS(bf16, 2);
+    else MOE_COMBINE_SHARDS(bf16, kMaxTopK);
+  } else {
+    if (s.k <= 2) MOE_COMBINE_SHARDS(float, 2);
+    else MOE_COMBINE_SHARDS(float, kMaxTopK);
+  }
+#undef MOE_COMBINE_SHARDS
   return hipGetLastError();
 }
 }  // namespace moe
